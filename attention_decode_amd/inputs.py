@@ -1,0 +1,271 @@
+"""Seeded synthetic decode-attention workloads.
+
+This module draws inputs only: shapes, random values, page permutations, block lists. It holds
+none of the attention arithmetic, and both the HIP path and the CPU reference read the tensors it
+returns. Every draw comes from ``torch.Generator('cpu')`` seeded with ``1000 + config`` (or the
+given seed) in a fixed order, so the same workload is produced on any machine.
+
+The five workloads (sizes of the decode benchmarks this library is measured on):
+
+1. tiny MHA: B=1, 8 q heads = 8 KV heads, D=64, 1 query, KV len 512 contiguous, fp32,
+   scale 1/8, forced 4 KV splits then merge.
+2. GQA contiguous: B=16, 32 q / 8 KV heads, D=128, 1 query, KV len 4096, bf16, scale 1/sqrt(128).
+3. paged GQA ragged: B=64, 32 q / 8 KV heads, D=128, bf16, page 16, seq lens uniform in
+   [128, 8192], block table = random permutation of a shared page pool.
+4. block-sparse + speculative: B=8, 64 q / 8 KV heads, D=128, 4 query tokens at the tail of KV
+   len 32768, bf16, KV blocks of 128 listed per (b, KV head), causal + sliding window 4096.
+5. MLA: B=32, 128 q heads on one latent KV head, q/k dim 576 (512 latent + 64 rope), v dim 512
+   (the latent), KV len 8192, bf16, paged with page 64, scale 1/sqrt(192).
+
+Cache layouts: a contiguous cache is stored head-major ``[B, Hkv, L, D]``; a paged pool is stored
+``[pages, Hkv, page_size, D]``. Both are handed out as token-major *views* ``[B, L, Hkv, D]`` /
+``[pages, page_size, Hkv, D]`` whose strides say where the data really is.
+"""
+from __future__ import annotations
+
+import copy
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+NUM_CONFIGS = 5
+
+
+@dataclass
+class Workload:
+    config: int
+    name: str
+    kind: str                      # "contiguous" | "paged" | "mla"
+    dtype: torch.dtype
+    batch: int
+    q_len: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    scale: float
+    kv_len_max: int
+    seq_lens: torch.Tensor         # int32 [B]
+    q: torch.Tensor                # [B, Q, Hq, Dqk]  (MLA: the 512 latent dims, q_nope)
+    k: torch.Tensor                # token-major view (MLA: ckv pool view [pages, page, 1, 512])
+    v: torch.Tensor                # token-major view (MLA: the same ckv view)
+    causal: bool = False
+    window: int = 0
+    num_splits: int | None = None  # forced split count (config 1), else None
+    # paged
+    block_table: torch.Tensor | None = None
+    page_size: int = 0
+    # block-sparse
+    num_blocks: torch.Tensor | None = None
+    block_idx: torch.Tensor | None = None
+    block_size: int = 0
+    # MLA second score part
+    q_pe: torch.Tensor | None = None   # [B, Q, Hq, 64]
+    kpe: torch.Tensor | None = None    # [pages, page, 1, 64]
+    storage: dict = field(default_factory=dict)
+
+    def to(self, device) -> "Workload":
+        """Copy every tensor to `device`, keeping the storage layout the views point into."""
+        out = copy.copy(self)
+        out.storage = {name: t.to(device) for name, t in self.storage.items()}
+        for f in ("seq_lens", "block_table", "num_blocks", "block_idx"):
+            t = getattr(self, f)
+            if t is not None:
+                setattr(out, f, t.to(device))
+        return _finish(out)
+
+    def kv_bytes(self) -> int:
+        """Bytes of K and V (MLA: ckv + kpe once) that a decode step must read: only keys that
+        are inside the sequence and, for a block list, inside a listed block."""
+        es = torch.finfo(self.dtype).bits // 8
+        lens = self.seq_lens.to("cpu").to(torch.int64)
+        if self.kind == "mla":
+            return int(lens.sum()) * (self.head_dim_qk) * es
+        per_tok = (self.head_dim_qk + self.head_dim_v) * es
+        if self.num_blocks is not None:
+            nb = self.num_blocks.to("cpu").to(torch.int64)
+            return int(nb.sum()) * self.block_size * per_tok
+        return int(lens.sum()) * self.num_kv_heads * per_tok
+
+
+# token-major view of each storage tensor: (storage name, permutation) per field
+_VIEWS = {
+    "contiguous": {"q": ("q", None), "k": ("k", (0, 2, 1, 3)), "v": ("v", (0, 2, 1, 3))},
+    "paged": {"q": ("q", None), "k": ("k", (0, 2, 1, 3)), "v": ("v", (0, 2, 1, 3))},
+    "mla": {"q": ("q", None), "q_pe": ("q_pe", None), "k": ("ckv", None), "v": ("ckv", None),
+            "kpe": ("kpe", None)},
+}
+
+
+def _randn(g, shape, dtype):
+    return torch.randn(*shape, generator=g, dtype=torch.float32).to(dtype)
+
+
+def _finish(w: Workload) -> Workload:
+    for f, (src, perm) in _VIEWS[w.kind].items():
+        setattr(w, f, w.storage[src].permute(*perm) if perm else w.storage[src])
+    return w
+
+
+def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len,
+               q_len=1, dtype=torch.bfloat16, scale=None, seq_lens=None, seed=0,
+               causal=False, window=0, num_splits=None) -> Workload:
+    """Head-major contiguous cache [B, Hkv, L, D]; `seq_lens` (list) may be ragged (<= kv_len)."""
+    g = torch.Generator().manual_seed(seed)
+    q = _randn(g, (batch, q_len, num_q_heads, head_dim), dtype)
+    k = _randn(g, (batch, num_kv_heads, kv_len, head_dim), dtype)
+    v = _randn(g, (batch, num_kv_heads, kv_len, head_dim), dtype)
+    sl = torch.full((batch,), kv_len, dtype=torch.int32) if seq_lens is None else \
+        torch.as_tensor(seq_lens, dtype=torch.int32)
+    w = Workload(config=config, name=name, kind="contiguous", dtype=dtype, batch=batch, q_len=q_len,
+                 num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim_qk=head_dim,
+                 head_dim_v=head_dim, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
+                 kv_len_max=kv_len, seq_lens=sl, q=None, k=None, v=None, causal=causal, window=window,
+                 num_splits=num_splits)
+    w.storage = {"q": q, "k": k, "v": v}
+    return _finish(w)
+
+
+def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
+          q_len=1, dtype=torch.bfloat16, scale=None, seed=0, poison=False, max_pages=None,
+          causal=False, window=0) -> Workload:
+    """Paged cache: pool [pages, Hkv, page_size, D] (head-major pages), block table [B, max_pages].
+
+    The logical content of sequence b depends only on the seed and seq_lens; the physical page
+    order is a random permutation. With ``poison`` the pool gets ~5% extra pages nobody
+    references, every page and tail slot not covered by a sequence holds NaN, the table is padded
+    with -1, and a different permutation is used -- the logical KV is unchanged.
+    """
+    g = torch.Generator().manual_seed(seed)
+    sl = torch.as_tensor(seq_lens, dtype=torch.int32)
+    B = sl.numel()
+    pages_b = [(int(x) + page_size - 1) // page_size for x in sl]
+    n_logical = sum(pages_b)
+    q = _randn(g, (B, q_len, num_q_heads, head_dim), dtype)
+    k_log = _randn(g, (n_logical, num_kv_heads, page_size, head_dim), dtype)
+    v_log = _randn(g, (n_logical, num_kv_heads, page_size, head_dim), dtype)
+    n_pool = n_logical + (max(1, n_logical // 20) if poison else 0)
+    pg = torch.Generator().manual_seed(seed + (7919 if poison else 0))
+    perm = torch.randperm(n_pool, generator=pg)[:n_logical]
+    fill = float("nan") if poison else 0.0
+    k_pool = torch.full((n_pool, num_kv_heads, page_size, head_dim), fill, dtype=dtype)
+    v_pool = torch.full((n_pool, num_kv_heads, page_size, head_dim), fill, dtype=dtype)
+    k_pool[perm] = k_log
+    v_pool[perm] = v_log
+    mp = max(pages_b) if max_pages is None else max_pages
+    bt = torch.full((B, max(mp, 1)), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(pages_b):
+        bt[b, :n] = perm[off:off + n].to(torch.int32)
+        # slots past the end of the sequence in its last page
+        tail = int(sl[b]) - (n - 1) * page_size if n else page_size
+        if poison and n and tail < page_size:
+            k_pool[bt[b, n - 1], :, tail:] = float("nan")
+            v_pool[bt[b, n - 1], :, tail:] = float("nan")
+        off += n
+    w = Workload(config=config, name=name, kind="paged", dtype=dtype, batch=B, q_len=q_len,
+                 num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim_qk=head_dim,
+                 head_dim_v=head_dim, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
+                 kv_len_max=mp * page_size, seq_lens=sl, q=None, k=None, v=None,
+                 block_table=bt, page_size=page_size, causal=causal, window=window)
+    w.storage = {"q": q, "k": k_pool, "v": v_pool}
+    return _finish(w)
+
+
+def window_block_list(kv_len: int, q_len: int, window: int, block_size: int):
+    """Blocks that hold at least one key inside the causal sliding window of some query row of a
+    q_len-token query at the tail of a kv_len cache (the 'causal + window expressed as block
+    lists' input of the block-sparse workload). Returned ascending."""
+    first_key = max(0, kv_len - q_len - window + 1)   # oldest key the first query can see
+    last_key = kv_len - 1                               # newest key the last query can see
+    return list(range(first_key // block_size, last_key // block_size + 1))
+
+
+def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len, q_len,
+           block_size, blocks, dtype=torch.bfloat16, scale=None, seed=0, causal=True, window=0,
+           poison=False) -> Workload:
+    """Contiguous head-major cache with a per-(b, KV head) list of KV blocks (same list for all).
+    With ``poison`` every unlisted block holds NaN."""
+    w = contiguous(config=config, name=name, batch=batch, num_q_heads=num_q_heads,
+                   num_kv_heads=num_kv_heads, head_dim=head_dim, kv_len=kv_len, q_len=q_len,
+                   dtype=dtype, scale=scale, seed=seed, causal=causal, window=window)
+    nb = len(blocks)
+    w.num_blocks = torch.full((batch, num_kv_heads), nb, dtype=torch.int32)
+    w.block_idx = torch.as_tensor(blocks, dtype=torch.int32).view(1, 1, nb).repeat(batch, num_kv_heads, 1)
+    w.block_size = block_size
+    if poison:
+        listed = torch.zeros(kv_len, dtype=torch.bool)
+        for blk in blocks:
+            listed[blk * block_size:(blk + 1) * block_size] = True
+        for name_ in ("k", "v"):
+            w.storage[name_][:, :, ~listed, :] = float("nan")
+    return w
+
+
+def mla(*, config=0, name="custom", batch, num_heads, kv_len, page_size, dim_latent=512, dim_rope=64,
+        dtype=torch.bfloat16, scale=None, seed=0, seq_lens=None, poison=False) -> Workload:
+    """MLA: q_nope [B,1,H,512], q_pe [B,1,H,64], ckv pool [pages, page, 512] and kpe pool
+    [pages, page, 64] (one shared latent KV head), block table from a random page permutation."""
+    g = torch.Generator().manual_seed(seed)
+    sl = torch.full((batch,), kv_len, dtype=torch.int32) if seq_lens is None else \
+        torch.as_tensor(seq_lens, dtype=torch.int32)
+    pages_b = [(int(x) + page_size - 1) // page_size for x in sl]
+    n_logical = sum(pages_b)
+    q = _randn(g, (batch, 1, num_heads, dim_latent), dtype)
+    q_pe = _randn(g, (batch, 1, num_heads, dim_rope), dtype)
+    ckv_log = _randn(g, (n_logical, page_size, dim_latent), dtype)
+    kpe_log = _randn(g, (n_logical, page_size, dim_rope), dtype)
+    n_pool = n_logical + (max(1, n_logical // 20) if poison else 0)
+    pg = torch.Generator().manual_seed(seed + (7919 if poison else 0))
+    perm = torch.randperm(n_pool, generator=pg)[:n_logical]
+    fill = float("nan") if poison else 0.0
+    ckv = torch.full((n_pool, page_size, dim_latent), fill, dtype=dtype)
+    kpe = torch.full((n_pool, page_size, dim_rope), fill, dtype=dtype)
+    ckv[perm] = ckv_log
+    kpe[perm] = kpe_log
+    mp = max(pages_b)
+    bt = torch.full((batch, mp), -1, dtype=torch.int32)
+    off = 0
+    for b, n in enumerate(pages_b):
+        bt[b, :n] = perm[off:off + n].to(torch.int32)
+        tail = int(sl[b]) - (n - 1) * page_size
+        if poison and tail < page_size:
+            ckv[bt[b, n - 1], tail:] = float("nan")
+            kpe[bt[b, n - 1], tail:] = float("nan")
+        off += n
+    w = Workload(config=config, name=name, kind="mla", dtype=dtype, batch=batch, q_len=1,
+                 num_q_heads=num_heads, num_kv_heads=1, head_dim_qk=dim_latent + dim_rope,
+                 head_dim_v=dim_latent, scale=(1.0 / math.sqrt(192)) if scale is None else scale,
+                 kv_len_max=mp * page_size, seq_lens=sl, q=None, k=None, v=None,
+                 block_table=bt, page_size=page_size)
+    w.storage = {"q": q, "q_pe": q_pe, "ckv": ckv.view(n_pool, page_size, 1, dim_latent),
+                 "kpe": kpe.view(n_pool, page_size, 1, dim_rope)}
+    return _finish(w)
+
+
+def make(config: int, *, seed: int | None = None, poison: bool = False) -> Workload:
+    """One of the five benchmark workloads, generated on the CPU."""
+    s = 1000 + config if seed is None else seed
+    if config == 1:
+        return contiguous(config=1, name="tiny_mha_fp32_split4", batch=1, num_q_heads=8, num_kv_heads=8,
+                          head_dim=64, kv_len=512, dtype=torch.float32, scale=1.0 / 8.0, seed=s,
+                          num_splits=4)
+    if config == 2:
+        return contiguous(config=2, name="gqa_bf16_contiguous", batch=16, num_q_heads=32, num_kv_heads=8,
+                          head_dim=128, kv_len=4096, dtype=torch.bfloat16, seed=s)
+    if config == 3:
+        g = torch.Generator().manual_seed(s)
+        lens = torch.randint(128, 8193, (64,), generator=g, dtype=torch.int64).tolist()
+        return paged(config=3, name="paged_gqa_bf16_ragged", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, page_size=16, dtype=torch.bfloat16, seed=s + 1, poison=poison,
+                     max_pages=512)
+    if config == 4:
+        blocks = window_block_list(32768, 4, 4096, 128)
+        return sparse(config=4, name="sparse_spec_bf16", batch=8, num_q_heads=64, num_kv_heads=8,
+                      head_dim=128, kv_len=32768, q_len=4, block_size=128, blocks=blocks,
+                      dtype=torch.bfloat16, seed=s, causal=True, window=4096, poison=poison)
+    if config == 5:
+        return mla(config=5, name="mla_bf16_paged64", batch=32, num_heads=128, kv_len=8192, page_size=64,
+                   dtype=torch.bfloat16, scale=1.0 / math.sqrt(192), seed=s, poison=poison)
+    raise ValueError(f"unknown workload {config}")

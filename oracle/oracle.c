@@ -1,0 +1,269 @@
+/*
+ * oracle.c -- plain fp64 CPU reference for single-step decode attention.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check of the package entry file and the
+ * CPU-baseline leg of the benchmark may load or run this library. The HIP library never
+ * links, includes or calls it, and it shares no code, header, table or helper with it.
+ *
+ * It computes the plain definition with no tiling, no split and no online softmax. For every
+ * query row (b, t, hq):
+ *
+ *   hkv   = hq / G,   G = num_q_heads / num_kv_heads             (GQA: G consecutive query heads
+ *                                                              share one KV head; PyTorch Inductor
+ *                                                              flex_decode.py.jinja, the
+ *                                                              "hq = hkv*G + g" head packing)
+ *   L     = seq_lens[b],   pos = L - q_len + t                   (query t sits at the tail of its
+ *                                                              sequence; mslk splitk_kernels.py,
+ *                                                              the causal-mask comment in
+ *                                                              _fwd_kernel_splitK)
+ *   s_j   = scale * sum_d q[d] * k_j[d]                          (plus the second part
+ *                                                              q2 . k2_j when present: the MLA
+ *                                                              score is q_nope.ckv + q_pe.kpe,
+ *                                                              FlashInfer attention/mla.cuh,
+ *                                                              compute_mla_qk)
+ *   out   = sum_j exp(s_j - m) v_j / sum_j exp(s_j - m)
+ *   lse   = m + ln sum_j exp(s_j - m)                            (natural-log LSE as written by
+ *                                                              mslk splitk_kernels.py at the end
+ *                                                              of _fwd_kernel_splitK)
+ *
+ * over the visible keys j, with m their largest score. A row with no visible key gets out = 0 and
+ * lse = -inf (mslk splitk_kernels.py, the l == 0 guard of the split epilogue and the lse_max ==
+ * -inf guard of _splitK_reduce).
+ *
+ * Key j is visible to row (b, t, hq) iff all of:
+ *   0 <= j < L;
+ *   key_lo <= j < key_hi when a key range is given (a split's own token range);
+ *   not causal, or j <= pos     (bottom-right causal: FlashInfer mla.cuh logits_mask_ masks
+ *                                kv_idx + qo_len > kv_len + q_idx);
+ *   window == 0, or pos - j < window   (the window keeps `window` keys ending at the query's own
+ *                                position: TensorRT-LLM xqa mha.cu skips the first len - W cache
+ *                                tokens; equal to mslk's WINDOW_LEFT = window - 1);
+ *   no block list, or j / block_size is one of the listed blocks of (b, hkv)   (PyTorch Inductor
+ *                                flex_decode.py.jinja, KV_NUM_BLKS / KV_IDX).
+ *
+ * K and V rows are found through the same address map the cache uses:
+ *   contiguous: base + b*st[0] + j*st[1] + hkv*st[2]
+ *   paged:      base + block_table[b][j / page_size]*st[0] + (j % page_size)*st[1] + hkv*st[2]
+ *               (mslk splitk_kernels.py paged branch; TensorRT-LLM xqa page list)
+ * The last dimension is contiguous. Elements are fp64, fp32 or bf16 (raw 16-bit patterns), all
+ * widened exactly to fp64.
+ *
+ * oracle_merge() is the LSE-weighted combine of per-split (o_s, lse_s) pairs written out in fp64
+ * (mslk splitk_kernels.py, _splitK_reduce): M = max_s lse_s, w_s = exp(lse_s - M),
+ * out = sum_s w_s o_s / sum_s w_s, lse = M + ln sum_s w_s; M = -inf gives out 0, lse -inf.
+ *
+ * Every function here is pinned by the oracle tests (closed forms, a library attention routine,
+ * hand-listed visibility sets, paging and split invariants); none is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+
+typedef struct {
+    int32_t batch, q_len, num_q_heads, num_kv_heads;
+    int32_t dim_qk;   /* first score part (all of it for plain attention; the 512 latent dims for MLA) */
+    int32_t dim_qk2;  /* second score part (the 64 rope dims for MLA); 0 when absent */
+    int32_t dim_v;
+    double scale;
+    int32_t q_type, kv_type; /* ORC_F64 / ORC_F32 / ORC_BF16 */
+    const void *q;  int64_t q_stride[3];  /* [b][t][hq] */
+    const void *q2; int64_t q2_stride[3]; /* [b][t][hq] */
+    const void *k;  int64_t k_stride[3];  /* contiguous [b][j][hkv]; paged [page][slot][hkv] */
+    const void *k2; int64_t k2_stride[3]; /* same indexing as k */
+    const void *v;  int64_t v_stride[3];  /* same indexing as k */
+    const int32_t *seq_lens;              /* [batch]; NULL: every sequence has kv_len keys */
+    int32_t kv_len;
+    const int32_t *block_table; int64_t bt_stride; int32_t page_size; /* NULL: contiguous */
+    const int32_t *num_blocks; int64_t nb_stride[2];                   /* NULL: no block list */
+    const int32_t *block_idx; int64_t idx_stride[3]; int32_t block_size;
+    int32_t causal, window;
+    int32_t key_lo, key_hi; /* key_hi < 0: no range restriction */
+} oracle_problem;
+
+static double widen(const void *base, int32_t type, int64_t i)
+{
+    if (type == ORC_F64) return ((const double *)base)[i];
+    if (type == ORC_F32) return (double)((const float *)base)[i];
+    /* bf16 is the upper half of an IEEE binary32 pattern */
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Offset (in elements) of the row of key j of head hkv of sequence b. */
+static int64_t kv_row(const oracle_problem *P, const int64_t st[3], int64_t b, int64_t hkv, int64_t j)
+{
+    if (P->block_table) {
+        int64_t page = P->block_table[b * P->bt_stride + j / P->page_size];
+        return page * st[0] + (j % P->page_size) * st[1] + hkv * st[2];
+    }
+    return b * st[0] + j * st[1] + hkv * st[2];
+}
+
+static int block_listed(const oracle_problem *P, int64_t b, int64_t hkv, int64_t j)
+{
+    if (!P->num_blocks) return 1;
+    int64_t n = P->num_blocks[b * P->nb_stride[0] + hkv * P->nb_stride[1]];
+    int64_t blk = j / P->block_size;
+    for (int64_t i = 0; i < n; i++)
+        if (P->block_idx[b * P->idx_stride[0] + hkv * P->idx_stride[1] + i * P->idx_stride[2]] == blk)
+            return 1;
+    return 0;
+}
+
+static int key_visible(const oracle_problem *P, int64_t b, int64_t t, int64_t hkv, int64_t L, int64_t j)
+{
+    int64_t pos = L - P->q_len + t;
+    if (j < 0 || j >= L) return 0;
+    if (P->key_hi >= 0 && (j < P->key_lo || j >= P->key_hi)) return 0;
+    if (P->causal && j > pos) return 0;
+    if (P->window > 0 && pos - j >= P->window) return 0;
+    return block_listed(P, b, hkv, j);
+}
+
+static double score(const oracle_problem *P, int64_t b, int64_t t, int64_t hq, int64_t hkv, int64_t j)
+{
+    double acc = 0.0;
+    int64_t qo = b * P->q_stride[0] + t * P->q_stride[1] + hq * P->q_stride[2];
+    int64_t ko = kv_row(P, P->k_stride, b, hkv, j);
+    for (int64_t d = 0; d < P->dim_qk; d++)
+        acc += widen(P->q, P->q_type, qo + d) * widen(P->k, P->kv_type, ko + d);
+    if (P->dim_qk2 > 0) {
+        int64_t qo2 = b * P->q2_stride[0] + t * P->q2_stride[1] + hq * P->q2_stride[2];
+        int64_t ko2 = kv_row(P, P->k2_stride, b, hkv, j);
+        for (int64_t d = 0; d < P->dim_qk2; d++)
+            acc += widen(P->q2, P->q_type, qo2 + d) * widen(P->k2, P->kv_type, ko2 + d);
+    }
+    return P->scale * acc;
+}
+
+static int check_problem(const oracle_problem *P)
+{
+    if (!P || P->batch < 0 || P->q_len <= 0 || P->num_q_heads <= 0 || P->num_kv_heads <= 0) return -1;
+    if (P->num_q_heads % P->num_kv_heads) return -1;
+    if (P->dim_qk <= 0 || P->dim_v <= 0 || P->dim_qk2 < 0) return -1;
+    if (!P->q || !P->k || !P->v) return -1;
+    if (P->dim_qk2 > 0 && (!P->q2 || !P->k2)) return -1;
+    if (P->block_table && P->page_size <= 0) return -1;
+    if (P->num_blocks && (!P->block_idx || P->block_size <= 0)) return -1;
+    if (P->window < 0) return -1;
+    return 0;
+}
+
+static int n_threads = 0; /* 0: OpenMP default */
+
+void oracle_set_threads(int n) { n_threads = n; }
+
+int oracle_get_threads(void)
+{
+#ifdef _OPENMP
+    return n_threads > 0 ? n_threads : omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Attention for the listed rows (row = (b*q_len + t)*num_q_heads + hq), or for every row in that
+ * order when rows == NULL. out is [nrows][dim_v], lse is [nrows]. Returns 0, or -1 on a
+ * malformed problem.
+ */
+int oracle_attend(const oracle_problem *P, const int64_t *rows, int64_t nrows, double *out, double *lse)
+{
+    if (check_problem(P) || !out || !lse) return -1;
+    const int64_t G = P->num_q_heads / P->num_kv_heads;
+    const int64_t total = (int64_t)P->batch * P->q_len * P->num_q_heads;
+    if (!rows) nrows = total;
+    for (int64_t i = 0; rows && i < nrows; i++)
+        if (rows[i] < 0 || rows[i] >= total) return -1;
+
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(oracle_get_threads())
+    for (int64_t i = 0; i < nrows; i++) {
+        const int64_t r = rows ? rows[i] : i;
+        const int64_t hq = r % P->num_q_heads;
+        const int64_t t = (r / P->num_q_heads) % P->q_len;
+        const int64_t b = r / ((int64_t)P->num_q_heads * P->q_len);
+        const int64_t hkv = hq / G;
+        const int64_t L = P->seq_lens ? P->seq_lens[b] : P->kv_len;
+        double *o = out + i * P->dim_v;
+
+        double *s = (double *)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
+        char *vis = (char *)malloc((size_t)(L > 0 ? L : 1));
+        if (!s || !vis) {
+            free(s);
+            free(vis);
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        double m = -INFINITY;
+        int64_t n_vis = 0;
+        for (int64_t j = 0; j < L; j++) {
+            vis[j] = (char)key_visible(P, b, t, hkv, L, j);
+            if (!vis[j]) continue;
+            s[j] = score(P, b, t, hq, hkv, j);
+            if (s[j] > m) m = s[j];
+            n_vis++;
+        }
+        for (int64_t d = 0; d < P->dim_v; d++) o[d] = 0.0;
+        if (n_vis == 0) {
+            lse[i] = -INFINITY;
+            free(s);
+            free(vis);
+            continue;
+        }
+        double l = 0.0;
+        for (int64_t j = 0; j < L; j++) {
+            if (!vis[j]) continue;
+            double w = exp(s[j] - m);
+            int64_t vo = kv_row(P, P->v_stride, b, hkv, j);
+            l += w;
+            for (int64_t d = 0; d < P->dim_v; d++) o[d] += w * widen(P->v, P->kv_type, vo + d);
+        }
+        for (int64_t d = 0; d < P->dim_v; d++) o[d] /= l;
+        lse[i] = m + log(l);
+        free(s);
+        free(vis);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * LSE-weighted merge of `splits` partial results per row.
+ * part_o is [rows][splits][dim_v], part_lse is [rows][splits]; out is [rows][dim_v], lse [rows].
+ */
+int oracle_merge(int64_t rows, int32_t splits, int32_t dim_v, const double *part_o, const double *part_lse,
+                 double *out, double *lse)
+{
+    if (rows < 0 || splits <= 0 || dim_v <= 0 || !part_o || !part_lse || !out || !lse) return -1;
+    for (int64_t r = 0; r < rows; r++) {
+        const double *ls = part_lse + r * splits;
+        double *o = out + r * dim_v;
+        double M = -INFINITY;
+        for (int32_t s = 0; s < splits; s++)
+            if (ls[s] > M) M = ls[s];
+        for (int32_t d = 0; d < dim_v; d++) o[d] = 0.0;
+        if (M == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double W = 0.0;
+        for (int32_t s = 0; s < splits; s++) {
+            double w = exp(ls[s] - M);
+            const double *os = part_o + (r * splits + s) * dim_v;
+            W += w;
+            for (int32_t d = 0; d < dim_v; d++) o[d] += w * os[d];
+        }
+        for (int32_t d = 0; d < dim_v; d++) o[d] /= W;
+        lse[r] = M + log(W);
+    }
+    return 0;
+}

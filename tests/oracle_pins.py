@@ -1,0 +1,380 @@
+"""Pins for the fp64 oracle: checks against things other than the oracle itself.
+
+Each pin takes an ``oracle.Oracle`` handle and raises AssertionError when the oracle disagrees
+with a library routine (PyTorch's scaled_dot_product_attention / logsumexp in fp64), a closed
+form, a hand-listed visibility set (tests/golden/visibility.json) or an invariant the method
+must satisfy (paging, splitting, layout, widening). The pins are plain functions so the mutation
+test can run them against deliberately broken builds of the oracle.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = 1e-12
+
+
+def _gen(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+def _randn(g, *shape, dtype=torch.float64):
+    return torch.randn(*shape, generator=g, dtype=torch.float64).to(dtype)
+
+
+def _close(a, b, tol=TOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    same_inf = (np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b)))
+    diff = np.where(same_inf, 0.0, np.abs(a - b))
+    assert np.all(np.isfinite(diff)), f"{what}: non-finite mismatch"
+    assert diff.max(initial=0.0) <= tol, f"{what}: max |diff| {diff.max()} > {tol}"
+
+
+def _sdpa(q, k, v, scale, mask):
+    """Library attention: q [B,Q,Hq,D], k/v [B,L,Hkv,D], mask [B,Q,L] bool (True = visible).
+    Returns out [B,Q,Hq,Dv] and lse [B,Q,Hq], both fp64."""
+    B, Q, Hq, _ = q.shape
+    Hkv = k.shape[2]
+    qh = q.permute(0, 2, 1, 3).double()
+    kh = k.permute(0, 2, 1, 3).double().contiguous()
+    vh = v.permute(0, 2, 1, 3).double().contiguous()
+    m = mask[:, None, :, :]
+    out = F.scaled_dot_product_attention(qh, kh, vh, attn_mask=m, scale=scale, enable_gqa=True)
+    kx = kh.repeat_interleave(Hq // Hkv, dim=1)
+    s = torch.matmul(qh, kx.transpose(-1, -2).contiguous()) * scale
+    lse = torch.logsumexp(s.masked_fill(~m, float("-inf")), dim=-1)
+    return out.permute(0, 2, 1, 3).numpy(), lse.permute(0, 2, 1).numpy()
+
+
+def _library_mask(B, Q, L, seq_lens, causal, window):
+    """Visibility from torch's triangular-matrix routines: tril/triu with a diagonal offset put
+    each query at the bottom-right (position L - Q + t)."""
+    masks = []
+    for b in range(B):
+        Lb = int(seq_lens[b])
+        m = torch.zeros(Q, L, dtype=torch.bool)
+        sub = torch.ones(Q, Lb, dtype=torch.bool)
+        if causal:
+            sub = sub.tril(diagonal=Lb - Q)
+        if window:
+            sub = sub.triu(diagonal=Lb - Q - window + 1)
+        m[:, :Lb] = sub
+        masks.append(m)
+    return torch.stack(masks)
+
+
+# ---------------------------------------------------------------------------------------------
+def pin_library_attention(orc):
+    """Ragged GQA attention equals PyTorch SDPA (fp64) and logsumexp."""
+    g = _gen(11)
+    B, Q, Hq, Hkv, D, Dv, L = 3, 1, 6, 2, 8, 5, 13
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, Dv)
+    lens = torch.tensor([13, 9, 1], dtype=torch.int32)
+    scale = 0.37
+    out, lse = orc.attend(q, k, v, scale=scale, seq_lens=lens)
+    ref_o, ref_l = _sdpa(q, k, v, scale, _library_mask(B, Q, L, lens, False, 0))
+    _close(out, ref_o, what="out")
+    _close(lse, ref_l, what="lse")
+
+
+def pin_library_causal_window(orc):
+    """Multi-query decode with bottom-right causal + window equals SDPA with a tril/triu mask."""
+    g = _gen(12)
+    B, Q, Hq, Hkv, D, L = 2, 4, 8, 2, 6, 19
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    lens = torch.tensor([19, 11], dtype=torch.int32)
+    for causal, window in ((True, 0), (True, 5), (False, 7)):
+        out, lse = orc.attend(q, k, v, scale=0.5, seq_lens=lens, causal=causal, window=window)
+        ref_o, ref_l = _sdpa(q, k, v, 0.5, _library_mask(B, Q, L, lens, causal, window))
+        _close(out, ref_o, what=f"out causal={causal} window={window}")
+        _close(lse, ref_l, what=f"lse causal={causal} window={window}")
+
+
+def pin_library_block_list(orc):
+    """A block list equals SDPA with a mask built from block membership (torch.isin)."""
+    g = _gen(13)
+    B, Q, Hq, Hkv, D, L, bs = 2, 2, 4, 2, 8, 24, 4
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    lens = torch.tensor([24, 22], dtype=torch.int32)
+    blocks = torch.tensor([[[1, 2, 5], [0, 3, 5]], [[2, 4, 5], [5, 1, 0]]], dtype=torch.int32)
+    nb = torch.tensor([[3, 2], [3, 3]], dtype=torch.int32)
+    out, lse = orc.attend(q, k, v, scale=0.3, seq_lens=lens, num_blocks=nb, block_idx=blocks,
+                          block_size=bs, causal=True, window=9)
+    base = _library_mask(B, Q, L, lens, True, 9)
+    for b in range(B):
+        for h in range(Hkv):
+            listed = blocks[b, h, : nb[b, h]].long()
+            keep = torch.isin(torch.arange(L) // bs, listed)
+            m = base[b:b + 1] & keep
+            qq = q[b:b + 1, :, h * 2:(h + 1) * 2]
+            ro, rl = _sdpa(qq, k[b:b + 1, :, h:h + 1], v[b:b + 1, :, h:h + 1], 0.3, m)
+            _close(out[b:b + 1, :, h * 2:(h + 1) * 2], ro, what=f"out b={b} h={h}")
+            _close(lse[b:b + 1, :, h * 2:(h + 1) * 2], rl, what=f"lse b={b} h={h}")
+
+
+def pin_golden_visibility(orc):
+    """scale = 0 and one-hot V reveal the visible set: out_j = 1/n for visible j, lse = ln n."""
+    with open(os.path.join(GOLDEN, "visibility.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        L, Q = c["kv_len"], c["q_len"]
+        q = torch.ones(1, Q, 1, 4, dtype=torch.float64)
+        k = torch.ones(1, max(L, 1), 1, 4, dtype=torch.float64)
+        v = torch.eye(max(L, 1), dtype=torch.float64).view(1, max(L, 1), 1, max(L, 1))
+        kw = dict(scale=0.0, seq_lens=torch.tensor([L], dtype=torch.int32),
+                  causal=c["causal"], window=c["window"])
+        if c["blocks"] is not None:
+            kw.update(num_blocks=torch.tensor([[len(c["blocks"])]], dtype=torch.int32),
+                      block_idx=torch.tensor([[c["blocks"]]], dtype=torch.int32),
+                      block_size=c["block_size"])
+        out, lse = orc.attend(q, k, v, **kw)
+        for t, vis in enumerate(c["visible"]):
+            expect = np.zeros(max(L, 1))
+            if vis:
+                expect[vis] = 1.0 / len(vis)
+                assert abs(lse[0, t, 0] - math.log(len(vis))) <= TOL, f"{c['name']} t={t} lse"
+            else:
+                assert lse[0, t, 0] == -math.inf, f"{c['name']} t={t}: expected an empty row"
+            _close(out[0, t, 0], expect, what=f"{c['name']} t={t}")
+
+
+def pin_one_visible_key(orc):
+    """A single visible key returns its value row and lse = its logit."""
+    g = _gen(14)
+    q = _randn(g, 1, 1, 2, 8)
+    k = _randn(g, 1, 9, 1, 8)
+    v = _randn(g, 1, 9, 1, 8)
+    lens = torch.tensor([9], dtype=torch.int32)
+    # block 2 of size 4 covers keys 8..11, of which only key 8 exists
+    out, lse = orc.attend(q, k, v, scale=0.7, seq_lens=lens, num_blocks=torch.tensor([[1]]),
+                          block_idx=torch.tensor([[[2]]]), block_size=4)
+    for h in range(2):
+        _close(out[0, 0, h], v[0, 8, 0].numpy(), what="out")
+        s = 0.7 * float((q[0, 0, h] * k[0, 8, 0]).sum())
+        assert abs(lse[0, 0, h] - s) <= TOL, "lse"
+
+
+def pin_identical_keys(orc):
+    """n identical keys with logit s give the mean of their values and lse = s + ln n."""
+    g = _gen(15)
+    n, D = 7, 8
+    q = _randn(g, 1, 1, 1, D)
+    k = _randn(g, 1, 1, 1, D).expand(1, n, 1, D).contiguous()
+    v = _randn(g, 1, n, 1, D)
+    out, lse = orc.attend(q, k, v, scale=0.9)
+    s = 0.9 * float((q[0, 0, 0] * k[0, 0, 0]).sum())
+    _close(out[0, 0, 0], v[0, :, 0].mean(0).numpy(), what="mean")
+    assert abs(lse[0, 0, 0] - (s + math.log(n))) <= TOL
+
+
+def pin_constant_values(orc):
+    """V identical for every key gives that value whatever the scores."""
+    g = _gen(16)
+    q = _randn(g, 2, 3, 4, 8) * 5
+    k = _randn(g, 2, 17, 2, 8)
+    c = _randn(g, 8)
+    v = c.view(1, 1, 1, 8).expand(2, 17, 2, 8).contiguous()
+    out, _ = orc.attend(q, k, v, scale=1.3, seq_lens=torch.tensor([17, 4]), causal=True, window=6)
+    for idx in np.ndindex(2, 3, 4):
+        _close(out[idx], c.numpy(), tol=1e-13, what="constant V")
+
+
+def pin_large_logits(orc):
+    """Logits near +-1000 (exp overflows without the max shift) match logsumexp."""
+    q = torch.tensor([[[[1.0, 0.0]]]], dtype=torch.float64)
+    k = torch.tensor([[[1000.0, 0]], [[999.0, 0]], [[-1000.0, 0]]], dtype=torch.float64).view(1, 3, 1, 2)
+    v = torch.tensor([[[1.0, 2.0]], [[3.0, 4.0]], [[5.0, 6.0]]], dtype=torch.float64).view(1, 3, 1, 2)
+    out, lse = orc.attend(q, k, v, scale=1.0)
+    logits = torch.tensor([1000.0, 999.0, -1000.0], dtype=torch.float64)
+    w = torch.softmax(logits, 0)
+    _close(lse[0, 0, 0], float(torch.logsumexp(logits, 0)), what="lse")
+    _close(out[0, 0, 0], (w[:, None] * v[0, :, 0]).sum(0).numpy(), what="out")
+
+
+def pin_empty_rows(orc):
+    """No visible key: out = 0 and lse = -inf (zero-length sequence, empty key range)."""
+    g = _gen(17)
+    q = _randn(g, 2, 1, 2, 4)
+    k = _randn(g, 2, 5, 1, 4)
+    v = _randn(g, 2, 5, 1, 4)
+    out, lse = orc.attend(q, k, v, scale=1.0, seq_lens=torch.tensor([0, 5], dtype=torch.int32))
+    assert np.all(out[0] == 0) and np.all(lse[0] == -np.inf)
+    assert np.all(np.isfinite(lse[1]))
+    out, lse = orc.attend(q, k, v, scale=1.0, key_range=(5, 9))
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+def pin_paged_equals_contiguous(orc):
+    """The same logical cache scattered over a permuted page pool gives bit-identical results."""
+    g = _gen(18)
+    B, Q, Hq, Hkv, D, P = 3, 2, 4, 2, 8, 4
+    lens = [13, 4, 9]
+    L = max(lens)
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    npb = [(x + P - 1) // P for x in lens]
+    perm = torch.randperm(sum(npb) + 3, generator=g)
+    kp = torch.full((sum(npb) + 3, P, Hkv, D), float("nan"), dtype=torch.float64)
+    vp = kp.clone()
+    bt = torch.full((B, max(npb)), -1, dtype=torch.int32)
+    i = 0
+    for b in range(B):
+        for p in range(npb[b]):
+            phys = int(perm[i])
+            i += 1
+            bt[b, p] = phys
+            n = min(P, lens[b] - p * P)
+            kp[phys, :n] = k[b, p * P:p * P + n]
+            vp[phys, :n] = v[b, p * P:p * P + n]
+    sl = torch.tensor(lens, dtype=torch.int32)
+    a = orc.attend(q, k, v, scale=0.6, seq_lens=sl, causal=True, window=5)
+    b_ = orc.attend(q, kp, vp, scale=0.6, seq_lens=sl, block_table=bt, page_size=P, causal=True, window=5)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1]), "paged != contiguous"
+
+
+def pin_layout_and_rows(orc):
+    """Head-major storage viewed token-major equals a token-major copy, and a row subset equals
+    the same rows of the full result (both bit-identical)."""
+    g = _gen(19)
+    B, Q, Hq, Hkv, D, L = 2, 1, 8, 4, 8, 11
+    q = _randn(g, B, Q, Hq, D)
+    kh = _randn(g, B, Hkv, L, D)
+    vh = _randn(g, B, Hkv, L, D)
+    k_view, v_view = kh.permute(0, 2, 1, 3), vh.permute(0, 2, 1, 3)
+    a = orc.attend(q, k_view, v_view, scale=0.4)
+    b_ = orc.attend(q, k_view.contiguous(), v_view.contiguous(), scale=0.4)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1])
+    rows = [15, 0, 7, 8]
+    o, l_ = orc.attend(q, k_view, v_view, scale=0.4, rows=rows)
+    flat_o, flat_l = a[0].reshape(-1, D), a[1].reshape(-1)
+    assert np.array_equal(o, flat_o[rows]) and np.array_equal(l_, flat_l[rows])
+
+
+def pin_widening(orc):
+    """bf16 and fp32 inputs are widened exactly: same result as the same values given in fp64."""
+    g = _gen(20)
+    for dt in (torch.bfloat16, torch.float32):
+        q = _randn(g, 1, 1, 2, 8, dtype=dt)
+        k = _randn(g, 1, 6, 1, 8, dtype=dt)
+        v = _randn(g, 1, 6, 1, 8, dtype=dt)
+        a = orc.attend(q, k, v, scale=0.25)
+        b_ = orc.attend(q.double(), k.double(), v.double(), scale=0.25)
+        assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1]), f"widening {dt}"
+
+
+def pin_mla_two_part_score(orc):
+    """MLA: score = q_nope.ckv + q_pe.kpe with V = ckv equals attention on the concatenated
+    576-style key (V = its first columns), and equals SDPA on it."""
+    g = _gen(21)
+    B, H, L, Dn, Dr = 2, 4, 10, 8, 4
+    qn = _randn(g, B, 1, H, Dn)
+    qp = _randn(g, B, 1, H, Dr)
+    ckv = _randn(g, B, L, 1, Dn)
+    kpe = _randn(g, B, L, 1, Dr)
+    lens = torch.tensor([10, 6], dtype=torch.int32)
+    o1, l1 = orc.attend(qn, ckv, ckv, q2=qp, k2=kpe, scale=0.2, seq_lens=lens)
+    qcat = torch.cat([qn, qp], dim=-1)
+    kcat = torch.cat([ckv, kpe], dim=-1)
+    o2, l2 = orc.attend(qcat, kcat, kcat[..., :Dn], scale=0.2, seq_lens=lens)
+    _close(o1, o2, what="two-part vs concatenated out")
+    _close(l1, l2, what="two-part vs concatenated lse")
+    ro, rl = _sdpa(qcat, kcat, kcat[..., :Dn].contiguous(), 0.2, _library_mask(B, 1, L, lens, False, 0))
+    _close(o1, ro, what="MLA vs SDPA out")
+    _close(l1, rl, what="MLA vs SDPA lse")
+
+
+def pin_merge_closed_form(orc):
+    """Two partials with lse (0, ln 3) weigh 1 : 3; merged lse = ln 4."""
+    po = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    pl = np.array([[0.0, math.log(3.0)]])
+    out, lse = orc.merge(po, pl)
+    _close(out[0], [0.25, 0.75], what="merged out")
+    _close(lse[0], math.log(4.0), what="merged lse")
+
+
+def pin_merge_identities(orc):
+    """S = 1 is the identity; a partial merged with itself keeps o and gains ln 2; an empty
+    (0, -inf) slot changes nothing; all-empty gives (0, -inf)."""
+    g = np.random.default_rng(22)
+    po = g.standard_normal((5, 1, 6))
+    pl = g.standard_normal((5, 1))
+    o, l_ = orc.merge(po, pl)
+    _close(o, po[:, 0], what="S=1 out")
+    _close(l_, pl[:, 0], what="S=1 lse")
+    o, l_ = orc.merge(np.concatenate([po, po], 1), np.concatenate([pl, pl], 1))
+    _close(o, po[:, 0], tol=1e-14, what="self-merge out")
+    _close(l_, pl[:, 0] + math.log(2.0), tol=1e-14, what="self-merge lse")
+    o, l_ = orc.merge(np.concatenate([po, np.zeros_like(po)], 1),
+                      np.concatenate([pl, np.full_like(pl, -np.inf)], 1))
+    _close(o, po[:, 0], what="empty slot out")
+    _close(l_, pl[:, 0], what="empty slot lse")
+    o, l_ = orc.merge(np.zeros((2, 3, 4)), np.full((2, 3), -np.inf))
+    assert np.all(o == 0) and np.all(l_ == -np.inf)
+
+
+def pin_split_then_merge(orc):
+    """Attention over key ranges [s*c, (s+1)*c) merged with the LSE weights equals the unsplit
+    result, including an empty trailing range."""
+    g = _gen(23)
+    B, Q, Hq, Hkv, D, L = 2, 2, 4, 2, 8, 37
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    lens = torch.tensor([37, 23], dtype=torch.int32)
+    whole_o, whole_l = orc.attend(q, k, v, scale=0.45, seq_lens=lens, causal=True)
+    c = 10
+    parts = [orc.attend(q, k, v, scale=0.45, seq_lens=lens, causal=True, key_range=(s * c, (s + 1) * c))
+             for s in range(5)]
+    po = np.stack([p[0].reshape(-1, D) for p in parts], axis=1)
+    pl = np.stack([p[1].reshape(-1) for p in parts], axis=1)
+    assert np.all(pl[:, 4] == -np.inf) and np.all(po[:, 4] == 0)
+    mo, ml = orc.merge(po, pl)
+    _close(mo, whole_o.reshape(-1, D), what="merged out")
+    _close(ml, whole_l.reshape(-1), what="merged lse")
+
+
+def pin_key_order_invariance(orc):
+    """Reordering the keys of an unmasked contiguous cache leaves the result unchanged."""
+    g = _gen(24)
+    q = _randn(g, 1, 1, 3, 8)
+    k = _randn(g, 1, 12, 3, 8)
+    v = _randn(g, 1, 12, 3, 8)
+    perm = torch.randperm(12, generator=g)
+    a = orc.attend(q, k, v, scale=0.8)
+    b_ = orc.attend(q, k[:, perm].contiguous(), v[:, perm].contiguous(), scale=0.8)
+    _close(a[0], b_[0], what="out")
+    _close(a[1], b_[1], what="lse")
+
+
+ALL_PINS = [
+    pin_library_attention, pin_library_causal_window, pin_library_block_list, pin_golden_visibility,
+    pin_one_visible_key, pin_identical_keys, pin_constant_values, pin_large_logits, pin_empty_rows,
+    pin_paged_equals_contiguous, pin_layout_and_rows, pin_widening, pin_mla_two_part_score,
+    pin_merge_closed_form, pin_merge_identities, pin_split_then_merge, pin_key_order_invariance,
+]
+
+
+def run_all(orc):
+    """Run every pin; return the names of the pins that failed (or raised)."""
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # noqa: BLE001 - any failure of a pin counts
+            failed.append(f"{pin.__name__}: {type(e).__name__}: {str(e)[:120]}")
+    return failed

@@ -1,0 +1,92 @@
+"""Pin strength: every plausible mistake planted in a copy of the oracle must fail some pin.
+
+Each mutant is a one-line textual change to a copy of oracle/oracle.c (a dropped term, a wrong
+sign, index or operand, an off-by-one in a mask). The copy is compiled into a temporary
+directory and the whole pin suite runs against it in a child process (a broken build may crash,
+which also counts as caught). The shipped oracle is never modified.
+"""
+import concurrent.futures
+import json
+import os
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+MUTANTS = [
+    ("gqa head map", "const int64_t hkv = hq / G;", "const int64_t hkv = hq % P->num_kv_heads;"),
+    ("causal off by one", "if (P->causal && j > pos) return 0;", "if (P->causal && j >= pos) return 0;"),
+    ("window off by one", "pos - j >= P->window", "pos - j > P->window"),
+    ("query position", "int64_t pos = L - P->q_len + t;", "int64_t pos = L - 1 - t;"),
+    ("second score part dropped",
+     "acc += widen(P->q2, P->q_type, qo2 + d) * widen(P->k2, P->kv_type, ko2 + d);", "acc += 0.0;"),
+    ("scale dropped", "return P->scale * acc;", "return acc;"),
+    ("softmax sign", "double w = exp(s[j] - m);", "double w = exp(m - s[j]);"),
+    ("lse without max", "lse[i] = m + log(l);", "lse[i] = log(l);"),
+    ("no normalisation", "for (int64_t d = 0; d < P->dim_v; d++) o[d] /= l;", ""),
+    ("page slot index", "(j % P->page_size) * st[1]", "(j / P->page_size) * st[1]"),
+    ("page table index", "P->block_table[b * P->bt_stride + j / P->page_size]",
+     "P->block_table[b * P->bt_stride + j % P->page_size]"),
+    ("values read from keys", "o[d] += w * widen(P->v, P->kv_type, vo + d);",
+     "o[d] += w * widen(P->k, P->kv_type, vo + d);"),
+    ("bf16 widening", "<< 16;", "<< 15;"),
+    ("block id off by one", "+ i * P->idx_stride[2]] == blk)", "+ i * P->idx_stride[2]] == blk + 1)"),
+    ("block of key", "int64_t blk = j / P->block_size;", "int64_t blk = j % P->block_size;"),
+    ("merge weight sign", "double w = exp(ls[s] - M);", "double w = exp(M - ls[s]);"),
+    ("merge lse without max", "lse[r] = M + log(W);", "lse[r] = log(W);"),
+    ("merge empty guard", "if (M == -INFINITY) {", "if (0) {"),
+    ("empty row lse", "lse[i] = -INFINITY;", "lse[i] = 0.0;"),
+    ("key range end", "j >= P->key_hi", "j > P->key_hi"),
+    ("sequence length of row", "P->seq_lens[b] : P->kv_len", "P->seq_lens[0] : P->kv_len"),
+    ("query token of row", "const int64_t t = (r / P->num_q_heads) % P->q_len;",
+     "const int64_t t = r % P->q_len;"),
+    ("q token stride", "t * P->q_stride[1]", "t * P->q_stride[2]"),
+    ("running max", "if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
+    ("merge normalisation", "for (int32_t d = 0; d < dim_v; d++) o[d] /= W;", ""),
+]
+
+_CHILD = """
+import json, sys
+sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+import oracle, oracle_pins
+failed = oracle_pins.run_all(oracle.Oracle({lib!r}))
+print(json.dumps(failed))
+"""
+
+
+def _run_mutant(tmp, idx, find, repl):
+    src = open(oracle.SOURCE).read()
+    assert src.count(find) == 1, f"mutant anchor not found exactly once: {find!r}"
+    path = os.path.join(tmp, f"m{idx}.c")
+    with open(path, "w") as f:
+        f.write(src.replace(find, repl))
+    lib = os.path.join(tmp, f"libm{idx}.so")
+    subprocess.run(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", path, "-o", lib, "-lm"],
+                   check=True, capture_output=True)
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    r = subprocess.run([sys.executable, "-c", _CHILD.format(root=ROOT, tests=HERE, lib=lib)],
+                       capture_output=True, text=True, timeout=300, env=env)
+    if r.returncode != 0:
+        return ["child exited with status %d" % r.returncode]
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def test_every_mutant_is_caught():
+    with tempfile.TemporaryDirectory() as tmp:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+            futs = {name: ex.submit(_run_mutant, tmp, i, f, r) for i, (name, f, r) in enumerate(MUTANTS)}
+            survivors = [name for name, fut in futs.items() if not fut.result()]
+    assert not survivors, f"mutants no pin caught: {survivors}"
+
+
+@pytest.mark.parametrize("name,find,repl", MUTANTS[:1])
+def test_unmutated_copy_passes(name, find, repl):
+    """Control: the same child-process harness on an unmodified copy reports no failure."""
+    with tempfile.TemporaryDirectory() as tmp:
+        assert _run_mutant(tmp, 0, find, find) == []
