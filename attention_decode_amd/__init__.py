@@ -1,0 +1,13 @@
+"""MI355X (gfx950) single-step decode attention: split-KV partial passes + LSE merge over
+contiguous, paged and block-sparse KV caches, and an MLA variant.
+
+The compute runs in the HIP library libattn_decode.so (C ABI in include/attn_decode.h); this
+package is its thin ctypes binding (same entry-point names), the seeded workload generators and
+a prepared-step helper. Importing the package does not load the library; the first call does,
+and raises if it is not built.
+"""
+from ._abi import (  # noqa: F401
+    AD_BF16, AD_F32, AD_MAX_SPLITS, ADError, attn_decode_last_error, attn_decode_merge, attn_decode_mla,
+    attn_decode_paged, attn_decode_plan, attn_decode_splitkv, attn_decode_workspace_size, lib, make_args,
+    make_paged, make_sparse,
+)

@@ -1,0 +1,202 @@
+"""ctypes binding of include/attn_decode.h.
+
+Argument marshalling only: every function here fills the C descriptors from torch tensors
+(device memory, element strides, the current HIP stream) and calls the library. All of the
+decode step runs in the library's HIP kernels. There is no fallback: if the library is not
+built, or a call is rejected, an exception says so.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libattn_decode.so")
+
+AD_F32, AD_BF16 = 0, 1
+AD_MAX_SPLITS = 256
+STATUS = {0: "AD_OK", -1: "AD_E_NULL", -2: "AD_E_DTYPE", -3: "AD_E_SHAPE", -4: "AD_E_ALIGN",
+          -5: "AD_E_UNSUPPORTED", -6: "AD_E_WORKSPACE", -7: "AD_E_RANGE"}
+_DTYPE = {torch.float32: AD_F32, torch.bfloat16: AD_BF16}
+
+I64x3 = ctypes.c_int64 * 3
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32), ("head_dim_v", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("q_stride", I64x3),
+        ("k", ctypes.c_void_p), ("k_stride", I64x3),
+        ("v", ctypes.c_void_p), ("v_stride", I64x3),
+        ("seq_lens", ctypes.c_void_p), ("kv_len_max", ctypes.c_int32),
+        ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("out_stride", I64x3),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+class Paged(ctypes.Structure):
+    _fields_ = [("block_table", ctypes.c_void_p), ("bt_stride", ctypes.c_int64), ("page_size", ctypes.c_int32)]
+
+
+class Sparse(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_void_p), ("block_idx", ctypes.c_void_p),
+                ("nb_stride", ctypes.c_int64 * 2), ("idx_stride", I64x3),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32)]
+
+
+class ADError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} returned {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+_LIB = None
+
+
+def lib():
+    """The loaded HIP library; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIBRARY):
+            raise RuntimeError(f"{LIBRARY} is missing: build it with `python -m attention_decode_amd.build` "
+                               "(there is no fallback path)")
+        L = ctypes.CDLL(LIBRARY)
+        P = ctypes.POINTER
+        L.attn_decode_plan.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), P(ctypes.c_int32), P(ctypes.c_int32)]
+        L.attn_decode_workspace_size.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32]
+        L.attn_decode_workspace_size.restype = ctypes.c_size_t
+        L.attn_decode_splitkv.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_decode_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_decode_paged.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_mla.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
+                                      P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_last_error.restype = ctypes.c_char_p
+        for fn in ("attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
+                   "attn_decode_mla"):
+            getattr(L, fn).restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def attn_decode_last_error() -> str:
+    return lib().attn_decode_last_error().decode()
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise ADError(fn, rc, attn_decode_last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _s3(t):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D tensor")
+    return I64x3(*t.stride()[:3])
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, window=0, out=None, lse=None,
+              head_dim_qk=None):
+    """Fill an ad_decode_args from tensors (q [B,Q,Hq,D]; k/v token-major 4-D views)."""
+    a = DecodeArgs()
+    if q.dtype not in _DTYPE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    a.dtype = _DTYPE[q.dtype]
+    a.batch, a.q_len, a.num_q_heads = q.shape[0], q.shape[1], q.shape[2]
+    a.num_kv_heads = k.shape[2]
+    a.head_dim_qk = q.shape[3] if head_dim_qk is None else head_dim_qk
+    a.head_dim_v = (v if v is not None else k).shape[3]
+    a.scale = float(scale)
+    a.q, a.q_stride = _ptr(q), _s3(q)
+    a.k, a.k_stride = _ptr(k), _s3(k)
+    if v is not None:
+        a.v, a.v_stride = _ptr(v), _s3(v)
+    a.seq_lens = _ptr(seq_lens)
+    a.kv_len_max = int(k.shape[1] if kv_len_max is None else kv_len_max)
+    a.causal, a.window = int(bool(causal)), int(window)
+    if out is not None:
+        a.out, a.out_stride = _ptr(out), _s3(out)
+    a.lse = _ptr(lse)
+    return a
+
+
+def make_paged(block_table, page_size):
+    p = Paged()
+    p.block_table = _ptr(block_table)
+    p.bt_stride = block_table.stride(0)
+    p.page_size = int(page_size)
+    return p
+
+
+def make_sparse(num_blocks, block_idx, block_size):
+    s = Sparse()
+    s.num_blocks, s.block_idx = _ptr(num_blocks), _ptr(block_idx)
+    s.nb_stride = (ctypes.c_int64 * 2)(*num_blocks.stride())
+    s.idx_stride = I64x3(*block_idx.stride())
+    s.block_size = int(block_size)
+    s.max_blocks = int(block_idx.shape[-1])
+    return s
+
+
+# ------------------------------------------------------------------------------ entry points
+def attn_decode_plan(args: DecodeArgs, paged: Paged | None = None, sparse: Sparse | None = None):
+    S, C = ctypes.c_int32(), ctypes.c_int32()
+    _check("attn_decode_plan", lib().attn_decode_plan(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                                                      ctypes.byref(sparse) if sparse else None,
+                                                      ctypes.byref(S), ctypes.byref(C)))
+    return S.value, C.value
+
+
+def attn_decode_workspace_size(args: DecodeArgs, paged: Paged | None = None, num_splits: int = 0) -> int:
+    n = lib().attn_decode_workspace_size(ctypes.byref(args), ctypes.byref(paged) if paged else None, num_splits)
+    if n == 0:
+        raise ADError("attn_decode_workspace_size", 0, attn_decode_last_error())
+    return n
+
+
+def attn_decode_splitkv(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, num_splits: int, part_o,
+                        part_lse, stream=None):
+    _check("attn_decode_splitkv",
+           lib().attn_decode_splitkv(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                                     ctypes.byref(sparse) if sparse else None, num_splits,
+                                     _ptr(part_o), _ptr(part_lse), _stream(stream)))
+
+
+def attn_decode_merge(part_o, part_lse, num_splits, out, lse=None, stream=None):
+    """part_o [B,Q,Hq,S,Dv] fp32, part_lse [B,Q,Hq,S] -> out [B,Q,Hq,Dv] (any strides), lse [B,Q,Hq]."""
+    B, Q, Hq, _, Dv = part_o.shape
+    _check("attn_decode_merge",
+           lib().attn_decode_merge(_ptr(part_o), _ptr(part_lse), num_splits, B, Q, Hq, Dv, _DTYPE[out.dtype],
+                                   _ptr(out), I64x3(*out.stride()[:3]), _ptr(lse), _stream(stream)))
+
+
+def attn_decode_paged(args: DecodeArgs, paged: Paged, num_splits: int, workspace, stream=None):
+    _check("attn_decode_paged",
+           lib().attn_decode_paged(ctypes.byref(args), ctypes.byref(paged), num_splits, _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_mla(args: DecodeArgs, kpe, q_pe, paged: Paged, num_splits: int, workspace, stream=None):
+    _check("attn_decode_mla",
+           lib().attn_decode_mla(ctypes.byref(args), _ptr(kpe), _s3(kpe), _ptr(q_pe), _s3(q_pe),
+                                 ctypes.byref(paged), num_splits, _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)))

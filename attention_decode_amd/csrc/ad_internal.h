@@ -1,0 +1,75 @@
+// ad_internal.h -- parameter blocks shared by the host entry points (api.cpp) and the kernel
+// launchers (*.hip). Not installed; the public interface is include/attn_decode.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ad {
+
+enum KvMode : int { KV_CONTIG = 0, KV_PAGED = 1, KV_SPARSE = 2 };
+enum Dtype : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// Largest page-id / block-id window one work unit stages in LDS (tokens per split / page + 2).
+constexpr int kMapCapacity = 1040;
+
+// One partial pass: every work unit is (split s, KV head h, sequence b).
+struct PartialParams {
+    const void *q;
+    int64_t q_s[3];       // {b, t, hq}
+    const void *k;
+    int64_t k_s[3];       // contiguous {b, token, h}; paged {page, slot, h}
+    const void *v;
+    int64_t v_s[3];
+    const int32_t *seq_lens;  // nullable: every sequence has kv_len_max keys
+    int32_t kv_len_max;
+    // paged
+    const int32_t *block_table;
+    int64_t bt_stride;
+    int32_t page_shift;
+    // block-sparse
+    const int32_t *num_blocks;
+    const int32_t *block_idx;
+    int64_t nb_s[2];
+    int64_t ix_s[3];
+    int32_t block_shift;
+    // shape
+    int32_t batch, q_len, num_q_heads, num_kv_heads, group, head_dim_v;
+    float scale_log2;     // softmax scale * log2(e): scores are kept in base-2 units
+    int32_t causal, window;
+    int32_t num_splits, chunk;  // split s covers [s*chunk, (s+1)*chunk) of the (virtual) key range
+    int32_t write_empty;        // 1: splits past the end still write (0, -inf); 0: they do nothing
+    float *part_o;              // [rows][num_splits][head_dim_v]
+    float *part_lse;            // [rows][num_splits]
+    // MLA second score part (rope): q_pe rows and kpe rows, 64 columns
+    const void *q2;
+    int64_t q2_s[3];
+    const void *k2;
+    int64_t k2_s[3];
+};
+
+struct MergeParams {
+    const float *part_o;
+    const float *part_lse;
+    int32_t num_splits;
+    int32_t rows;             // batch * q_len * num_q_heads
+    int32_t head_dim_v;
+    int32_t q_len, num_q_heads;
+    // count_by_len: row b merges only min(num_splits, ceil(L_b / chunk)) splits, L_b = seq_lens[b]
+    // (or kv_len_max when seq_lens is NULL) -- the splits a paged pass actually wrote.
+    int32_t count_by_len;
+    const int32_t *seq_lens;
+    int32_t kv_len_max;
+    int32_t chunk;
+    int32_t out_dtype;
+    void *out;
+    int64_t out_s[3];
+    float *lse;
+};
+
+// Launchers (hipSuccess or the launch error). They assume the host checks already passed.
+hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, int rows_padded, int mode,
+                               hipStream_t stream);
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
+
+}  // namespace ad

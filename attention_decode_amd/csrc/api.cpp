@@ -1,0 +1,403 @@
+// api.cpp -- host side of the C ABI declared in include/attn_decode.h.
+//
+// Every entry point validates its arguments completely on the host before touching the HIP
+// runtime, so every rejection path is observable without a GPU. Then it plans the split, fills a
+// parameter block and enqueues the kernels on the caller's stream. Nothing here allocates,
+// synchronises or throws.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <cmath>
+#include <string>
+
+#include "ad_internal.h"
+#include "attn_decode.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    g_error = std::string(what) + ": " + hipGetErrorString(e);
+    return (int)e;
+}
+
+int ok() {
+    g_error.clear();
+    return AD_OK;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(int dtype) { return dtype == AD_F32 ? 4 : 2; }
+
+bool strides_aligned(const int64_t s[3], int es) {
+    for (int i = 0; i < 3; ++i)
+        if ((s[i] * es) % 16 != 0) return false;
+    return true;
+}
+
+int log2_exact(int x) {
+    int s = 0;
+    while ((1 << s) < x) ++s;
+    return (1 << s) == x ? s : -1;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ validation
+enum class Path { Contig, Paged, Mla };
+
+int check_args(const ad_decode_args *a, Path path, bool need_out) {
+    if (!a) return fail(AD_E_NULL, "args is NULL");
+    if (a->dtype != AD_F32 && a->dtype != AD_BF16) return fail(AD_E_DTYPE, "dtype %d is not AD_F32 or AD_BF16", a->dtype);
+    if (a->batch < 0 || a->q_len < 1 || a->num_q_heads < 1 || a->num_kv_heads < 1)
+        return fail(AD_E_SHAPE, "batch must be >= 0 and q_len, num_q_heads, num_kv_heads >= 1");
+    if (a->num_q_heads % a->num_kv_heads)
+        return fail(AD_E_SHAPE, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", a->num_q_heads,
+                    a->num_kv_heads);
+    if (a->kv_len_max < 0) return fail(AD_E_RANGE, "kv_len_max must be >= 0");
+    if (a->window < 0) return fail(AD_E_RANGE, "window must be >= 0");
+    if (a->causal != 0 && a->causal != 1) return fail(AD_E_RANGE, "causal must be 0 or 1");
+    if (!(std::isfinite(a->scale))) return fail(AD_E_RANGE, "scale must be finite");
+    if (path == Path::Mla) {
+        if (a->dtype != AD_BF16) return fail(AD_E_UNSUPPORTED, "MLA supports bf16 only");
+        if (a->head_dim_qk != 576 || a->head_dim_v != 512 || a->num_kv_heads != 1)
+            return fail(AD_E_UNSUPPORTED, "MLA needs head_dim_qk 576, head_dim_v 512 and one KV head");
+        if (a->v && a->v != a->k)
+            return fail(AD_E_UNSUPPORTED, "MLA reads values from the latent cache: v must be NULL or equal k");
+    } else {
+        if (a->head_dim_qk != a->head_dim_v) return fail(AD_E_UNSUPPORTED, "head_dim_qk must equal head_dim_v");
+        if (a->head_dim_qk != 64 && a->head_dim_qk != 128)
+            return fail(AD_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", a->head_dim_qk);
+        const int rows = (a->num_q_heads / a->num_kv_heads) * a->q_len;
+        if (rows > 8)
+            return fail(AD_E_UNSUPPORTED, "%d query rows per KV head (G*q_len) exceed the 8 this build supports",
+                        rows);
+        if (!a->v) return fail(AD_E_NULL, "v is NULL");
+    }
+    if (!a->q || !a->k) return fail(AD_E_NULL, "q or k is NULL");
+    const int es = elem_bytes(a->dtype);
+    if (!aligned16(a->q) || !aligned16(a->k) || (a->v && !aligned16(a->v)))
+        return fail(AD_E_ALIGN, "q, k and v must be 16-byte aligned");
+    if (!strides_aligned(a->q_stride, es) || !strides_aligned(a->k_stride, es) ||
+        (a->v && !strides_aligned(a->v_stride, es)))
+        return fail(AD_E_ALIGN, "q/k/v strides must keep every row 16-byte aligned");
+    if (need_out) {
+        if (!a->out) return fail(AD_E_NULL, "out is NULL");
+        if (!aligned16(a->out) || !strides_aligned(a->out_stride, es))
+            return fail(AD_E_ALIGN, "out rows must be 16-byte aligned");
+        if (a->lse && (reinterpret_cast<uintptr_t>(a->lse) & 3u)) return fail(AD_E_ALIGN, "lse must be 4-byte aligned");
+    }
+    return AD_OK;
+}
+
+int check_paged(const ad_decode_args *a, const ad_paged *pg) {
+    if (!pg) return fail(AD_E_NULL, "paged is NULL");
+    if (!pg->block_table) return fail(AD_E_NULL, "block_table is NULL");
+    if (pg->page_size != 16 && pg->page_size != 32 && pg->page_size != 64)
+        return fail(AD_E_RANGE, "page_size %d is not 16, 32 or 64", pg->page_size);
+    if (pg->bt_stride < cdiv(a->kv_len_max, pg->page_size))
+        return fail(AD_E_RANGE, "bt_stride %lld is smaller than ceil(kv_len_max / page_size)",
+                    (long long)pg->bt_stride);
+    return AD_OK;
+}
+
+int check_sparse(const ad_sparse *sp) {
+    if (!sp->num_blocks || !sp->block_idx) return fail(AD_E_NULL, "num_blocks or block_idx is NULL");
+    const int sh = log2_exact(sp->block_size);
+    if (sh < 4 || sh > 12) return fail(AD_E_RANGE, "block_size %d is not a power of two in [16, 4096]", sp->block_size);
+    if (sp->max_blocks < 0) return fail(AD_E_RANGE, "max_blocks must be >= 0");
+    return AD_OK;
+}
+
+// ------------------------------------------------------------------ planning
+int device_cus(int *cus) {
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+        *cus = cache[dev];
+        return AD_OK;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    *cus = n;
+    return AD_OK;
+}
+
+int env_int(const char *name) {
+    const char *s = getenv(name);
+    return s ? atoi(s) : 0;
+}
+
+struct Plan {
+    int splits;
+    int chunk;
+};
+
+// Largest key range the splits partition (virtual for a block list).
+int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
+    return sp ? (int64_t)sp->max_blocks * sp->block_size : (int64_t)a->kv_len_max;
+}
+
+int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
+                Plan *out) {
+    const int64_t span = key_span(a, sp);
+    int S = requested > 0 ? requested : env_int("AD_NUM_SPLITS");
+    if (S < 0 || S > AD_MAX_SPLITS) return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", S, AD_MAX_SPLITS);
+    if (S == 0) {
+        int cus = 0;
+        int rc = device_cus(&cus);
+        if (rc != AD_OK) return rc;
+        const int units = a->batch * (path == Path::Mla ? 1 : a->num_kv_heads);
+        // Ragged lengths: assume the average sequence is half the bound when planning.
+        const int64_t est = (a->seq_lens && !sp) ? std::max<int64_t>(span / 2, 1) : std::max<int64_t>(span, 1);
+        const int target = (env_int("AD_TARGET_UNITS") > 0 ? env_int("AD_TARGET_UNITS") : 8) * cus;
+        int64_t chunk = cdiv((int64_t)units * est, target);
+        const int64_t lo = path == Path::Mla ? 256 : 256, hi = 4096;
+        chunk = std::min<int64_t>(std::max<int64_t>(chunk, lo), hi);
+        S = (int)std::min<int64_t>(std::max<int64_t>(cdiv(span, chunk), 1), AD_MAX_SPLITS);
+    }
+    int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
+    chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);
+    const int grain = pg ? pg->page_size : (sp ? sp->block_size : 16);
+    if (pg || sp) {
+        if (cdiv(chunk, grain) + 2 > ad::kMapCapacity)
+            return fail(AD_E_RANGE, "%d splits leave %lld keys per split; at most %d pages/blocks per split", S,
+                        (long long)chunk, ad::kMapCapacity - 2);
+    }
+    if (chunk > (1 << 30)) return fail(AD_E_RANGE, "key range too long");
+    out->splits = S;
+    out->chunk = (int)chunk;
+    return AD_OK;
+}
+
+ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
+    ad::PartialParams p{};
+    p.q = a->q;
+    p.k = a->k;
+    p.v = a->v ? a->v : a->k;
+    for (int i = 0; i < 3; ++i) {
+        p.q_s[i] = a->q_stride[i];
+        p.k_s[i] = a->k_stride[i];
+        p.v_s[i] = a->v ? a->v_stride[i] : a->k_stride[i];
+    }
+    p.seq_lens = a->seq_lens;
+    p.kv_len_max = a->kv_len_max;
+    p.batch = a->batch;
+    p.q_len = a->q_len;
+    p.num_q_heads = a->num_q_heads;
+    p.num_kv_heads = a->num_kv_heads;
+    p.group = a->num_q_heads / a->num_kv_heads;
+    p.head_dim_v = a->head_dim_v;
+    p.scale_log2 = a->scale * kLog2e;
+    p.causal = a->causal;
+    p.window = a->window;
+    p.num_splits = pl.splits;
+    p.chunk = pl.chunk;
+    return p;
+}
+
+int rows_padded(const ad_decode_args *a) {
+    const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
+    return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t partial_bytes(const ad_decode_args *a, int S, size_t *lse_offset) {
+    const size_t rows = (size_t)a->batch * a->q_len * a->num_q_heads;
+    const size_t o = align256(rows * S * a->head_dim_v * sizeof(float));
+    if (lse_offset) *lse_offset = o;
+    return o + align256(rows * S * sizeof(float));
+}
+
+int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, bool count_by_len, int chunk,
+              hipStream_t stream) {
+    ad::MergeParams m{};
+    m.part_o = po;
+    m.part_lse = pl;
+    m.num_splits = S;
+    m.rows = a->batch * a->q_len * a->num_q_heads;
+    m.head_dim_v = a->head_dim_v;
+    m.q_len = a->q_len;
+    m.num_q_heads = a->num_q_heads;
+    m.count_by_len = count_by_len ? 1 : 0;
+    m.seq_lens = a->seq_lens;
+    m.kv_len_max = a->kv_len_max;
+    m.chunk = chunk;
+    m.out_dtype = a->dtype;
+    m.out = a->out;
+    for (int i = 0; i < 3; ++i) m.out_s[i] = a->out_stride[i];
+    m.lse = a->lse;
+    hipError_t e = ad::launch_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "merge launch");
+    return AD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t *num_splits,
+                     int32_t *chunk) {
+    const bool mla = args && args->head_dim_qk == 576 && args->head_dim_v == 512;
+    const Path path = mla ? Path::Mla : (paged ? Path::Paged : Path::Contig);
+    int rc = check_args(args, path, false);
+    if (rc != AD_OK) return rc;
+    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, sparse, path, 0, &pl)) != AD_OK) return rc;
+    if (num_splits) *num_splits = pl.splits;
+    if (chunk) *chunk = pl.chunk;
+    return ok();
+}
+
+size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits) {
+    const bool mla = args && args->head_dim_qk == 576 && args->head_dim_v == 512;
+    const Path path = mla ? Path::Mla : (paged ? Path::Paged : Path::Contig);
+    if (check_args(args, path, false) != AD_OK) return 0;
+    if (paged && check_paged(args, paged) != AD_OK) return 0;
+    Plan pl{};
+    if (plan_splits(args, paged, nullptr, path, num_splits, &pl) != AD_OK) return 0;
+    ok();
+    return partial_bytes(args, pl.splits, nullptr);
+}
+
+int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                        int32_t num_splits, float *part_o, float *part_lse, void *stream) {
+    int rc = check_args(args, paged ? Path::Paged : Path::Contig, false);
+    if (rc != AD_OK) return rc;
+    if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
+    if (!part_o || !part_lse) return fail(AD_E_NULL, "part_o or part_lse is NULL");
+    if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_lse) & 3u))
+        return fail(AD_E_ALIGN, "part_o must be 16-byte and part_lse 4-byte aligned");
+    if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
+        return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
+    if (args->batch == 0) return ok();
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, sparse, paged ? Path::Paged : Path::Contig, num_splits, &pl)) != AD_OK)
+        return rc;
+    ad::PartialParams p = base_params(args, pl);
+    int mode = ad::KV_CONTIG;
+    if (sparse) {
+        mode = ad::KV_SPARSE;
+        p.num_blocks = sparse->num_blocks;
+        p.block_idx = sparse->block_idx;
+        p.nb_s[0] = sparse->nb_stride[0];
+        p.nb_s[1] = sparse->nb_stride[1];
+        for (int i = 0; i < 3; ++i) p.ix_s[i] = sparse->idx_stride[i];
+        p.block_shift = log2_exact(sparse->block_size);
+    } else if (paged) {
+        mode = ad::KV_PAGED;
+        p.block_table = paged->block_table;
+        p.bt_stride = paged->bt_stride;
+        p.page_shift = log2_exact(paged->page_size);
+    }
+    p.write_empty = 1;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    hipError_t e = ad::launch_partial_valu(p, args->dtype, args->head_dim_qk, rows_padded(args), mode,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "split-KV launch");
+    return ok();
+}
+
+int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_splits, int32_t batch, int32_t q_len,
+                      int32_t num_q_heads, int32_t head_dim_v, int32_t out_dtype, void *out,
+                      const int64_t out_stride[3], float *lse, void *stream) {
+    if (!part_o || !part_lse || !out || !out_stride) return fail(AD_E_NULL, "part_o, part_lse, out or out_stride is NULL");
+    if (out_dtype != AD_F32 && out_dtype != AD_BF16) return fail(AD_E_DTYPE, "out_dtype %d unknown", out_dtype);
+    if (num_splits < 1 || num_splits > AD_MAX_SPLITS)
+        return fail(AD_E_RANGE, "num_splits %d outside [1, %d]", num_splits, AD_MAX_SPLITS);
+    if (batch < 0 || q_len < 1 || num_q_heads < 1) return fail(AD_E_SHAPE, "bad batch / q_len / num_q_heads");
+    if (head_dim_v != 64 && head_dim_v != 128 && head_dim_v != 256 && head_dim_v != 512 && head_dim_v != 1024)
+        return fail(AD_E_UNSUPPORTED, "head_dim_v %d not in {64, 128, 256, 512, 1024}", head_dim_v);
+    if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_lse) & 3u) || !aligned16(out) ||
+        !strides_aligned(out_stride, elem_bytes(out_dtype)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+        return fail(AD_E_ALIGN, "misaligned part_o / part_lse / out / lse");
+    if (batch == 0) return ok();
+    ad_decode_args a{};
+    a.dtype = out_dtype;
+    a.batch = batch;
+    a.q_len = q_len;
+    a.num_q_heads = num_q_heads;
+    a.head_dim_v = head_dim_v;
+    a.out = out;
+    for (int i = 0; i < 3; ++i) a.out_stride[i] = out_stride[i];
+    a.lse = lse;
+    int rc = run_merge(&a, part_o, part_lse, num_splits, false, 1, static_cast<hipStream_t>(stream));
+    return rc == AD_OK ? ok() : rc;
+}
+
+int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    int rc = check_args(args, Path::Paged, true);
+    if (rc != AD_OK) return rc;
+    if ((rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
+        return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
+    if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
+    if (args->batch == 0) return ok();
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, nullptr, Path::Paged, num_splits, &pl)) != AD_OK) return rc;
+    size_t lse_off = 0;
+    const size_t need = partial_bytes(args, pl.splits, &lse_off);
+    if (workspace_bytes < need)
+        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    float *po = static_cast<float *>(workspace);
+    float *plse = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
+    ad::PartialParams p = base_params(args, pl);
+    p.block_table = paged->block_table;
+    p.bt_stride = paged->bt_stride;
+    p.page_shift = log2_exact(paged->page_size);
+    p.write_empty = 0;
+    p.part_o = po;
+    p.part_lse = plse;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = ad::launch_partial_valu(p, args->dtype, args->head_dim_qk, rows_padded(args), ad::KV_PAGED, s);
+    if (e != hipSuccess) return hip_fail(e, "paged split-KV launch");
+    // Splits past a sequence's end wrote nothing: row b merges only ceil(L_b / chunk) of them.
+    rc = run_merge(args, po, plse, pl.splits, true, pl.chunk, s);
+    return rc == AD_OK ? ok() : rc;
+}
+
+int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3], const void *q_pe,
+                    const int64_t q_pe_stride[3], const ad_paged *paged, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    int rc = check_args(args, Path::Mla, true);
+    if (rc != AD_OK) return rc;
+    if ((rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (!kpe || !q_pe || !kpe_stride || !q_pe_stride) return fail(AD_E_NULL, "kpe / q_pe or their strides are NULL");
+    (void)num_splits;
+    (void)workspace;
+    (void)workspace_bytes;
+    (void)stream;
+    return fail(AD_E_UNSUPPORTED, "MLA kernel not built yet");
+}
+
+const char *attn_decode_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

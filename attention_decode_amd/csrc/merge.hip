@@ -1,0 +1,106 @@
+// merge.hip -- LSE-weighted combine of split partials (mslk splitk_kernels.py, _splitK_reduce):
+//
+//   M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
+//   lse = M + ln sum_s w_s;   M = -inf  ->  out = 0, lse = -inf.
+//
+// One wave per output row; lane l owns head_dim_v / 64 consecutive output columns, so every
+// partial row is read with one coalesced wave-wide load. The split weights are wave-uniform:
+// the row index is made uniform with readfirstlane, so the LSE reads become scalar loads and the
+// exponentials are computed once per split per lane without any cross-lane traffic beyond the
+// max. Ragged batches (paged path) merge only the ceil(L_b / chunk) splits that hold keys.
+#include "ad_internal.h"
+
+#include <math.h>
+
+namespace ad {
+namespace {
+
+constexpr int kRowsPerBlock = 4;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+template <int VEC, bool OUT_BF16>
+__global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergeParams p) {
+    const int lane = threadIdx.x & 63;
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
+    if (row >= p.rows) return;
+    const int hq = row % p.num_q_heads;
+    const int t = (row / p.num_q_heads) % p.q_len;
+    const int b = row / (p.num_q_heads * p.q_len);
+    const int Dv = p.head_dim_v;
+
+    int S = p.num_splits;
+    if (p.count_by_len) {
+        const int Lb = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
+        const int Sb = Lb > 0 ? (Lb + p.chunk - 1) / p.chunk : 0;
+        S = min(S, Sb);
+    }
+    const float *ls = p.part_lse + (int64_t)row * p.num_splits;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
+    const float ms = (M == -INFINITY) ? 0.f : M;
+
+    float o[VEC];
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) o[j] = 0.f;
+    float W = 0.f;
+    const float *po = p.part_o + (int64_t)row * p.num_splits * Dv + lane * VEC;
+    for (int s = 0; s < S; ++s) {
+        const float w = __builtin_amdgcn_exp2f((ls[s] - ms) * kLog2e);
+        W += w;
+        const float *src = po + (int64_t)s * Dv;
+        if constexpr (VEC % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < VEC; j += 4) {
+                const float4 x = *reinterpret_cast<const float4 *>(src + j);
+                o[j] += w * x.x;
+                o[j + 1] += w * x.y;
+                o[j + 2] += w * x.z;
+                o[j + 3] += w * x.w;
+            }
+        } else if constexpr (VEC == 2) {
+            const float2 x = *reinterpret_cast<const float2 *>(src);
+            o[0] += w * x.x;
+            o[1] += w * x.y;
+        } else {
+            o[0] += w * src[0];
+        }
+    }
+    const float inv = W > 0.f ? 1.f / W : 0.f;
+    char *dst = static_cast<char *>(p.out) +
+                (b * p.out_s[0] + t * p.out_s[1] + hq * p.out_s[2] + lane * VEC) * (OUT_BF16 ? 2 : 4);
+    if constexpr (OUT_BF16) {
+        __bf16 *d = reinterpret_cast<__bf16 *>(dst);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) d[j] = (__bf16)(o[j] * inv);
+    } else {
+        float *d = reinterpret_cast<float *>(dst);
+#pragma unroll
+        for (int j = 0; j < VEC; ++j) d[j] = o[j] * inv;
+    }
+    if (p.lse && lane == 0) p.lse[row] = W > 0.f ? M + __builtin_amdgcn_logf(W) * kLn2 : -INFINITY;
+}
+
+template <int VEC>
+hipError_t launch_vec(const MergeParams &p, hipStream_t stream) {
+    dim3 grid((p.rows + kRowsPerBlock - 1) / kRowsPerBlock);
+    if (p.out_dtype == DT_BF16)
+        hipLaunchKernelGGL((merge_kernel<VEC, true>), grid, dim3(64 * kRowsPerBlock), 0, stream, p);
+    else
+        hipLaunchKernelGGL((merge_kernel<VEC, false>), grid, dim3(64 * kRowsPerBlock), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeParams &p, hipStream_t stream) {
+    switch (p.head_dim_v) {
+        case 64: return launch_vec<1>(p, stream);
+        case 128: return launch_vec<2>(p, stream);
+        case 256: return launch_vec<4>(p, stream);
+        case 512: return launch_vec<8>(p, stream);
+        default: return launch_vec<16>(p, stream);
+    }
+}
+
+}  // namespace ad

@@ -1,0 +1,227 @@
+"""Decode-attention benchmark: KV-read GB/s (fraction of HBM peak) and µs per decode step.
+
+Default workload: paged GQA, bf16, batch 64, 32 q / 8 KV heads, head dim 128, page 16, ragged
+seq lens uniform in [128, 8192] over a randomly permuted page pool (seeded, synthetic).
+
+One step = the whole hot path on inputs already resident in HBM: split planning (host, done once),
+the partial split-KV pass, and the LSE merge, launched through the C ABI on torch's current
+stream. W untimed warm-up steps, then exactly K timed steps bracketed by synchronisation.
+Consecutive steps rotate over enough copies of the KV cache to exceed the 256 MB last-level cache,
+so every step reads its KV from HBM.
+
+`value` = algorithmic KV bytes per step (only keys inside each sequence, K and V once) / step time.
+`roofline` prices the dominant kernel (the partial pass) alone: the same algorithmic bytes over
+its average duration, measured with HIP events recorded on its launch stream around every timed
+launch. `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload on the host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "KV-read GB/s (% of HBM peak) and µs per decode step, GQA bf16 paged"
+LLC_BYTES = 256 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class Step:
+    """The hot path of one workload, prepared once; run(i) enqueues step i on the current stream."""
+
+    def __init__(self, w, copies):
+        import torch
+
+        from attention_decode_amd import _abi
+
+        self.w = w
+        self.abi = _abi
+        dev = w.q.device
+        B, Q, Hq, Dv = w.batch, w.q_len, w.num_q_heads, w.head_dim_v
+        self.out = torch.empty(B, Q, Hq, Dv, dtype=w.dtype, device=dev)
+        self.lse = torch.empty(B, Q, Hq, dtype=torch.float32, device=dev)
+        self.sets = []
+        for c in range(copies):
+            k = w.k if c == 0 else w.k.clone()  # .clone() of a strided view keeps its strides
+            v = w.v if c == 0 else w.v.clone()
+            a = _abi.make_args(w.q, k, v, scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max,
+                               causal=w.causal, window=w.window, out=self.out, lse=self.lse)
+            self.sets.append((a, k, v))
+        self.paged = _abi.make_paged(w.block_table, w.page_size) if w.kind == "paged" else None
+        self.sparse = _abi.make_sparse(w.num_blocks, w.block_idx, w.block_size) if w.num_blocks is not None else None
+        self.splits, self.chunk = _abi.attn_decode_plan(self.sets[0][0], self.paged, self.sparse)
+        if w.num_splits:
+            self.splits = w.num_splits
+        self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+
+    def partial(self, i):
+        a = self.sets[i % len(self.sets)][0]
+        self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.part_o, self.part_lse)
+
+    def merge(self):
+        self.abi.attn_decode_merge(self.part_o, self.part_lse, self.splits, self.out, self.lse)
+
+
+def cpu_baseline(w_cpu, budget_s=12.0):
+    """The fp64 oracle, as it stands, on whole (b, KV head) groups of the workload until about
+    budget_s seconds of host work; reported in the metric's unit (algorithmic KV GB/s)."""
+    import oracle
+
+    orc = oracle.load()
+    Hq, Hkv, Q = w_cpu.num_q_heads, w_cpu.num_kv_heads, w_cpu.q_len
+    G = Hq // Hkv
+    es = 2 if w_cpu.dtype.itemsize == 2 else 4
+    per_tok = (w_cpu.head_dim_qk + w_cpu.head_dim_v) * es
+    lens = [int(x) for x in w_cpu.seq_lens]
+    kw = dict(scale=w_cpu.scale, seq_lens=w_cpu.seq_lens, causal=w_cpu.causal, window=w_cpu.window)
+    if w_cpu.kind == "paged":
+        kw.update(block_table=w_cpu.block_table, page_size=w_cpu.page_size)
+    done_bytes, elapsed, groups = 0, 0.0, 0
+    order = [(b, h) for b in range(w_cpu.batch) for h in range(Hkv)]
+    i = 0
+    # Whole (sequence, KV head) groups in a fixed order, wrapping around, until the budget is spent.
+    while elapsed < budget_s:
+        # next chunk of groups: grow geometrically so the timing overhead stays negligible
+        n = max(1, min(len(order) - i, 2 ** min(groups.bit_length(), 6)))
+        sel = order[i:i + n]
+        rows = [(b * Q + t) * Hq + h * G + g for (b, h) in sel for t in range(Q) for g in range(G)]
+        t0 = time.perf_counter()
+        orc.attend(w_cpu.q, w_cpu.k, w_cpu.v, rows=rows, **kw)
+        elapsed += time.perf_counter() - t0
+        done_bytes += sum(lens[b] * per_tok for (b, h) in sel)
+        groups += n
+        i = (i + n) % len(order)
+    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": orc.threads(),
+            "kind": "oracle",
+            "sample": f"{groups} (sequence, KV head) groups of the {len(order)} in the workload (in order, "
+                      f"wrapping), all {G * Q} query rows each: {done_bytes / 1e6:.1f} MB of KV in {elapsed:.1f} s"}
+
+
+def load_traffic(kernel_tag):
+    """HBM traffic of the dominant kernel from committed rocprofv3 counter runs, or None when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src):
+        return None
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if h != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        log("bench.py: only --gpus 1 is supported (the decode step runs on a single GPU)")
+        sys.exit(2)
+
+    import torch
+
+    from attention_decode_amd import inputs
+
+    if not torch.cuda.is_available():
+        log("bench.py needs a GPU")
+        sys.exit(1)
+    torch.cuda.set_device(int(os.environ.get("LOCAL_RANK", "0")))
+
+    log(f"generating workload {args.workload} ...")
+    w_cpu = inputs.make(args.workload)
+    w = w_cpu.to("cuda")
+    kv_bytes = w_cpu.kv_bytes()
+    footprint = w.k.untyped_storage().nbytes() + (w.v.untyped_storage().nbytes() if w.v is not w.k else 0)
+    copies = max(1, math.ceil((1 << 30) / footprint) + 1) if footprint < (1 << 30) else 2
+    if w.kind == "mla":
+        raise SystemExit("the MLA workload is benchmarked with its own entry point (not wired here yet)")
+    step = Step(w, copies)
+    log(f"workload {w.name}: {kv_bytes / 1e6:.1f} MB KV/step, splits {step.splits} x {step.chunk} keys, "
+        f"{copies} cache copies ({footprint / 1e6:.0f} MB each)")
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step.partial(i)
+        step.merge()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step.partial(i)
+        ev[i][1].record(stream)
+        step.merge()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / K
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_ms.sort()
+    kern_avg = sum(kern_ms) / K
+    gbps = kv_bytes / (ms_step * 1e-3) / 1e9
+    achieved = kv_bytes / (kern_avg * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); partial kernel avg "
+        f"{kern_avg * 1e3:.1f} us (p10 {kern_ms[K // 10] * 1e3:.1f}, p90 {kern_ms[(9 * K) // 10] * 1e3:.1f}) "
+        f"-> {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, seeded ragged lengths and page permutation)",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim_qk, "q_len": w.q_len, "page_size": w.page_size,
+                   "kv_tokens": int(w_cpu.seq_lens.sum()), "kv_bytes_per_step": kv_bytes,
+                   "splits": step.splits, "split_keys": step.chunk, "cache_copies_rotated": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": load_traffic(f"partial_valu_{w.kind}"),
+                     "kernel": "partial_valu_kernel (split-KV partial pass)",
+                     "kernel_avg_us": round(kern_avg * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline(w_cpu, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * attn_decode.h -- C ABI of the MI355X (gfx950) single-step decode-attention library.
+ *
+ * One decode step computes, for every query row (b, t, hq),
+ *
+ *     out = softmax(scale * q . K^T + mask) . V        lse = ln sum_j exp(scale * q . k_j)
+ *
+ * for a few query rows per KV head (GQA: query head hq reads KV head hq / G, G = Hq / Hkv; the G
+ * heads x q_len tokens of one KV head are packed into one work tile, as in the PyTorch Inductor
+ * flex_decode.py.jinja template's GQA_SHARED_HEADS packing) against a long KV cache that is
+ * contiguous, paged or block-sparse. The work is split along the KV length into partial passes
+ * that each emit a normalised partial output and a natural-log LSE (mslk splitk_kernels.py,
+ * _fwd_kernel_splitK epilogue), followed by an LSE-weighted merge (the same page,
+ * _splitK_reduce). An MLA variant reads one shared latent KV head whose first 512 columns are
+ * also the values (FlashInfer attention/mla.cuh, compute_mla_qk / compute_mla_pv).
+ *
+ * Conventions for every entry point:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; descriptors (the structs and
+ *     the stride arrays) are HOST memory, read during the call only. The library allocates no
+ *     device memory, never synchronises and never throws. Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and runs asynchronously.
+ *   - Strides are in ELEMENTS. The last (feature) dimension of every tensor is contiguous, and
+ *     every row start must be 16-byte aligned.
+ *   - Return value: AD_OK (0), a negative AD_E_* code when the arguments were rejected on the
+ *     host before anything was enqueued, or a positive hipError_t when a launch failed.
+ *     attn_decode_last_error() gives a message for the calling thread's last non-OK return.
+ *   - Data contracts that are NOT checked (they live in device memory): seq_lens[b] <=
+ *     kv_len_max and >= q_len; block-table entries for the pages a sequence covers lie in
+ *     [0, pages of the pool) (entries past the sequence are never read and may hold -1);
+ *     listed sparse blocks are < ceil(kv_len_max / block_size). Keys outside a sequence, past
+ *     its last page slot, in unlisted blocks or in unreferenced pages are never read into the
+ *     result and may hold any bits (NaN included).
+ */
+#ifndef ATTN_DECODE_H
+#define ATTN_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------------------------ */
+#define AD_OK 0
+#define AD_E_NULL (-1)        /* a required pointer is NULL */
+#define AD_E_DTYPE (-2)       /* unknown or unsupported element type */
+#define AD_E_SHAPE (-3)       /* inconsistent sizes (e.g. Hq % Hkv != 0, non-positive sizes) */
+#define AD_E_ALIGN (-4)       /* a row start or the last dimension is not 16-byte aligned/contiguous */
+#define AD_E_UNSUPPORTED (-5) /* a valid request this build has no kernel for (e.g. head dim 96) */
+#define AD_E_WORKSPACE (-6)   /* workspace missing or smaller than attn_decode_workspace_size() */
+#define AD_E_RANGE (-7)       /* a count out of range (num_splits, page size, window, ...) */
+
+/* ---- element types (Q, K, V and the output share one) ------------------------------------ */
+#define AD_F32 0
+#define AD_BF16 1
+
+#define AD_MAX_SPLITS 256
+
+/*
+ * One decode step.
+ *   q      [batch, q_len, num_q_heads, head_dim_qk]    (MLA: the latent part q_nope, 512 cols)
+ *   k, v   contiguous cache: logical [batch, kv_len_max, num_kv_heads, D], strides
+ *          {per batch, per token, per head}; a head-major cache [B, Hkv, L, D] is expressed by
+ *          its strides. Paged cache: logical [pages, page_size, num_kv_heads, D] with strides
+ *          {per page, per slot, per head}, addressed through ad_paged.block_table.
+ *   out    [batch, q_len, num_q_heads, head_dim_v] in `dtype` (bf16 rounded to nearest even).
+ *   lse    [batch, q_len, num_q_heads] fp32, natural log, contiguous; NULL to skip. A row with
+ *          no visible key gets out = 0 and lse = -inf.
+ * Query t of a q_len-token query sits at position L_b - q_len + t of its sequence (its own K/V
+ * are already in the cache). With `causal`, it sees keys j <= that position (bottom-right
+ * alignment: FlashInfer mla.cuh logits_mask_; mslk splitk_kernels.py causal comment). With
+ * window W > 0 it sees only keys with position - j < W: the W most recent keys up to and
+ * including its own (TensorRT-LLM xqa mha.cu sliding window). `scale` multiplies q . k in
+ * natural-exp units and is never derived from the head dim (xqa passes qScale separately;
+ * mla.cuh and splitk_kernels.py take sm_scale).
+ */
+typedef struct ad_decode_args {
+    int32_t dtype;
+    int32_t batch, q_len, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v;
+    float scale;
+    const void *q;
+    int64_t q_stride[3];
+    const void *k;
+    int64_t k_stride[3];
+    const void *v;
+    int64_t v_stride[3];
+    const int32_t *seq_lens; /* [batch] KV lengths (incl. the q_len new tokens); NULL: all kv_len_max */
+    int32_t kv_len_max;      /* host-side bound on every seq_lens[b]; a contiguous cache's capacity */
+    int32_t causal;
+    int32_t window;          /* 0: none */
+    void *out;
+    int64_t out_stride[3];
+    float *lse;
+} ad_decode_args;
+
+/* Paged cache: logical page p of sequence b is pool page block_table[b * bt_stride + p]
+ * (mslk splitk_kernels.py paged branch; TensorRT-LLM xqa page list). page_size is 16, 32 or 64. */
+typedef struct ad_paged {
+    const int32_t *block_table;
+    int64_t bt_stride;
+    int32_t page_size;
+} ad_paged;
+
+/* Block-sparse KV (PyTorch Inductor flex_decode.py.jinja, KV_NUM_BLKS / KV_IDX): for each
+ * (b, KV head), num_blocks[b*nb_stride[0] + h*nb_stride[1]] blocks of block_size keys are listed
+ * in block_idx[b*idx_stride[0] + h*idx_stride[1] + i*idx_stride[2]], i < num_blocks, ascending.
+ * A stride of 0 broadcasts one list over that dimension. Key j contributes iff its block is
+ * listed AND the causal/window masks admit it. max_blocks bounds every num_blocks entry.
+ * block_size is a power of two in [16, 4096]. */
+typedef struct ad_sparse {
+    const int32_t *num_blocks;
+    const int32_t *block_idx;
+    int64_t nb_stride[2];
+    int64_t idx_stride[3];
+    int32_t block_size;
+    int32_t max_blocks;
+} ad_sparse;
+
+/*
+ * Split planner. Writes the split count the library would choose for this step (num_splits = 0
+ * on the calls below) to *num_splits, and the tokens per split to *chunk (either may be NULL).
+ * `paged` and `sparse` are nullable and select the path; MLA is selected by head_dim_qk == 576
+ * with head_dim_v == 512. The choice fills every compute unit with work units of a few hundred
+ * tokens (cf. TensorRT-LLM xqa launchMHA: sub-sequences = min(SMs / (batch * kv heads),
+ * tiles per sequence)). Environment AD_NUM_SPLITS forces the count (testing aid, cf. xqa's
+ * XQA_NB_SUB_SEQ).
+ */
+int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                     int32_t *num_splits, int32_t *chunk);
+
+/* Bytes of workspace attn_decode_paged / attn_decode_mla need for `num_splits` splits
+ * (0: the planner's choice): rows * splits * (head_dim_v + 1) * 4, 256-byte aligned parts.
+ * Returns 0 for arguments the calls would reject. */
+size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits);
+
+/*
+ * Partial pass. The cache is contiguous (paged == NULL) or paged; a contiguous cache may carry a
+ * block list (sparse; paged and sparse together are rejected). Split s covers keys
+ * [s*c, (s+1)*c) with c = ceil(kv_len_max / num_splits) rounded up to 16 (for a block list: the
+ * same ranges over the concatenation of the listed blocks, of length max_blocks*block_size).
+ * Writes EVERY slot, also of splits that lie past a short sequence's end:
+ *   part_o   [batch, q_len, num_q_heads, num_splits, head_dim_v] fp32, o_s = acc_s / l_s
+ *   part_lse [batch, q_len, num_q_heads, num_splits] fp32, natural log; a split with no visible
+ *            key gets o_s = 0, lse_s = -inf (mslk splitk_kernels.py: zeros when l == 0).
+ * args->out and args->lse are ignored. num_splits in [1, AD_MAX_SPLITS]; 0 = the planner's
+ * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, G * q_len <= 64.
+ */
+int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                        int32_t num_splits, float *part_o, float *part_lse, void *stream);
+
+/*
+ * LSE-weighted merge of num_splits partials per row (mslk splitk_kernels.py, _splitK_reduce):
+ *   M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
+ *   lse = M + ln sum_s w_s;  M = -inf gives out = 0, lse = -inf.
+ * part_o / part_lse use the layout attn_decode_splitkv writes. out [batch, q_len, num_q_heads,
+ * head_dim_v] in out_dtype with element strides out_stride {b, t, hq}; lse nullable, contiguous.
+ * head_dim_v is a multiple of 64, at most 1024.
+ */
+int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_splits, int32_t batch,
+                      int32_t q_len, int32_t num_q_heads, int32_t head_dim_v, int32_t out_dtype,
+                      void *out, const int64_t out_stride[3], float *lse, void *stream);
+
+/*
+ * Whole decode step over a paged cache: partial pass + merge, writing args->out / args->lse.
+ * workspace: device memory of at least attn_decode_workspace_size(args, paged, num_splits)
+ * bytes, 256-byte aligned, scratch for the partials (contents on return are unspecified).
+ * num_splits 0 = the planner's choice. Ragged seq_lens are handled per sequence: a split past
+ * the end of its sequence does no work.
+ */
+int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * MLA decode step (FlashInfer attention/mla.cuh, BatchMLAPagedAttention): one shared latent KV
+ * head (num_kv_heads = 1), head_dim_qk = 576 = 512 latent + 64 rope, head_dim_v = 512.
+ *   args->q      q_nope [batch, q_len, num_q_heads, 512]
+ *   args->k      ckv pool [pages, page_size, 1, 512] (strides {page, slot, head}); the values are
+ *                the same latent rows, so args->v must be NULL or equal to args->k.
+ *   q_pe         [batch, q_len, num_q_heads, 64] with strides q_pe_stride {b, t, hq}
+ *   kpe          [pages, page_size, 1, 64] with strides kpe_stride {page, slot, head}
+ * The score is scale * (q_nope . ckv_j + q_pe . kpe_j). Workspace as for attn_decode_paged.
+ */
+int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3],
+                    const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,
+                    int32_t num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Message for the calling thread's last non-OK return ("" if none). Valid until the thread's
+ * next call into the library. */
+const char *attn_decode_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_DECODE_H */

@@ -1,0 +1,235 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares, and rejects
+malformed arguments with the documented code before making any HIP call (none of these tests
+needs a GPU; valid calls are exercised by the GPU tests)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import attention_decode_amd as ad
+from attention_decode_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_decode.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_decode_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
+              "attn_decode_workspace_size", "attn_decode_plan", "attn_decode_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_abi.LIBRARY)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    codes = {m.group(1): int(m.group(2)) for m in re.finditer(r"#define (AD_\w+) \(?(-?\d+)\)?", text)}
+    for code, name in _abi.STATUS.items():
+        assert codes[name] == code
+    assert codes["AD_F32"] == _abi.AD_F32 and codes["AD_BF16"] == _abi.AD_BF16
+    assert codes["AD_MAX_SPLITS"] == _abi.AD_MAX_SPLITS
+
+
+def test_struct_layouts_match_header_sizes():
+    # ad_decode_args: 7 int32 + float (32 B), then pointer/stride groups, seq_lens, 3 int32, out, lse
+    assert ctypes.sizeof(_abi.DecodeArgs) == 32 + 3 * (8 + 24) + 8 + 4 + 4 + 4 + 4 + 8 + 24 + 8
+    assert ctypes.sizeof(_abi.Paged) == 24
+    assert ctypes.sizeof(_abi.Sparse) == 8 + 8 + 16 + 24 + 8
+
+
+# ------------------------------------------------------------------------------ rejection paths
+def _tensors(dtype=torch.bfloat16, B=2, Q=1, Hq=8, Hkv=2, D=128, L=64):
+    q = torch.zeros(B, Q, Hq, D, dtype=dtype)
+    k = torch.zeros(B, Hkv, L, D, dtype=dtype).permute(0, 2, 1, 3)
+    v = torch.zeros(B, Hkv, L, D, dtype=dtype).permute(0, 2, 1, 3)
+    out = torch.zeros(B, Q, Hq, D, dtype=dtype)
+    return q, k, v, out
+
+
+def _args(**over):
+    q, k, v, out = _tensors()
+    a = _abi.make_args(q, k, v, scale=0.1, out=out)
+    for key, val in over.items():
+        setattr(a, key, val)
+    return a, (q, k, v, out)
+
+
+def _splitkv(a, sparse=None, S=2):
+    po = torch.zeros(64, dtype=torch.float32)
+    pl = torch.zeros(64, dtype=torch.float32)
+    return _abi.lib().attn_decode_splitkv(ctypes.byref(a), None, ctypes.byref(sparse) if sparse else None, S,
+                                          po.data_ptr(), pl.data_ptr(), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("dtype", 7, -2),
+    ("num_q_heads", 7, -3),
+    ("q_len", 0, -3),
+    ("batch", -1, -3),
+    ("head_dim_qk", 96, -5),
+    ("head_dim_v", 64, -5),
+    ("kv_len_max", -5, -7),
+    ("window", -1, -7),
+    ("causal", 2, -7),
+    ("q", None, -1),
+    ("k", None, -1),
+    ("v", None, -1),
+])
+def test_splitkv_rejects(field, value, code):
+    a, keep = _args(**{field: value})
+    assert _splitkv(a) == code
+    assert ad.attn_decode_last_error() != ""
+
+
+def test_splitkv_rejects_too_many_rows_per_kv_head():
+    q, k, v, out = _tensors(Hq=32, Hkv=1)
+    a = _abi.make_args(q, k, v, scale=0.1)
+    assert _splitkv(a) == -5
+
+
+def test_splitkv_rejects_misaligned_rows():
+    q, k, v, out = _tensors()
+    a = _abi.make_args(q, k, v, scale=0.1)
+    a.q = a.q + 2  # one bf16 element off a 16-byte boundary
+    assert _splitkv(a) == -4
+    a, keep = _args()
+    a.k_stride[1] = 129  # odd row pitch
+    assert _splitkv(a) == -4
+
+
+def test_splitkv_rejects_split_counts():
+    a, keep = _args()
+    assert _splitkv(a, S=-1) == -7
+    assert _splitkv(a, S=_abi.AD_MAX_SPLITS + 1) == -7
+    assert _splitkv(a, S=0 + 0, sparse=None) not in (-1, -2, -3, -4, -5, -6)  # 0 = plan (needs a GPU)
+
+
+def test_splitkv_rejects_null_partials():
+    a, keep = _args()
+    assert _abi.lib().attn_decode_splitkv(ctypes.byref(a), None, None, 2, None, None, None) == -1
+
+
+def test_splitkv_rejects_bad_block_lists():
+    a, keep = _args()
+    nb = torch.zeros(2, 2, dtype=torch.int32)
+    ix = torch.zeros(2, 2, 4, dtype=torch.int32)
+    for bs, code in ((24, -7), (8, -7), (8192, -7)):
+        sp = _abi.make_sparse(nb, ix, bs)
+        assert _splitkv(a, sparse=sp) == code
+    sp = _abi.make_sparse(nb, ix, 128)
+    sp.block_idx = None
+    assert _splitkv(a, sparse=sp) == -1
+
+
+def _paged_call(a, pg, ws_bytes=1 << 20, ws_ptr=None, S=2):
+    ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    return _abi.lib().attn_decode_paged(ctypes.byref(a), ctypes.byref(pg) if pg else None, S,
+                                        base if ws_ptr is None else ws_ptr, ws_bytes, None), ws
+
+
+def test_paged_rejections():
+    q, _, _, out = _tensors()
+    pool = torch.zeros(10, 2, 16, 128, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    a = _abi.make_args(q, pool, pool, scale=0.1, kv_len_max=64, out=out)
+    assert _paged_call(a, None)[0] == -1
+    for ps in (8, 48, 128):
+        assert _paged_call(a, _abi.make_paged(bt, ps))[0] == -7
+    short = torch.zeros(2, 3, dtype=torch.int32)  # 3 pages < ceil(64 / 16)
+    assert _paged_call(a, _abi.make_paged(short, 16))[0] == -7
+    pg = _abi.make_paged(bt, 16)
+    assert _paged_call(a, pg, ws_ptr=0)[0] == -6
+    ws = torch.zeros((1 << 20) + 512, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    assert _abi.lib().attn_decode_paged(ctypes.byref(a), ctypes.byref(pg), 2, base + 16, 1 << 20, None) == -4
+    a.out = None
+    assert _paged_call(a, pg)[0] == -1
+    # a block list over a paged cache
+    po = torch.zeros(64)
+    sp = _abi.make_sparse(torch.zeros(2, 2, dtype=torch.int32), torch.zeros(2, 2, 4, dtype=torch.int32), 16)
+    assert _abi.lib().attn_decode_splitkv(ctypes.byref(a), ctypes.byref(pg), ctypes.byref(sp), 2, po.data_ptr(),
+                                          po.data_ptr(), None) == -5
+
+
+def test_paged_rejects_small_workspace():
+    q, _, _, out = _tensors()
+    pool = torch.zeros(10, 2, 16, 128, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    a = _abi.make_args(q, pool, pool, scale=0.1, kv_len_max=64, out=out)
+    pg = _abi.make_paged(bt, 16)
+    # 2 splits: rows 16 * 2 * 128 * 4 = 16 KiB of partial outputs + 256 B of LSEs
+    assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), 2) == 16384 + 256
+    assert _paged_call(a, pg, ws_bytes=16384)[0] == -6
+
+
+def test_merge_rejections():
+    L = _abi.lib()
+    po = torch.zeros(4096, dtype=torch.float32)
+    out = torch.zeros(2, 1, 8, 128, dtype=torch.bfloat16)
+    s3 = _abi.I64x3(*out.stride()[:3])
+    args = [po.data_ptr(), po.data_ptr(), 2, 2, 1, 8, 128, 1, out.data_ptr(), s3, None, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["po", "pl", "S", "B", "Q", "Hq", "Dv", "dt", "out", "stride", "lse", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return L.attn_decode_merge(*a)
+
+    assert call(po=None) == -1
+    assert call(out=None) == -1
+    assert call(dt=5) == -2
+    assert call(S=0) == -7
+    assert call(S=_abi.AD_MAX_SPLITS + 1) == -7
+    assert call(Dv=96) == -5
+    assert call(Q=0) == -3
+    assert call(out=out.data_ptr() + 2) == -4
+    assert call(B=0) == 0  # nothing to merge: no launch, success
+
+
+def test_mla_rejections():
+    qn = torch.zeros(2, 1, 16, 512, dtype=torch.bfloat16)
+    ckv = torch.zeros(8, 64, 1, 512, dtype=torch.bfloat16)
+    kpe = torch.zeros(8, 64, 1, 64, dtype=torch.bfloat16)
+    qpe = torch.zeros(2, 1, 16, 64, dtype=torch.bfloat16)
+    out = torch.zeros(2, 1, 16, 512, dtype=torch.bfloat16)
+    bt = torch.zeros(2, 4, dtype=torch.int32)
+    a = _abi.make_args(qn, ckv, None, scale=0.1, kv_len_max=256, out=out, head_dim_qk=576)
+    pg = _abi.make_paged(bt, 64)
+    L = _abi.lib()
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+
+    def call(args, kpe_p=kpe.data_ptr(), qpe_p=qpe.data_ptr()):
+        return L.attn_decode_mla(ctypes.byref(args), kpe_p, _abi._s3(kpe), qpe_p, _abi._s3(qpe), ctypes.byref(pg),
+                                 2, ws.data_ptr(), ws.numel(), None)
+
+    assert call(a, kpe_p=None) == -1
+    a.v = ckv.data_ptr() + 1024
+    assert call(a) == -5  # values must be the latent rows themselves
+    a.v = None
+    a.head_dim_qk = 192
+    assert call(a) == -5
+    a.head_dim_qk = 576
+    a.dtype = _abi.AD_F32
+    assert call(a) == -5
+
+
+def test_errors_raise_in_python():
+    a, keep = _args(num_q_heads=7)
+    with pytest.raises(_abi.ADError) as e:
+        _abi.attn_decode_splitkv(a, None, None, 2, torch.zeros(16), torch.zeros(16))
+    assert e.value.code == -3 and "multiple" in str(e.value)
