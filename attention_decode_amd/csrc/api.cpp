@@ -74,6 +74,7 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
     if (a->window < 0) return fail(AD_E_RANGE, "window must be >= 0");
     if (a->causal != 0 && a->causal != 1) return fail(AD_E_RANGE, "causal must be 0 or 1");
     if (!(std::isfinite(a->scale))) return fail(AD_E_RANGE, "scale must be finite");
+    if (a->batch == 0) return AD_OK;  // nothing is read or written: no pointer is needed
     if (path == Path::Mla) {
         if (a->dtype != AD_BF16) return fail(AD_E_UNSUPPORTED, "MLA supports bf16 only");
         if (a->head_dim_qk != 576 || a->head_dim_v != 512 || a->num_kv_heads != 1)
@@ -288,6 +289,7 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
     int rc = check_args(args, paged ? Path::Paged : Path::Contig, false);
     if (rc != AD_OK) return rc;
     if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+    if (args->batch == 0) return ok();
     if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
     if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
     if (!part_o || !part_lse) return fail(AD_E_NULL, "part_o or part_lse is NULL");
@@ -295,7 +297,6 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
         return fail(AD_E_ALIGN, "part_o must be 16-byte and part_lse 4-byte aligned");
     if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
-    if (args->batch == 0) return ok();
     Plan pl{};
     if ((rc = plan_splits(args, paged, sparse, paged ? Path::Paged : Path::Contig, num_splits, &pl)) != AD_OK)
         return rc;
@@ -327,17 +328,17 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
 int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_splits, int32_t batch, int32_t q_len,
                       int32_t num_q_heads, int32_t head_dim_v, int32_t out_dtype, void *out,
                       const int64_t out_stride[3], float *lse, void *stream) {
-    if (!part_o || !part_lse || !out || !out_stride) return fail(AD_E_NULL, "part_o, part_lse, out or out_stride is NULL");
     if (out_dtype != AD_F32 && out_dtype != AD_BF16) return fail(AD_E_DTYPE, "out_dtype %d unknown", out_dtype);
     if (num_splits < 1 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [1, %d]", num_splits, AD_MAX_SPLITS);
     if (batch < 0 || q_len < 1 || num_q_heads < 1) return fail(AD_E_SHAPE, "bad batch / q_len / num_q_heads");
+    if (batch == 0) return ok();
+    if (!part_o || !part_lse || !out || !out_stride) return fail(AD_E_NULL, "part_o, part_lse, out or out_stride is NULL");
     if (head_dim_v != 64 && head_dim_v != 128 && head_dim_v != 256 && head_dim_v != 512 && head_dim_v != 1024)
         return fail(AD_E_UNSUPPORTED, "head_dim_v %d not in {64, 128, 256, 512, 1024}", head_dim_v);
     if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_lse) & 3u) || !aligned16(out) ||
         !strides_aligned(out_stride, elem_bytes(out_dtype)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
         return fail(AD_E_ALIGN, "misaligned part_o / part_lse / out / lse");
-    if (batch == 0) return ok();
     ad_decode_args a{};
     a.dtype = out_dtype;
     a.batch = batch;
@@ -355,6 +356,7 @@ int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t
                       size_t workspace_bytes, void *stream) {
     int rc = check_args(args, Path::Paged, true);
     if (rc != AD_OK) return rc;
+    if (args->batch == 0) return ok();
     if ((rc = check_paged(args, paged)) != AD_OK) return rc;
     if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);

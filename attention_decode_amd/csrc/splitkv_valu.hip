@@ -69,8 +69,13 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// Reinterpretations take the 32-bit word BY VALUE: hipcc miscompiles __builtin_bit_cast applied
+// directly to an element of an ext_vector_type lvalue (it reads the wrong element), so vector
+// elements always pass through a plain uint32_t first.
+__device__ __forceinline__ float as_f32(uint32_t w) { return __uint_as_float(w); }
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <typename T, int D, int RP, int MODE, int U>
 __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
@@ -153,7 +158,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
             for (int i = 0; i < kPieces; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) qf[r][i * 4 + j] = __builtin_bit_cast(float, qv[r][i][j]) * p.scale_log2;
+                for (int j = 0; j < 4; ++j) qf[r][i * 4 + j] = as_f32(qv[r][i][j]) * p.scale_log2;
     }
 
     // ---- key addressing
@@ -237,13 +242,13 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                     for (int i = 0; i < kPieces; ++i)
 #pragma unroll
                         for (int j = 0; j < 4; ++j)
-                            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qv[r][i][j]),
-                                                                __builtin_bit_cast(bf16x2, kr[u][i][j]), d, false);
+                            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[r][i][j]), as_bf16x2(kr[u][i][j]), d,
+                                                                false);
                 } else {
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) d += qf[r][i * 4 + j] * __builtin_bit_cast(float, kr[u][i][j]);
+                        for (int j = 0; j < 4; ++j) d += qf[r][i * 4 + j] * as_f32(kr[u][i][j]);
                 }
                 d = slot_sum(d);
                 if constexpr (kBf16) d *= p.scale_log2;
@@ -287,7 +292,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                         vf[i * 8 + 2 * j] = bf16_lo(vr[u][i][j]);
                         vf[i * 8 + 2 * j + 1] = bf16_hi(vr[u][i][j]);
                     } else {
-                        vf[i * 4 + j] = __builtin_bit_cast(float, vr[u][i][j]);
+                        vf[i * 4 + j] = as_f32(vr[u][i][j]);
                     }
                 }
             }
