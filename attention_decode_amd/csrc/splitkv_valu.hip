@@ -8,27 +8,40 @@
 // base-2 units, q.k * scale * log2(e), and rescales with exp2 (the same page's qk_scale and
 // exp2 update; FlashInfer mla.cuh update_mdo_states_).
 //
-// Why VALU and not MFMA: with at most 8 rows per KV head the step reads 256-512 B of K/V per key
-// and does ~4 flop/B, far under the fp32-vector ridge; padding 4 rows to an MFMA tile of 16 would
-// only move the bottleneck to operand shuffles. The kernel is built to keep HBM busy:
+// Why VALU and not MFMA: with at most 8 rows per KV head a key costs 256-512 B of K/V and ~4
+// flop/B; the step is bound by HBM and by VALU issue, and MFMA would add operand transposes of V.
+// The kernel is built to keep HBM busy with as few VALU instructions per key as possible:
 //
-//   * 8 lanes share one K/V row; each lane loads 16-byte pieces, so one wave-wide load covers 8
-//     rows x 128 contiguous bytes (full cache lines). The 8 lanes of a row reduce their partial
-//     dot products with 3 DPP adds (quad_perm 1032, quad_perm 2301, row_half_mirror).
-//   * Each of the 8 row-slots of a wave runs its own online softmax over the keys it loads, so
-//     the hot loop has no cross-slot traffic; slots and waves are combined once, at the end.
-//   * Software pipeline per wave: V loads of step i and K loads of step i+1 are in flight while
-//     step i's scores and P.V are computed.
-//   * bf16 scores use v_dot2 (bf16 pairs, fp32 accumulate); q stays exact bf16 and the scale is
-//     applied to the fp32 dot. P.V accumulates in fp32 with P kept in fp32.
-//   * Page ids (paged cache) and listed block ids (block-sparse) of the split are staged in LDS
-//     once, so address generation never waits on a global load behind the K/V stream.
+//   * LPT lanes share one K/V row; each lane loads 16-byte pieces, so one wave-wide load covers
+//     64/LPT rows x 16*LPT contiguous bytes (whole cache lines). The lanes of a row reduce their
+//     partial dot products with DPP adds (quad_perm 1032, quad_perm 2301, row_half_mirror,
+//     row_mirror).
+//   * Each row-slot of a wave runs its own online softmax over the keys it loads, so the hot
+//     loop has no cross-slot traffic; slots and waves are combined once, at the end.
+//   * A step is 64/LPT * U consecutive keys (<= 16), so it never straddles a page of the paged
+//     cache or a listed block of the block-sparse cache: the page / block id is one LDS read per
+//     step, and the step's keys are one contiguous run.
+//   * Prefetch depth one step: the K and V loads of step i+1 are issued before step i's
+//     arithmetic; two register buffers alternate (loop unrolled by two) so no register moves are
+//     needed, and a scheduling fence keeps the loads where they are issued.
+//   * Steps wholly inside the visible range (every key in the split, inside the sequence, not
+//     cut by causal or window bounds) skip all masking; only boundary steps evaluate masks.
+//   * Lazy rescaling: the running max of a row is only raised when a score exceeds it by more
+//     than 2^8, so the accumulator rescale is rare; probabilities stay <= 256, the result is the
+//     same softmax with a different (exactly cancelled) reference point.
+//   * bf16: scores use v_dot2 on bf16 pairs (q stays exact, scale applied to the fp32 dot); P is
+//     rounded to bf16 and P.V uses v_dot2 over key pairs (V words re-paired with v_perm), with
+//     the row sum taken from the same rounded P, as the xqa (TensorRT-LLM mha.cu, toFp16 /
+//     computeRowSum) and FlashInfer (mla.cuh compute_mla_pv) kernels do. fp32 keeps P in fp32.
 //   * Masked keys are never read: their loads are redirected to the unit's own query row (always
-//     valid, finite memory) and their probability is forced to 0, so NaN/Inf in unused cache
-//     slots cannot leak into the result.
+//     valid, finite memory) and their probability is exactly 0, so NaN/Inf in unused cache slots
+//     cannot leak into the result.
 #include "ad_internal.h"
 
+#include <limits.h>
 #include <math.h>
+
+#include <type_traits>
 
 namespace ad {
 namespace {
@@ -38,8 +51,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kLanesPerRow = 8;               // lanes sharing one K/V row
-constexpr int kSlots = 64 / kLanesPerRow;     // rows one wave-wide load covers
+constexpr float kLazyRescale = 8.f;  // log2 units
+
+// Tuning: lanes that share one K/V row (4, 8 or 16; capped at row bytes / 16) and keys each
+// row-slot loads per step (even for bf16).
+#ifndef AD_VALU_LANES_PER_ROW
+#define AD_VALU_LANES_PER_ROW 8
+#endif
+#ifndef AD_VALU_KEYS_PER_SLOT
+#define AD_VALU_KEYS_PER_SLOT 2
+#endif
 
 template <typename T>
 struct Elem;
@@ -54,14 +75,16 @@ struct Elem<uint16_t> {  // bf16 bit patterns
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 8 lanes of a row-slot; every lane of the slot gets the total.
+// Sum over the LPT consecutive lanes of a row-slot; every lane of the slot gets the total.
+template <int LPT>
 __device__ __forceinline__ float slot_sum(float x) {
-    x += dpp<0xB1>(x);   // quad_perm [1,0,3,2]
-    x += dpp<0x4E>(x);   // quad_perm [2,3,0,1]
-    x += dpp<0x141>(x);  // row_half_mirror: the other quad of the 8
+    x += dpp<0xB1>(x);                            // quad_perm [1,0,3,2]
+    x += dpp<0x4E>(x);                            // quad_perm [2,3,0,1]
+    if constexpr (LPT >= 8) x += dpp<0x141>(x);   // row_half_mirror: the other quad of the 8
+    if constexpr (LPT >= 16) x += dpp<0x140>(x);  // row_mirror: the other half of the 16
     return x;
 }
 
@@ -74,21 +97,33 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 // elements always pass through a plain uint32_t first.
 __device__ __forceinline__ float as_f32(uint32_t w) { return __uint_as_float(w); }
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ bf16x2 pack_bf16(float lo, float hi) {  // round to nearest even
+    bf16x2 r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return r;
+}
+__device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
 
-template <typename T, int D, int RP, int MODE, int U>
+template <typename T, int D, int RP, int MODE, int U, int LPT>
 __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
     constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int kPer16 = Elem<T>::kPer16;
-    constexpr int kPieces = D * (int)sizeof(T) / (16 * kLanesPerRow);  // 16-B pieces per lane per row
-    static_assert(kPieces >= 1, "row too short for 8 lanes of 16 bytes");
-    constexpr int kEPL = kPieces * kPer16;  // elements per lane per row
-    constexpr int kStep = kSlots * U;       // keys per wave per step
+    constexpr int kSlots = 64 / LPT;                          // rows per wave-wide load
+    constexpr int kPieces = D * (int)sizeof(T) / (16 * LPT);  // 16-B pieces per lane per row
+    constexpr int kEPL = kPieces * kPer16;                    // elements per lane per row
+    constexpr int kStep = kSlots * U;                         // keys per wave per step
+    static_assert(kPieces >= 1, "row too short for the lanes sharing it");
+    static_assert(MODE == KV_CONTIG || (kStep <= 16 && 16 % kStep == 0),
+                  "a step must stay inside one page / listed block (both are >= 16 keys)");
+    static_assert(!kBf16 || U % 2 == 0, "bf16 P.V pairs keys");
 
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int slot = lane / kLanesPerRow, c = lane % kLanesPerRow;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps step bases scalar
+    const int slot = lane / LPT, c = lane % LPT;
     const int G = p.group, Q = p.q_len, R = G * Q, S = p.num_splits, Dv = p.head_dim_v;
     const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
 
@@ -120,16 +155,16 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     __shared__ float s_acc[kWaves][RP][D];
     __shared__ float s_m[kWaves][RP];
     __shared__ float s_l[kWaves][RP];
+    __shared__ float s_lf[kWaves][RP];
 
-    int map_first = 0;
+    const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
+    const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
     if constexpr (MODE == KV_PAGED) {
-        map_first = t0 >> p.page_shift;
-        const int n = ((t1 - 1) >> p.page_shift) - map_first + 1;
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
         const int32_t *bt = p.block_table + b * p.bt_stride + map_first;
         for (int i = tid; i < n; i += kThreads) s_map[i] = bt[i];
     } else if constexpr (MODE == KV_SPARSE) {
-        map_first = t0 >> p.block_shift;
-        const int n = ((t1 - 1) >> p.block_shift) - map_first + 1;
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
         const int32_t *ix = p.block_idx + b * p.ix_s[0] + h * p.ix_s[1];
         for (int i = tid; i < n; i += kThreads) s_map[i] = ix[(int64_t)(map_first + i) * p.ix_s[2]];
     }
@@ -138,17 +173,24 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     // ---- query rows of this unit: row r = t*G + g (hq = h*G + g)
     const T *qbase = static_cast<const T *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
     u32x4 qv[RP][kPieces];
-    int qpos[RP];
+    int lo[RP], hi[RP];  // visible key positions of row r: [lo, hi)
+    int lo_max = INT_MIN, hi_min = INT_MAX;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         const int t = r / G, g = r - t * G;
-        qpos[r] = L - Q + t;
+        const int qpos = L - Q + t;
+        hi[r] = p.causal ? qpos + 1 : INT_MAX;
+        lo[r] = p.window ? qpos - p.window + 1 : INT_MIN;
+        if (r < R) {
+            hi_min = min(hi_min, hi[r]);
+            lo_max = max(lo_max, lo[r]);
+        }
         const T *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) qv[r][i] = u32x4{0, 0, 0, 0};
         if (r < R) {
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) qv[r][i] = ld16(qr + (i * kLanesPerRow + c) * kPer16);
+            for (int i = 0; i < kPieces; ++i) qv[r][i] = ld16(qr + (i * LPT + c) * kPer16);
         }
     }
     float qf[kBf16 ? 1 : RP][kBf16 ? 1 : kEPL];  // fp32 queries, prescaled by scale*log2(e)
@@ -168,69 +210,69 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         kbase += b * p.k_s[0];
         vbase += b * p.v_s[0];
     }
-    const T *safe = qbase;  // a finite, always-readable row for masked lanes
-    const int page_mask = (1 << p.page_shift) - 1;
-    const int block_mask = (1 << p.block_shift) - 1;
+    const T *safe = qbase;  // a finite, always-readable row for lanes whose key is not visible
+    const int map_mask = (1 << map_shift) - 1;
+    const int lane_piece = c * kPer16;
 
-    float m[RP], l[RP], acc[RP][kEPL];
+    // l: row sum of the probabilities as multiplied into acc (the rounded P for bf16), the output
+    // normaliser; lf: the same sum in full fp32, which gives the LSE.
+    float m[RP], l[RP], lf[RP], acc[RP][kEPL];
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         m[r] = -INFINITY;
         l[r] = 0.f;
+        lf[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < kEPL; ++e) acc[r][e] = 0.f;
     }
 
-    u32x4 kr[U][kPieces];
-    const T *vptr[U];
-    int kpos[U];
-    bool kval[U];
+    // One step's K and V registers and the facts about its keys.
+    struct Buf {
+        u32x4 k[U][kPieces];
+        u32x4 v[U][kPieces];
+        bool val[U];
+        int base, pos0;
+    };
 
-    auto fetch_k = [&](int base) {
+    auto fetch = [&](Buf &f, int base) {
+        f.base = base;
+        int pos0 = base;
+        const T *krow = kbase;
+        const T *vrow = vbase;
+        const bool live = base < t1;  // uniform; a step past the end reads the safe row only
+        if (live) {
+            if constexpr (MODE == KV_PAGED) {
+                const int64_t page = __builtin_amdgcn_readfirstlane(s_map[(base >> map_shift) - map_first]);
+                const int slot0 = base & map_mask;
+                krow = kbase + page * p.k_s[0] + slot0 * p.k_s[1];
+                vrow = vbase + page * p.v_s[0] + slot0 * p.v_s[1];
+            } else {
+                if constexpr (MODE == KV_SPARSE)
+                    pos0 = (__builtin_amdgcn_readfirstlane(s_map[(base >> map_shift) - map_first]) << map_shift) +
+                           (base & map_mask);
+                krow = kbase + (int64_t)pos0 * p.k_s[1];
+                vrow = vbase + (int64_t)pos0 * p.v_s[1];
+            }
+        }
+        f.pos0 = pos0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int tok = base + u * kSlots + slot;
-            bool valid = tok < t1;
-            const int tt = valid ? tok : t0;
-            int pos = tt;
-            const T *kp;
-            const T *vp;
-            if constexpr (MODE == KV_PAGED) {
-                const int64_t page = s_map[(tt >> p.page_shift) - map_first];
-                const int sl = tt & page_mask;
-                kp = kbase + page * p.k_s[0] + sl * p.k_s[1];
-                vp = vbase + page * p.v_s[0] + sl * p.v_s[1];
-            } else {
-                if constexpr (MODE == KV_SPARSE) {
-                    pos = (s_map[(tt >> p.block_shift) - map_first] << p.block_shift) + (tt & block_mask);
-                    valid = valid && pos < L;
-                }
-                kp = kbase + (int64_t)pos * p.k_s[1];
-                vp = vbase + (int64_t)pos * p.v_s[1];
-            }
-            if (!valid) {
-                kp = safe;
-                vp = safe;
-            }
-            kpos[u] = pos;
-            kval[u] = valid;
-            vptr[u] = vp;
+            const int off = u * kSlots + slot;  // key offset inside the step
+            bool valid = live && base + off < t1;
+            if constexpr (MODE == KV_SPARSE) valid = valid && pos0 + off < L;
+            const T *kp = valid ? krow + off * p.k_s[1] : safe;
+            const T *vp = valid ? vrow + off * p.v_s[1] : safe;
+            f.val[u] = valid;
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) kr[u][i] = ld16(kp + (i * kLanesPerRow + c) * kPer16);
+            for (int i = 0; i < kPieces; ++i) f.k[u][i] = ld16(kp + i * LPT * kPer16 + lane_piece);
+#pragma unroll
+            for (int i = 0; i < kPieces; ++i) f.v[u][i] = ld16(vp + i * LPT * kPer16 + lane_piece);
         }
     };
 
-    const int stride = kWaves * kStep;
-    int base = t0 + wave * kStep;
-    if (base < t1) fetch_k(base);
-    while (base < t1) {
-        // V of this step: in flight while the scores are computed
-        u32x4 vr[U][kPieces];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int i = 0; i < kPieces; ++i) vr[u][i] = ld16(vptr[u] + (i * kLanesPerRow + c) * kPer16);
-
+    // Arithmetic of one step on its loaded K and V.
+    auto compute = [&](const Buf &cur, auto masked_tag) {
+        constexpr bool kMasked = decltype(masked_tag)::value;
         float sc[U][RP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -241,80 +283,132 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            d = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(qv[r][i][j]), as_bf16x2(kr[u][i][j]), d,
-                                                                false);
+                        for (int j = 0; j < 4; ++j) d = dot2(as_bf16x2(qv[r][i][j]), as_bf16x2(cur.k[u][i][j]), d);
                 } else {
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) d += qf[r][i * 4 + j] * as_f32(kr[u][i][j]);
+                        for (int j = 0; j < 4; ++j) d += qf[r][i * 4 + j] * as_f32(cur.k[u][i][j]);
                 }
-                d = slot_sum(d);
+                d = slot_sum<LPT>(d);
                 if constexpr (kBf16) d *= p.scale_log2;
-                bool vis = kval[u];
-                if (p.causal) vis = vis && kpos[u] <= qpos[r];
-                if (p.window) vis = vis && qpos[r] - kpos[u] < p.window;
-                sc[u][r] = vis ? d : -INFINITY;
+                if constexpr (kMasked) {
+                    const int pos = cur.pos0 + u * kSlots + slot;
+                    const bool vis = cur.val[u] && pos >= lo[r] && pos < hi[r];
+                    d = vis ? d : -INFINITY;
+                }
+                sc[u][r] = d;
             }
         }
-
-        const int next = base + stride;
-        if (next < t1) fetch_k(next);  // K of the next step: in flight during P.V
-
+        // lazy running max: raise a row's reference only when a score clears it by > 2^8
+        bool need = false;
+        float mx[RP];
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
-            float mx = sc[0][r];
+            mx[r] = sc[0][r];
 #pragma unroll
-            for (int u = 1; u < U; ++u) mx = fmaxf(mx, sc[u][r]);
-            const float mn = fmaxf(m[r], mx);
-            const float ms = (mn == -INFINITY) ? 0.f : mn;
-            const float alpha = exp2_fast(m[r] - ms);
-            m[r] = mn;
-            float ps = 0.f;
+            for (int u = 1; u < U; ++u) mx[r] = fmaxf(mx[r], sc[u][r]);
+            need = need || (mx[r] > m[r] + kLazyRescale);
+        }
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {  // wave-uniform
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                sc[u][r] = exp2_fast(sc[u][r] - ms);  // exp2(-inf) = 0 for masked keys
-                ps += sc[u][r];
+            for (int r = 0; r < RP; ++r) {
+                // A row (or slot) that does not need it keeps factor 1 exactly: exp2(m - m) would be
+                // NaN while m is still -inf. A raised row starting from -inf gets exp2(-inf) = 0.
+                const bool raise = mx[r] > m[r] + kLazyRescale;
+                const float alpha = raise ? exp2_fast(m[r] - mx[r]) : 1.f;
+                m[r] = raise ? mx[r] : m[r];
+                l[r] *= alpha;
+                lf[r] *= alpha;
+#pragma unroll
+                for (int e = 0; e < kEPL; ++e) acc[r][e] *= alpha;
             }
-            l[r] = l[r] * alpha + ps;
-#pragma unroll
-            for (int e = 0; e < kEPL; ++e) acc[r][e] *= alpha;
         }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float vf[kEPL];
+        for (int r = 0; r < RP; ++r) {
+            const float ms = (m[r] == -INFINITY) ? 0.f : m[r];  // m = -inf only while every score is -inf
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) {
+            for (int u = 0; u < U; ++u) sc[u][r] = exp2_fast(sc[u][r] - ms);  // exp2(-inf) = 0
+        }
+        if constexpr (kBf16) {
+            const bf16x2 ones = as_bf16x2(0x3F803F80u);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (kBf16) {
-                        vf[i * 8 + 2 * j] = bf16_lo(vr[u][i][j]);
-                        vf[i * 8 + 2 * j + 1] = bf16_hi(vr[u][i][j]);
-                    } else {
-                        vf[i * 4 + j] = as_f32(vr[u][i][j]);
+            for (int u = 0; u < U; u += 2) {
+                bf16x2 pk[RP];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    pk[r] = pack_bf16(sc[u][r], sc[u + 1][r]);
+                    l[r] = dot2(pk[r], ones, l[r]);  // row sum of the rounded P
+                    lf[r] += sc[u][r] + sc[u + 1][r];
+                }
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w0 = cur.v[u][i][j], w1 = cur.v[u + 1][i][j];
+                        const bf16x2 vlo = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x05040100u));
+                        const bf16x2 vhi = as_bf16x2(__builtin_amdgcn_perm(w1, w0, 0x07060302u));
+#pragma unroll
+                        for (int r = 0; r < RP; ++r) {
+                            acc[r][i * 8 + 2 * j] = dot2(pk[r], vlo, acc[r][i * 8 + 2 * j]);
+                            acc[r][i * 8 + 2 * j + 1] = dot2(pk[r], vhi, acc[r][i * 8 + 2 * j + 1]);
+                        }
                     }
                 }
             }
+        } else {
 #pragma unroll
-            for (int r = 0; r < RP; ++r)
+            for (int u = 0; u < U; ++u) {
 #pragma unroll
-                for (int e = 0; e < kEPL; ++e) acc[r][e] += sc[u][r] * vf[e];
+                for (int r = 0; r < RP; ++r) l[r] += sc[u][r];
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float vf = as_f32(cur.v[u][i][j]);
+#pragma unroll
+                        for (int r = 0; r < RP; ++r) acc[r][i * 4 + j] += sc[u][r] * vf;
+                    }
+            }
         }
-        base = next;
+    };
+
+    const int stride = kWaves * kStep;
+    // One step: issue K and V of step i+1, then the arithmetic of step i (whose loads were issued
+    // one step earlier). Returns false past the end.
+    auto iterate = [&](Buf &cur, Buf &nxt) -> bool {
+        if (cur.base >= t1) return false;
+        fetch(nxt, cur.base + stride);
+        // Keep the issue here: the register-pressure scheduler would otherwise sink the loads below
+        // the arithmetic, and every step would wait a full memory round trip.
+        __builtin_amdgcn_sched_barrier(0);
+        const bool full = cur.base + kStep <= t1 && cur.pos0 >= lo_max && cur.pos0 + kStep <= hi_min &&
+                          (MODE != KV_SPARSE || cur.pos0 + kStep <= L);
+        if (full)
+            compute(cur, std::integral_constant<bool, false>{});
+        else
+            compute(cur, std::integral_constant<bool, true>{});
+        return true;
+    };
+
+    Buf A, B;
+    fetch(A, t0 + wave * kStep);
+    while (iterate(A, B) && iterate(B, A)) {
     }
 
-    // ---- combine the 8 row-slots of the wave (lanes c, c+8, ..., c+56)
+    // ---- combine the row-slots of the wave (lanes c, c+LPT, ...)
 #pragma unroll
-    for (int off = kLanesPerRow; off < 64; off <<= 1) {
+    for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             const float mo = __shfl_xor(m[r], off);
-            const float lo = __shfl_xor(l[r], off);
+            const float lo_ = __shfl_xor(l[r], off);
+            const float lfo = kBf16 ? __shfl_xor(lf[r], off) : 0.f;
             const float mn = fmaxf(m[r], mo);
             const float ms = (mn == -INFINITY) ? 0.f : mn;
             const float a = exp2_fast(m[r] - ms), bb = exp2_fast(mo - ms);
-            l[r] = l[r] * a + lo * bb;
+            l[r] = l[r] * a + lo_ * bb;
+            if constexpr (kBf16) lf[r] = lf[r] * a + lfo * bb;
             m[r] = mn;
 #pragma unroll
             for (int e = 0; e < kEPL; ++e) acc[r][e] = acc[r][e] * a + __shfl_xor(acc[r][e], off) * bb;
@@ -326,10 +420,11 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
             for (int i = 0; i < kPieces; ++i)
 #pragma unroll
-                for (int j = 0; j < kPer16; ++j) s_acc[wave][r][(i * kLanesPerRow + c) * kPer16 + j] = acc[r][i * kPer16 + j];
+                for (int j = 0; j < kPer16; ++j) s_acc[wave][r][(i * LPT + c) * kPer16 + j] = acc[r][i * kPer16 + j];
             if (c == 0) {
                 s_m[wave][r] = m[r];
                 s_l[wave][r] = l[r];
+                s_lf[wave][r] = kBf16 ? lf[r] : l[r];
             }
         }
     }
@@ -342,25 +437,29 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
         const float ms = (M == -INFINITY) ? 0.f : M;
-        float lsum = 0.f, o = 0.f;
+        float lsum = 0.f, lfsum = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float f = exp2_fast(s_m[w][r] - ms);
             lsum += s_l[w][r] * f;
+            lfsum += s_lf[w][r] * f;
             o += s_acc[w][r][d] * f;
         }
         const int64_t row = out_row(r);
         p.part_o[(row * S + split) * Dv + d] = lsum > 0.f ? o / lsum : 0.f;
         if (d == 0)
-            p.part_lse[row * S + split] = lsum > 0.f ? (M + __builtin_amdgcn_logf(lsum)) * 0.69314718055994531f : -INFINITY;
+            p.part_lse[row * S + split] =
+                lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
 template <typename T, int D, int RP, int MODE>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
-    constexpr int U = RP <= 4 ? 4 : 2;
+    constexpr int kRowLanes = D * (int)sizeof(T) / 16;
+    constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
+    constexpr int U = AD_VALU_KEYS_PER_SLOT;
     dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
-    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

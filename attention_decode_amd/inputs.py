@@ -129,7 +129,7 @@ def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, hea
 
 def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
           q_len=1, dtype=torch.bfloat16, scale=None, seed=0, poison=False, max_pages=None,
-          causal=False, window=0) -> Workload:
+          causal=False, window=0, shuffle_pages=True) -> Workload:
     """Paged cache: pool [pages, Hkv, page_size, D] (head-major pages), block table [B, max_pages].
 
     The logical content of sequence b depends only on the seed and seq_lens; the physical page
@@ -147,7 +147,7 @@ def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_
     v_log = _randn(g, (n_logical, num_kv_heads, page_size, head_dim), dtype)
     n_pool = n_logical + (max(1, n_logical // 20) if poison else 0)
     pg = torch.Generator().manual_seed(seed + (7919 if poison else 0))
-    perm = torch.randperm(n_pool, generator=pg)[:n_logical]
+    perm = torch.randperm(n_pool, generator=pg)[:n_logical] if shuffle_pages else torch.arange(n_logical)
     fill = float("nan") if poison else 0.0
     k_pool = torch.full((n_pool, num_kv_heads, page_size, head_dim), fill, dtype=dtype)
     v_pool = torch.full((n_pool, num_kv_heads, page_size, head_dim), fill, dtype=dtype)
