@@ -168,14 +168,12 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         int cus = 0;
         int rc = device_cus(&cus);
         if (rc != AD_OK) return rc;
-        const int units = a->batch * (path == Path::Mla ? 1 : a->num_kv_heads);
-        // Ragged lengths: assume the average sequence is half the bound when planning.
-        const int64_t est = (a->seq_lens && !sp) ? std::max<int64_t>(span / 2, 1) : std::max<int64_t>(span, 1);
-        const int target = (env_int("AD_TARGET_UNITS") > 0 ? env_int("AD_TARGET_UNITS") : 8) * cus;
-        int64_t chunk = cdiv((int64_t)units * est, target);
-        const int64_t lo = path == Path::Mla ? 256 : 256, hi = 4096;
-        chunk = std::min<int64_t>(std::max<int64_t>(chunk, lo), hi);
-        S = (int)std::min<int64_t>(std::max<int64_t>(cdiv(span, chunk), 1), AD_MAX_SPLITS);
+        const int64_t units = (int64_t)a->batch * (path == Path::Mla ? 1 : a->num_kv_heads);
+        // Few, long splits: a work group streams its keys most efficiently as one long run, and
+        // one group per compute unit already saturates HBM. Two splits per sequence (one for short
+        // caches), doubled until every compute unit has a work group, never below 256 keys each.
+        S = span >= 2048 ? 2 : 1;
+        while (units * S < cus && span / (2 * S) >= 256 && S * 2 <= AD_MAX_SPLITS) S *= 2;
     }
     int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
     chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);

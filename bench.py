@@ -136,7 +136,20 @@ def main():
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run 3 device copies of 256 MiB (reads and writes 268,435,456 B each): the "
+                         "reference dispatch that scales the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+
+        x = torch.ones(64 << 20, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": x.numel() * 4, "bytes_written": y.numel() * 4}))
+        return
 
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
