@@ -35,6 +35,7 @@ struct PartialParams {
     int32_t block_shift;
     // shape
     int32_t batch, q_len, num_q_heads, num_kv_heads, group, head_dim_v;
+    int32_t row_blocks;   // work units per KV head along its G * q_len query rows (grid y = Hkv * row_blocks)
     float scale_log2;     // softmax scale * log2(e): scores are kept in base-2 units
     int32_t causal, window;
     int32_t num_splits, chunk;  // split s covers [s*chunk, (s+1)*chunk) of the (virtual) key range
@@ -70,6 +71,7 @@ struct MergeParams {
 // Launchers (hipSuccess or the launch error). They assume the host checks already passed.
 hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, int rows_padded, int mode,
                                hipStream_t stream);
+hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
 
 }  // namespace ad

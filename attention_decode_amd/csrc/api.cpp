@@ -8,6 +8,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <cmath>
 #include <string>
@@ -85,10 +86,6 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
         if (a->head_dim_qk != a->head_dim_v) return fail(AD_E_UNSUPPORTED, "head_dim_qk must equal head_dim_v");
         if (a->head_dim_qk != 64 && a->head_dim_qk != 128)
             return fail(AD_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", a->head_dim_qk);
-        const int rows = (a->num_q_heads / a->num_kv_heads) * a->q_len;
-        if (rows > 8)
-            return fail(AD_E_UNSUPPORTED, "%d query rows per KV head (G*q_len) exceed the 8 this build supports",
-                        rows);
         if (!a->v) return fail(AD_E_NULL, "v is NULL");
     }
     if (!a->q || !a->k) return fail(AD_E_NULL, "q or k is NULL");
@@ -127,6 +124,30 @@ int check_sparse(const ad_sparse *sp) {
 }
 
 // ------------------------------------------------------------------ planning
+// Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
+// units: the matrix-core kernel takes 32 rows per unit (bf16 with more than 8 rows), the vector
+// kernel up to 8. AD_PARTIAL_KERNEL=valu|mfma overrides the choice (bf16 only for mfma).
+struct Rows {
+    bool mfma;
+    int per_unit;  // rows one unit holds (the vector kernel's padded row count)
+    int blocks;    // units per KV head
+};
+
+Rows row_plan(const ad_decode_args *a) {
+    const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
+    const char *force = getenv("AD_PARTIAL_KERNEL");
+    bool mfma = a->dtype == AD_BF16 && r > 8;
+    if (force && a->dtype == AD_BF16) {
+        if (!strcmp(force, "mfma")) mfma = true;
+        if (!strcmp(force, "valu")) mfma = false;
+    }
+    Rows x{};
+    x.mfma = mfma;
+    x.per_unit = mfma ? 32 : (r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8);
+    x.blocks = (int)cdiv(r, x.per_unit);
+    return x;
+}
+
 int device_cus(int *cus) {
     static int cache[64] = {0};
     int dev = 0;
@@ -168,7 +189,8 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         int cus = 0;
         int rc = device_cus(&cus);
         if (rc != AD_OK) return rc;
-        const int64_t units = (int64_t)a->batch * (path == Path::Mla ? 1 : a->num_kv_heads);
+        const int64_t units =
+            (int64_t)a->batch * (path == Path::Mla ? 1 : (int64_t)a->num_kv_heads * row_plan(a).blocks);
         // Few, long splits: a work group streams its keys most efficiently as one long run, and
         // one group per compute unit already saturates HBM. Two splits per sequence (one for short
         // caches), doubled until every compute unit has a work group, never below 256 keys each.
@@ -215,9 +237,11 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
     return p;
 }
 
-int rows_padded(const ad_decode_args *a) {
-    const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
-    return r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8;
+hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mode, hipStream_t stream) {
+    const Rows rows = row_plan(a);
+    p.row_blocks = rows.blocks;
+    if (rows.mfma) return ad::launch_partial_mfma(p, a->head_dim_qk, mode, stream);
+    return ad::launch_partial_valu(p, a->dtype, a->head_dim_qk, rows.per_unit, mode, stream);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -317,8 +341,7 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
     p.write_empty = 1;
     p.part_o = part_o;
     p.part_lse = part_lse;
-    hipError_t e = ad::launch_partial_valu(p, args->dtype, args->head_dim_qk, rows_padded(args), mode,
-                                           static_cast<hipStream_t>(stream));
+    hipError_t e = launch_partial(args, p, mode, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "split-KV launch");
     return ok();
 }
@@ -377,7 +400,7 @@ int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t
     p.part_o = po;
     p.part_lse = plse;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = ad::launch_partial_valu(p, args->dtype, args->head_dim_qk, rows_padded(args), ad::KV_PAGED, s);
+    hipError_t e = launch_partial(args, p, ad::KV_PAGED, s);
     if (e != hipSuccess) return hip_fail(e, "paged split-KV launch");
     // Splits past a sequence's end wrote nothing: row b merges only ceil(L_b / chunk) of them.
     rc = run_merge(args, po, plse, pl.splits, true, pl.chunk, s);

@@ -1,0 +1,400 @@
+// splitkv_mfma.hip -- partial split-KV pass on the matrix cores (bf16, more than 8 query rows per
+// KV head: grouped heads times speculative query tokens).
+//
+// What it computes is the same as the vector-ALU pass: per work unit (split s, block of up to 32
+// query rows of KV head h, sequence b), the attention of those rows restricted to the split's keys,
+// written as o_s = acc / l and a natural-log LSE (mslk splitk_kernels.py, _fwd_kernel_splitK
+// epilogue), with the online softmax kept in base-2 units (same page, qk_scale and exp2 update).
+// Rows r = t*G + g are the G query heads of every query token that read head h, packed as in the
+// PyTorch Inductor flex_decode.py.jinja template; the bottom-right causal position of token t is
+// L - q_len + t (mslk splitk_kernels.py, causal mask of the speculative-decode path).
+//
+// Layout on the CDNA4 matrix cores (v_mfma_f32_32x32x16_bf16; operand lane maps measured on gfx950):
+//
+//   * Scores are computed transposed, S^T = K Q^T: K is the A operand (lane l holds 8 consecutive
+//     head-dim elements of key l%32), loaded straight from HBM as 16-byte pieces; Q is the B
+//     operand and stays in registers for the whole unit. The result leaves each lane with 16 keys
+//     of ONE query row (row l%32; lanes l and l^32 split the tile's keys), so the row max and row
+//     sum are an in-lane reduction plus one v_permlane32_swap.
+//   * That accumulator already is the A operand of P.V once converted to bf16: the MFMA reduction
+//     index k of lane l maps to key 16t + 8(i/4) + 4(l/32) + i%4 (t = k-step, i = element), and
+//     the V operand is built with the same key order.
+//   * V is the B operand of P.V and must be read key-major per lane, while memory holds it
+//     head-dim-major. Each wave stores its V tile in a private LDS region (16-byte chunks
+//     XOR-swizzled by row so that both the stores and the transposing reads avoid bank
+//     conflicts) and reads it back with ds_read_b64_tr_b16, which hands every lane four keys of
+//     one column.
+//   * A wave handles 32-key tiles; the 4 waves of a work group take every 4th tile of the split,
+//     each with its own running max / sum / accumulator, combined once through LDS at the end.
+//     Loads of the next tile are issued before the arithmetic of the current one (two register
+//     buffers, loop unrolled by two).
+//   * Keys outside the split, past the sequence, in no visible range of any row of the unit, or in
+//     unlisted blocks are never read: their loads are redirected to the unit's own query row and
+//     their probability is exactly 0. Tiles that are fully visible to every row skip all masking.
+//   * Lazy rescaling as in the vector pass: a row's reference max only moves when a score clears
+//     it by more than 2^8; the accumulator rows are rescaled through a small LDS exchange because
+//     the output layout spreads a row over other lanes than the score layout does.
+//   * P is rounded to bf16 for the P.V product and the output normaliser sums the rounded values
+//     (TensorRT-LLM mha.cu computeRowSum; FlashInfer mla.cuh compute_mla_pv); the LSE uses the
+//     fp32 sum.
+#include "ad_internal.h"
+
+#include <limits.h>
+#include <math.h>
+
+#include <type_traits>
+
+namespace ad {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;   // keys per wave per step
+constexpr int kRows = 32;   // query rows per work unit
+constexpr float kLazyRescale = 8.f;
+
+__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Both lanes l and l^32 get max / sum of their two values.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {  // round to nearest even
+    bf16x2 r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// 16-byte chunk position of chunk c of LDS row k (rows of D bf16). Rows 0..15 of a store land on
+// 16 distinct chunk positions; the 4 rows x 2 chunks of one transposing read land on 8.
+template <int D>
+__device__ __forceinline__ int swz(int k) {
+    return ((2 * (k & 7)) | ((k >> 3) & 1)) & (D / 8 - 1);
+}
+
+template <int D, int MODE>
+__global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialParams p) {
+    constexpr int kKs = D / 16;    // k-steps of the score product
+    constexpr int kSlabs = D / 32; // 32-column slabs of the output
+    constexpr int kRowBytes = D * 2;
+
+    const int split = blockIdx.x;
+    const int rb = blockIdx.y % p.row_blocks, h = blockIdx.y / p.row_blocks, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, half = lane >> 5;
+    const int G = p.group, Q = p.q_len, R = G * Q, S = p.num_splits, Dv = p.head_dim_v;
+    const int r0 = rb * kRows, nr = min(kRows, R - r0);
+    const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
+
+    int vlen = L;
+    if constexpr (MODE == KV_SPARSE) vlen = p.num_blocks[b * p.nb_s[0] + h * p.nb_s[1]] << p.block_shift;
+    const int t0 = split * p.chunk;
+    const int t1 = min(t0 + p.chunk, vlen);
+
+    auto out_row = [&](int r) -> int64_t {  // r: row inside the unit
+        const int ra = r0 + r, t = ra / G, g = ra - t * G;
+        return (int64_t)(b * Q + t) * p.num_q_heads + h * G + g;
+    };
+
+    if (t0 >= t1) {  // uniform
+        if (p.write_empty) {
+            for (int i = tid; i < nr * Dv; i += kThreads) {
+                const int r = i / Dv, d = i - r * Dv;
+                p.part_o[(out_row(r) * S + split) * Dv + d] = 0.f;
+            }
+            for (int r = tid; r < nr; r += kThreads) p.part_lse[out_row(r) * S + split] = -INFINITY;
+        }
+        return;
+    }
+
+    __shared__ int s_map[kMapCapacity];
+    // Per-wave V tiles during the loop; per-wave fp32 accumulators for the final combine.
+    __shared__ __attribute__((aligned(16))) unsigned char s_buf[kWaves * kRows * D * 4];
+    __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
+    __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
+
+    const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
+    const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
+    if constexpr (MODE == KV_PAGED) {
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
+        const int32_t *bt = p.block_table + b * p.bt_stride + map_first;
+        for (int i = tid; i < n; i += kThreads) s_map[i] = bt[i];
+    } else if constexpr (MODE == KV_SPARSE) {
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
+        const int32_t *ix = p.block_idx + b * p.ix_s[0] + h * p.ix_s[1];
+        for (int i = tid; i < n; i += kThreads) s_map[i] = ix[(int64_t)(map_first + i) * p.ix_s[2]];
+    }
+    if constexpr (MODE != KV_CONTIG) __syncthreads();
+    const int map_mask = (1 << map_shift) - 1;
+
+    // ---- this lane's query row (row col of the unit) as the B operand, and its visible range
+    const uint16_t *qbase = static_cast<const uint16_t *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
+    u32x4 qb[kKs];
+    int lo_r = INT_MIN, hi_r = INT_MAX;
+    {
+        const int ra = r0 + col;
+        const int t = ra / G, g = ra - t * G;
+        if (col < nr) {
+            const uint16_t *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) qb[ks] = ld16(qr + 16 * ks + 8 * half);
+            const int qpos = L - Q + t;
+            if (p.causal) hi_r = qpos + 1;
+            if (p.window) lo_r = qpos - p.window + 1;
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+        }
+    }
+    // Visible range of the unit: keys outside [lo_min, hi_max) are seen by no row; keys inside
+    // [lo_max, hi_min) by every row.
+    const int t_first = __builtin_amdgcn_readfirstlane(r0 / G);
+    const int t_last = __builtin_amdgcn_readfirstlane((r0 + nr - 1) / G);
+    const int hi_min = p.causal ? L - Q + t_first + 1 : INT_MAX;
+    const int hi_max = p.causal ? L - Q + t_last + 1 : INT_MAX;
+    const int lo_min = p.window ? L - Q + t_first - p.window + 1 : INT_MIN;
+    const int lo_max = p.window ? L - Q + t_last - p.window + 1 : INT_MIN;
+
+    // ---- key addressing: virtual key index v (position in the split's key range) -> logical
+    // position and row offsets. Only called with v < t1.
+    const uint16_t *kbase = static_cast<const uint16_t *>(p.k) + (int64_t)h * p.k_s[2];
+    const uint16_t *vbase = static_cast<const uint16_t *>(p.v) + (int64_t)h * p.v_s[2];
+    if constexpr (MODE != KV_PAGED) {
+        kbase += b * p.k_s[0];
+        vbase += b * p.v_s[0];
+    }
+    auto logical = [&](int v) -> int {
+        if constexpr (MODE == KV_SPARSE) return (s_map[(v >> map_shift) - map_first] << map_shift) + (v & map_mask);
+        return v;
+    };
+    const uint16_t *safe = qbase;  // finite, always readable, at least D elements
+
+    struct Buf {
+        u32x4 k[kKs];
+        u32x4 v[kKs];
+        int base;
+    };
+    auto fetch = [&](Buf &f, int base) {
+        f.base = base;
+        const int v = base + col;
+        const uint16_t *kp = safe, *vp = safe;
+        if (v < t1) {
+            if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
+                if (v >= lo_min && v < hi_max) {
+                    const int64_t page = s_map[(v >> map_shift) - map_first];
+                    const int slot = v & map_mask;
+                    kp = kbase + page * p.k_s[0] + slot * p.k_s[1];
+                    vp = vbase + page * p.v_s[0] + slot * p.v_s[1];
+                }
+            } else {
+                const int pos = logical(v);
+                if (pos < L && pos >= lo_min && pos < hi_max) {
+                    kp = kbase + (int64_t)pos * p.k_s[1];
+                    vp = vbase + (int64_t)pos * p.v_s[1];
+                }
+            }
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) f.k[ks] = ld16(kp + 16 * ks + 8 * half);
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) f.v[ks] = ld16(vp + 16 * ks + 8 * half);
+    };
+
+    lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;  // this wave's V tile
+    // Transposing-read addresses (bytes in vw) of this lane, for k-step t, read rd and slab s:
+    // row 16t + 8rd + 4*half + (lane&15)/4, chunk 4s + 2*((lane>>4)&1) + (lane&3)/2, half-chunk lane&1.
+    const int tr_row = 4 * half + ((lane & 15) >> 2);
+    const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    const int tr_byte = (lane & 1) << 3;
+
+    float m = -INFINITY, l = 0.f, lf = 0.f;  // row col's running state (this lane's keys)
+    f32x16 o[kSlabs];
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) o[s][j] = 0.f;
+
+    auto compute = [&](const Buf &cur, bool full) {
+        // V tile -> LDS (row col, chunk 2ks + half)
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks)
+            *(__attribute__((address_space(3))) u32x4 *)(vw + col * kRowBytes + (((2 * ks + half) ^ swz<D>(col)) << 4)) =
+                cur.v[ks];
+        // S^T = K Q^T
+        f32x16 sc;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[j] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) sc = mfma(cur.k[ks], qb[ks], sc);
+        float sv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sv[j] = sc[j] * p.scale_log2;
+        if (!full) {  // uniform
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int v4 = cur.base + 8 * q4 + 4 * half;  // keys v4 .. v4+3 share a page / block
+                const int pos4 = v4 < t1 ? logical(v4) : 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pos = pos4 + e;
+                    const bool vis = v4 + e < t1 && pos < L && pos >= lo_r && pos < hi_r;
+                    sv[4 * q4 + e] = vis ? sv[4 * q4 + e] : -INFINITY;
+                }
+            }
+        }
+        float mx = sv[0];
+#pragma unroll
+        for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
+        mx = pair_max(mx);
+        const bool raise = mx > m + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+            // Rows that do not move keep factor 1 exactly (exp2(m - m) is NaN while m = -inf).
+            const float alpha = raise ? exp2_fast(m - mx) : 1.f;
+            m = raise ? mx : m;
+            l *= alpha;
+            lf *= alpha;
+            if (half == 0) s_alpha[wave][col] = alpha;
+            // output rows of this lane: 8*(j/4) + 4*half + j%4
+            f32x4 a4[4];
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) a4[q4] = *(const f32x4 *)&s_alpha[wave][8 * q4 + 4 * half];
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) o[s][j] *= a4[j / 4][j % 4];
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        uint32_t pk[8];
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float p0 = exp2_fast(sv[2 * i] - ms), p1 = exp2_fast(sv[2 * i + 1] - ms);  // exp2(-inf) = 0
+            pk[i] = pack_bf16(p0, p1);
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
+            lf += p0 + p1;
+        }
+        // O += P V over the tile's two 16-key k-steps
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const u32x4 pa = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+#pragma unroll
+            for (int s = 0; s < kSlabs; ++s) {
+                s16x4 part[2];
+#pragma unroll
+                for (int rd = 0; rd < 2; ++rd) {
+                    const int row = 16 * t + 8 * rd + tr_row;
+                    const int chunk = 4 * s + tr_chunk;
+                    part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) s16x4 *)(vw + row * kRowBytes +
+                                                                    ((chunk ^ swz<D>(row)) << 4) + tr_byte));
+                }
+                const s16x8 vb = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+                o[s] = mfma(pa, __builtin_bit_cast(u32x4, vb), o[s]);
+            }
+        }
+    };
+
+    constexpr int kStride = kWaves * kTile;
+    auto iterate = [&](Buf &cur, Buf &nxt) -> bool {
+        if (cur.base >= t1) return false;
+        fetch(nxt, cur.base + kStride);
+        __builtin_amdgcn_sched_barrier(0);
+        bool full = cur.base + kTile <= t1;
+        if (full) {
+            const int pf = logical(cur.base), pl = logical(cur.base + kTile - 1);
+            full = pl - pf == kTile - 1 && pl < L && pf >= lo_max && pl < hi_min;
+        }
+        compute(cur, full);
+        return true;
+    };
+
+    Buf A, B;
+    fetch(A, t0 + wave * kTile);
+    while (iterate(A, B) && iterate(B, A)) {
+    }
+
+    // ---- combine the waves: o_s = acc / l, lse_s = (m + log2 lf) * ln 2
+    l = pair_sum(l);
+    lf = pair_sum(lf);
+    __syncthreads();  // every wave is done with its V tile: s_buf now holds the accumulators
+    float *s_o = reinterpret_cast<float *>(s_buf) + wave * kRows * D;
+    if (half == 0) {
+        s_m[wave][col] = m;
+        s_l[wave][col] = l;
+        s_lf[wave][col] = lf;
+    }
+#pragma unroll
+    for (int s = 0; s < kSlabs; ++s)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) s_o[(8 * (j / 4) + 4 * half + (j % 4)) * D + 32 * s + col] = o[s][j];
+    __syncthreads();
+
+    const float *s_all = reinterpret_cast<const float *>(s_buf);
+    for (int i = tid; i < nr * D; i += kThreads) {
+        const int r = i / D, d = i - r * D;
+        float M = s_m[0][r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+        const float ms = (M == -INFINITY) ? 0.f : M;
+        float lsum = 0.f, lfsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = exp2_fast(s_m[w][r] - ms);
+            lsum += s_l[w][r] * f;
+            lfsum += s_lf[w][r] * f;
+            acc += s_all[(w * kRows + r) * D + d] * f;
+        }
+        const int64_t row = out_row(r);
+        p.part_o[(row * S + split) * Dv + d] = lsum > 0.f ? acc / lsum : 0.f;
+        if (d == 0)
+            p.part_lse[row * S + split] =
+                lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY;
+    }
+}
+
+template <int D, int MODE>
+hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
+    dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
+    hipLaunchKernelGGL((partial_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
+    switch (mode) {
+        case KV_CONTIG: return launch_t<D, KV_CONTIG>(p, s);
+        case KV_PAGED: return launch_t<D, KV_PAGED>(p, s);
+        default: return launch_t<D, KV_SPARSE>(p, s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream) {
+    return head_dim == 64 ? by_mode<64>(p, mode, stream) : by_mode<128>(p, mode, stream);
+}
+
+}  // namespace ad

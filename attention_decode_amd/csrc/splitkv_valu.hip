@@ -120,11 +120,13 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                   "a step must stay inside one page / listed block (both are >= 16 keys)");
     static_assert(!kBf16 || U % 2 == 0, "bf16 P.V pairs keys");
 
-    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x;
+    const int rb = blockIdx.y % p.row_blocks, h = blockIdx.y / p.row_blocks, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps step bases scalar
     const int slot = lane / LPT, c = lane % LPT;
     const int G = p.group, Q = p.q_len, R = G * Q, S = p.num_splits, Dv = p.head_dim_v;
+    const int r0 = rb * RP, nr = min(RP, R - r0);  // this unit's rows: r0 .. r0 + nr - 1
     const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
 
     int vlen = L;  // length of the key range the splits partition
@@ -135,18 +137,18 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const int t0 = split * p.chunk;
     const int t1 = min(t0 + p.chunk, vlen);
 
-    auto out_row = [&](int r) -> int64_t {
-        const int t = r / G, g = r - t * G;
+    auto out_row = [&](int r) -> int64_t {  // r: row inside the unit
+        const int ra = r0 + r, t = ra / G, g = ra - t * G;
         return (int64_t)(b * Q + t) * p.num_q_heads + h * G + g;
     };
 
     if (t0 >= t1) {  // uniform over the work group
         if (p.write_empty) {
-            for (int i = tid; i < R * Dv; i += kThreads) {
+            for (int i = tid; i < nr * Dv; i += kThreads) {
                 const int r = i / Dv, d = i - r * Dv;
                 p.part_o[(out_row(r) * S + split) * Dv + d] = 0.f;
             }
-            for (int r = tid; r < R; r += kThreads) p.part_lse[out_row(r) * S + split] = -INFINITY;
+            for (int r = tid; r < nr; r += kThreads) p.part_lse[out_row(r) * S + split] = -INFINITY;
         }
         return;
     }
@@ -170,25 +172,25 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     }
     if constexpr (MODE != KV_CONTIG) __syncthreads();
 
-    // ---- query rows of this unit: row r = t*G + g (hq = h*G + g)
+    // ---- query rows of this unit: row r0 + r = t*G + g (hq = h*G + g)
     const T *qbase = static_cast<const T *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
     u32x4 qv[RP][kPieces];
     int lo[RP], hi[RP];  // visible key positions of row r: [lo, hi)
     int lo_max = INT_MIN, hi_min = INT_MAX;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
-        const int t = r / G, g = r - t * G;
+        const int ra = r0 + r, t = ra / G, g = ra - t * G;
         const int qpos = L - Q + t;
         hi[r] = p.causal ? qpos + 1 : INT_MAX;
         lo[r] = p.window ? qpos - p.window + 1 : INT_MIN;
-        if (r < R) {
+        if (r < nr) {
             hi_min = min(hi_min, hi[r]);
             lo_max = max(lo_max, lo[r]);
         }
         const T *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
 #pragma unroll
         for (int i = 0; i < kPieces; ++i) qv[r][i] = u32x4{0, 0, 0, 0};
-        if (r < R) {
+        if (r < nr) {
 #pragma unroll
             for (int i = 0; i < kPieces; ++i) qv[r][i] = ld16(qr + (i * LPT + c) * kPer16);
         }
@@ -431,7 +433,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     __syncthreads();
 
     // ---- combine the waves and write o_s = acc / l, lse_s = (m + log2 l) * ln 2
-    for (int i = tid; i < R * D; i += kThreads) {
+    for (int i = tid; i < nr * D; i += kThreads) {
         const int r = i / D, d = i - r * D;
         float M = s_m[0][r];
 #pragma unroll
@@ -458,7 +460,7 @@ hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int kRowLanes = D * (int)sizeof(T) / 16;
     constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
     constexpr int U = AD_VALU_KEYS_PER_SLOT;
-    dim3 grid(p.num_splits, p.num_kv_heads, p.batch);
+    dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
     hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

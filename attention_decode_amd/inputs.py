@@ -76,17 +76,26 @@ class Workload:
         return _finish(out)
 
     def kv_bytes(self) -> int:
-        """Bytes of K and V (MLA: ckv + kpe once) that a decode step must read: only keys that
-        are inside the sequence and, for a block list, inside a listed block."""
+        """Bytes of K and V (MLA: ckv + kpe once) that a decode step must read: each key once per
+        KV head if it is inside the sequence, inside a listed block (block-sparse cache), and
+        visible to at least one query row under the causal / sliding-window bounds."""
         es = torch.finfo(self.dtype).bits // 8
-        lens = self.seq_lens.to("cpu").to(torch.int64)
-        if self.kind == "mla":
-            return int(lens.sum()) * (self.head_dim_qk) * es
-        per_tok = (self.head_dim_qk + self.head_dim_v) * es
-        if self.num_blocks is not None:
-            nb = self.num_blocks.to("cpu").to(torch.int64)
-            return int(nb.sum()) * self.block_size * per_tok
-        return int(lens.sum()) * self.num_kv_heads * per_tok
+        lens = [int(x) for x in self.seq_lens.to("cpu")]
+        per_tok = self.head_dim_qk * es if self.kind == "mla" else (self.head_dim_qk + self.head_dim_v) * es
+        heads = 1 if self.kind == "mla" else self.num_kv_heads
+        total = 0
+        for b, L in enumerate(lens):
+            hi = L                                                   # newest query sits at L - 1
+            lo = max(0, L - self.q_len - self.window + 1) if self.window else 0   # oldest key of the first query
+            if self.num_blocks is None:
+                total += max(0, hi - lo) * heads
+                continue
+            for h in range(heads):
+                n = int(self.num_blocks[b, h])
+                for blk in self.block_idx[b, h, :n].tolist():
+                    a, z = max(blk * self.block_size, lo), min((blk + 1) * self.block_size, hi)
+                    total += max(0, z - a)
+        return total * per_tok
 
 
 # token-major view of each storage tensor: (storage name, permutation) per field
@@ -184,22 +193,35 @@ def window_block_list(kv_len: int, q_len: int, window: int, block_size: int):
 
 def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len, q_len,
            block_size, blocks, dtype=torch.bfloat16, scale=None, seed=0, causal=True, window=0,
-           poison=False) -> Workload:
-    """Contiguous head-major cache with a per-(b, KV head) list of KV blocks (same list for all).
-    With ``poison`` every unlisted block holds NaN."""
+           poison=False, seq_lens=None) -> Workload:
+    """Contiguous head-major cache with a per-(b, KV head) list of KV blocks: ``blocks`` is one list
+    shared by every (b, KV head), or a nested list blocks[b][h] of lists of any lengths (the index
+    array is padded with -1, which is never read). With ``poison`` every key outside the listed
+    blocks of its own (b, h), and every key at or past seq_lens[b], holds NaN."""
     w = contiguous(config=config, name=name, batch=batch, num_q_heads=num_q_heads,
                    num_kv_heads=num_kv_heads, head_dim=head_dim, kv_len=kv_len, q_len=q_len,
-                   dtype=dtype, scale=scale, seed=seed, causal=causal, window=window)
-    nb = len(blocks)
-    w.num_blocks = torch.full((batch, num_kv_heads), nb, dtype=torch.int32)
-    w.block_idx = torch.as_tensor(blocks, dtype=torch.int32).view(1, 1, nb).repeat(batch, num_kv_heads, 1)
+                   dtype=dtype, scale=scale, seed=seed, causal=causal, window=window, seq_lens=seq_lens)
+    if blocks and isinstance(blocks[0], (list, tuple)):
+        lists = [[list(blocks[b][h]) for h in range(num_kv_heads)] for b in range(batch)]
+    else:
+        lists = [[list(blocks) for _ in range(num_kv_heads)] for _ in range(batch)]
+    nmax = max(1, max(len(x) for row in lists for x in row))
+    w.num_blocks = torch.tensor([[len(x) for x in row] for row in lists], dtype=torch.int32)
+    w.block_idx = torch.full((batch, num_kv_heads, nmax), -1, dtype=torch.int32)
+    for b in range(batch):
+        for h in range(num_kv_heads):
+            if lists[b][h]:
+                w.block_idx[b, h, :len(lists[b][h])] = torch.as_tensor(lists[b][h], dtype=torch.int32)
     w.block_size = block_size
     if poison:
-        listed = torch.zeros(kv_len, dtype=torch.bool)
-        for blk in blocks:
-            listed[blk * block_size:(blk + 1) * block_size] = True
-        for name_ in ("k", "v"):
-            w.storage[name_][:, :, ~listed, :] = float("nan")
+        for b in range(batch):
+            for h in range(num_kv_heads):
+                keep = torch.zeros(kv_len, dtype=torch.bool)
+                for blk in lists[b][h]:
+                    keep[blk * block_size:(blk + 1) * block_size] = True
+                keep[int(w.seq_lens[b]):] = False
+                for name_ in ("k", "v"):
+                    w.storage[name_][b, h, ~keep, :] = float("nan")
     return w
 
 

@@ -94,10 +94,15 @@ def test_splitkv_rejects(field, value, code):
     assert ad.attn_decode_last_error() != ""
 
 
-def test_splitkv_rejects_too_many_rows_per_kv_head():
-    q, k, v, out = _tensors(Hq=32, Hkv=1)
-    a = _abi.make_args(q, k, v, scale=0.1)
-    assert _splitkv(a) == -5
+def test_many_rows_per_kv_head_pass_validation():
+    """32 and 128 query rows per KV head (grouped heads x speculative tokens) are accepted, bf16 and
+    fp32 alike: the workspace query gets past every host check and sizes the partials."""
+    for dtype, Hq, Q in ((torch.bfloat16, 32, 1), (torch.bfloat16, 32, 4), (torch.float32, 16, 2)):
+        q, k, v, out = _tensors(dtype=dtype, Hq=Hq, Hkv=1, Q=Q)
+        a = _abi.make_args(q, k, v, scale=0.1, out=out)
+        rows = 2 * Q * Hq
+        expect = -(-rows * 2 * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
+        assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, 2) == expect
 
 
 def test_splitkv_rejects_misaligned_rows():
