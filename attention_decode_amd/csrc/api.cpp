@@ -124,6 +124,9 @@ int check_sparse(const ad_sparse *sp) {
 }
 
 // ------------------------------------------------------------------ planning
+// The latent-attention kernel takes 128 query rows (heads x query tokens) per work unit.
+int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, 128); }
+
 // Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
 // units: the matrix-core kernel takes 32 rows per unit (bf16 with more than 8 rows), the vector
 // kernel up to 8. AD_PARTIAL_KERNEL=valu|mfma overrides the choice (bf16 only for mfma).
@@ -190,7 +193,7 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         int rc = device_cus(&cus);
         if (rc != AD_OK) return rc;
         const int64_t units =
-            (int64_t)a->batch * (path == Path::Mla ? 1 : (int64_t)a->num_kv_heads * row_plan(a).blocks);
+            (int64_t)a->batch * (path == Path::Mla ? mla_row_blocks(a) : (int64_t)a->num_kv_heads * row_plan(a).blocks);
         // Few, long splits: a work group streams its keys most efficiently as one long run, and
         // one group per compute unit already saturates HBM. Two splits per sequence (one for short
         // caches), doubled until every compute unit has a work group, never below 256 keys each.
@@ -412,13 +415,42 @@ int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t k
                     size_t workspace_bytes, void *stream) {
     int rc = check_args(args, Path::Mla, true);
     if (rc != AD_OK) return rc;
+    if (args->batch == 0) return ok();
     if ((rc = check_paged(args, paged)) != AD_OK) return rc;
     if (!kpe || !q_pe || !kpe_stride || !q_pe_stride) return fail(AD_E_NULL, "kpe / q_pe or their strides are NULL");
-    (void)num_splits;
-    (void)workspace;
-    (void)workspace_bytes;
-    (void)stream;
-    return fail(AD_E_UNSUPPORTED, "MLA kernel not built yet");
+    if (!aligned16(kpe) || !aligned16(q_pe) || !strides_aligned(kpe_stride, 2) || !strides_aligned(q_pe_stride, 2))
+        return fail(AD_E_ALIGN, "kpe and q_pe rows must be 16-byte aligned");
+    if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
+        return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
+    if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, nullptr, Path::Mla, num_splits, &pl)) != AD_OK) return rc;
+    size_t lse_off = 0;
+    const size_t need = partial_bytes(args, pl.splits, &lse_off);
+    if (workspace_bytes < need)
+        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+    float *po = static_cast<float *>(workspace);
+    float *plse = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
+    ad::PartialParams p = base_params(args, pl);
+    p.q2 = q_pe;
+    p.k2 = kpe;
+    for (int i = 0; i < 3; ++i) {
+        p.q2_s[i] = q_pe_stride[i];
+        p.k2_s[i] = kpe_stride[i];
+    }
+    p.block_table = paged->block_table;
+    p.bt_stride = paged->bt_stride;
+    p.page_shift = log2_exact(paged->page_size);
+    p.row_blocks = mla_row_blocks(args);
+    p.write_empty = 0;
+    p.part_o = po;
+    p.part_lse = plse;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = ad::launch_partial_mla(p, s);
+    if (e != hipSuccess) return hip_fail(e, "MLA split-KV launch");
+    rc = run_merge(args, po, plse, pl.splits, true, pl.chunk, s);
+    return rc == AD_OK ? ok() : rc;
 }
 
 const char *attn_decode_last_error(void) { return g_error.c_str(); }

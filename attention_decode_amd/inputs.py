@@ -226,16 +226,17 @@ def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_di
 
 
 def mla(*, config=0, name="custom", batch, num_heads, kv_len, page_size, dim_latent=512, dim_rope=64,
-        dtype=torch.bfloat16, scale=None, seed=0, seq_lens=None, poison=False) -> Workload:
-    """MLA: q_nope [B,1,H,512], q_pe [B,1,H,64], ckv pool [pages, page, 512] and kpe pool
+        dtype=torch.bfloat16, scale=None, seed=0, seq_lens=None, poison=False, q_len=1, causal=False,
+        window=0) -> Workload:
+    """MLA: q_nope [B,Q,H,512], q_pe [B,Q,H,64], ckv pool [pages, page, 512] and kpe pool
     [pages, page, 64] (one shared latent KV head), block table from a random page permutation."""
     g = torch.Generator().manual_seed(seed)
     sl = torch.full((batch,), kv_len, dtype=torch.int32) if seq_lens is None else \
         torch.as_tensor(seq_lens, dtype=torch.int32)
     pages_b = [(int(x) + page_size - 1) // page_size for x in sl]
     n_logical = sum(pages_b)
-    q = _randn(g, (batch, 1, num_heads, dim_latent), dtype)
-    q_pe = _randn(g, (batch, 1, num_heads, dim_rope), dtype)
+    q = _randn(g, (batch, q_len, num_heads, dim_latent), dtype)
+    q_pe = _randn(g, (batch, q_len, num_heads, dim_rope), dtype)
     ckv_log = _randn(g, (n_logical, page_size, dim_latent), dtype)
     kpe_log = _randn(g, (n_logical, page_size, dim_rope), dtype)
     n_pool = n_logical + (max(1, n_logical // 20) if poison else 0)
@@ -256,11 +257,11 @@ def mla(*, config=0, name="custom", batch, num_heads, kv_len, page_size, dim_lat
             ckv[bt[b, n - 1], tail:] = float("nan")
             kpe[bt[b, n - 1], tail:] = float("nan")
         off += n
-    w = Workload(config=config, name=name, kind="mla", dtype=dtype, batch=batch, q_len=1,
+    w = Workload(config=config, name=name, kind="mla", dtype=dtype, batch=batch, q_len=q_len,
                  num_q_heads=num_heads, num_kv_heads=1, head_dim_qk=dim_latent + dim_rope,
                  head_dim_v=dim_latent, scale=(1.0 / math.sqrt(192)) if scale is None else scale,
                  kv_len_max=mp * page_size, seq_lens=sl, q=None, k=None, v=None,
-                 block_table=bt, page_size=page_size)
+                 block_table=bt, page_size=page_size, causal=causal, window=window)
     w.storage = {"q": q, "q_pe": q_pe, "ckv": ckv.view(n_pool, page_size, 1, dim_latent),
                  "kpe": kpe.view(n_pool, page_size, 1, dim_rope)}
     return _finish(w)

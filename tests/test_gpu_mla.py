@@ -1,0 +1,113 @@
+"""GPU parity of multi-head latent attention (shared latent KV head: 512 latent + 64 rotary
+dims, values = the latent row) against the fp64 oracle on the same seeded inputs, through the
+C ABI entry point attn_decode_mla."""
+import numpy as np
+import pytest
+import torch
+
+from attention_decode_amd import inputs
+from attention_decode_amd.step import DecodeStep
+from gpu_util import assert_matches, gpu_available, oracle_of, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def run(w_cpu, num_splits=None):
+    wg = w_cpu.to("cuda")
+    step = DecodeStep(wg, num_splits=num_splits)
+    out, lse = step()
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), step
+
+
+def flat_rows(w):
+    return w.batch * w.q_len * w.num_q_heads
+
+
+def test_workload5_sampled_rows(orc):
+    """Full size (32 sequences x 128 heads x 8192 keys, page 64): every head of sequences 0 and 31
+    plus 256 random rows, compared with the oracle row by row."""
+    say("[gpu] workload 5 (MLA) full size, sampled rows")
+    w = inputs.make(5)
+    out, lse, step = run(w)
+    say(f"  splits {step.splits}")
+    g = torch.Generator().manual_seed(5)
+    H = w.num_q_heads
+    rows = sorted(set(list(range(H)) + list(range(31 * H, 32 * H)) +
+                      torch.randint(0, flat_rows(w), (256,), generator=g).tolist()))
+    ref_o, ref_l = oracle_of(orc, w, rows=rows)
+    o = out.reshape(-1, w.head_dim_v)[rows]
+    l_ = lse.reshape(-1)[rows]
+    assert_matches(o, l_, ref_o, ref_l, w.dtype, f"workload 5, {len(rows)} rows")
+
+
+def test_workload5_poisoned_bit_identical():
+    say("[gpu] workload 5 clean vs poisoned pool")
+    a = run(inputs.make(5))
+    b = run(inputs.make(5, poison=True))
+    assert torch.isfinite(b[0]).all()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+CASES = [  # (heads, page, lens, q_len, causal, window)
+    (128, 64, [1, 31, 33, 700], 1, False, 0),
+    (128, 16, [64, 1000, 5], 1, False, 0),
+    (16, 32, [300, 2], 1, False, 0),
+    (160, 64, [257, 90], 1, False, 0),       # two row blocks, the second partly empty
+    (64, 16, [500, 77], 2, True, 0),         # two query tokens, causal
+    (32, 64, [640, 129], 3, True, 200),      # three query tokens, causal + window
+]
+
+
+@pytest.mark.parametrize("H,page,lens,Q,causal,window", CASES, ids=lambda x: str(x))
+def test_mla_small(orc, H, page, lens, Q, causal, window):
+    say(f"[gpu] mla H={H} page={page} lens={lens} Q={Q} causal={causal} window={window}")
+    w = inputs.mla(batch=len(lens), num_heads=H, kv_len=max(lens), page_size=page, seq_lens=lens, q_len=Q,
+                   causal=causal, window=window, seed=700 + H + page + Q)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 3):
+        out, lse, _ = run(w, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, w.dtype, f"S={S}")
+
+
+def test_mla_poisoned_small_bit_identical():
+    lens = [5, 64, 250, 1000, 31]
+    say("[gpu] mla poisoned small pool")
+    kw = dict(batch=len(lens), num_heads=128, kv_len=1000, page_size=16, seq_lens=lens, seed=9)
+    a = run(inputs.mla(**kw), num_splits=4)
+    b = run(inputs.mla(**kw, poison=True), num_splits=4)
+    assert torch.isfinite(b[0]).all()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_mla_score_far_above_first_tile(orc):
+    """A late key scores ~110 (natural log units) above the rest: far beyond what a reference max
+    fixed at the first tile may absorb, so the unit is recomputed exactly with each row's true
+    max. The result still equals the oracle (dominated by that key)."""
+    say("[gpu] mla: score far above the first tile's max")
+    lens = [300, 300]
+    w = inputs.mla(batch=2, num_heads=32, kv_len=300, page_size=16, seq_lens=lens, seed=11)
+    u = w.storage["q"][0, 0, 0].clone()
+    w.storage["q"][0, 0, :] = u                      # every head of sequence 0 queries along u
+    j0 = 250
+    page = int(w.block_table[0, j0 // 16])
+    w.storage["ckv"][page, j0 % 16, 0] = (3.0 * u.float()).to(w.dtype)
+    ref_o, ref_l = oracle_of(orc, w)
+    assert np.min(ref_l.reshape(2, 32)[0]) > 60       # the key really dominates sequence 0
+    out, lse, _ = run(w, num_splits=1)
+    assert_matches(out, lse, ref_o, ref_l, w.dtype, "far score")
+
+
+def test_mla_split_invariance():
+    say("[gpu] mla split invariance")
+    w = inputs.mla(batch=2, num_heads=128, kv_len=3000, page_size=64, seq_lens=[3000, 1777], seed=13)
+    outs = [(S,) + run(w, num_splits=S)[:2] for S in (1, 2, 5, 8)]
+    o0, l0 = outs[0][1].double(), outs[0][2].double()
+    # Each result carries bf16 rounding of P (2^-9 relative on every weight) and of the output; the
+    # worst element of either stays inside the oracle tolerance, and the mean difference is
+    # rounding noise (a systematic error, e.g. a mishandled split boundary, moves the mean).
+    for S, o, l_ in outs[1:]:
+        d = (o.double() - o0).abs()
+        assert float(d.max()) <= 1e-2 and float(d.mean()) <= 3e-4, f"S={S}: max {float(d.max())} mean {float(d.mean())}"
+        assert (l_.double() - l0).abs().max() <= 1e-4, f"S={S}"
