@@ -81,9 +81,12 @@ def lib():
         L.attn_decode_mla.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
                                       P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_mla_splitkv.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
+                                              P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p]
         L.attn_decode_last_error.restype = ctypes.c_char_p
         for fn in ("attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
-                   "attn_decode_mla"):
+                   "attn_decode_mla", "attn_decode_mla_splitkv"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -193,6 +196,14 @@ def attn_decode_paged(args: DecodeArgs, paged: Paged, num_splits: int, workspace
     _check("attn_decode_paged",
            lib().attn_decode_paged(ctypes.byref(args), ctypes.byref(paged), num_splits, _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_mla_splitkv(args: DecodeArgs, kpe, q_pe, paged: Paged, num_splits: int, part_o, part_lse,
+                            stream=None):
+    _check("attn_decode_mla_splitkv",
+           lib().attn_decode_mla_splitkv(ctypes.byref(args), _ptr(kpe), _s3(kpe), _ptr(q_pe), _s3(q_pe),
+                                         ctypes.byref(paged), num_splits, _ptr(part_o), _ptr(part_lse),
+                                         _stream(stream)))
 
 
 def attn_decode_mla(args: DecodeArgs, kpe, q_pe, paged: Paged, num_splits: int, workspace, stream=None):

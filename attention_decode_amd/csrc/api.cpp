@@ -410,47 +410,86 @@ int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t
     return rc == AD_OK ? ok() : rc;
 }
 
-int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3], const void *q_pe,
-                    const int64_t q_pe_stride[3], const ad_paged *paged, int32_t num_splits, void *workspace,
-                    size_t workspace_bytes, void *stream) {
-    int rc = check_args(args, Path::Mla, true);
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two MLA entry points; on success fills *pl and *p (partials not set).
+int mla_prepare(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3], const void *q_pe,
+                const int64_t q_pe_stride[3], const ad_paged *paged, int32_t num_splits, bool need_out, Plan *pl,
+                ad::PartialParams *p) {
+    int rc = check_args(args, Path::Mla, need_out);
     if (rc != AD_OK) return rc;
-    if (args->batch == 0) return ok();
+    if (args->batch == 0) return AD_OK;
     if ((rc = check_paged(args, paged)) != AD_OK) return rc;
     if (!kpe || !q_pe || !kpe_stride || !q_pe_stride) return fail(AD_E_NULL, "kpe / q_pe or their strides are NULL");
     if (!aligned16(kpe) || !aligned16(q_pe) || !strides_aligned(kpe_stride, 2) || !strides_aligned(q_pe_stride, 2))
         return fail(AD_E_ALIGN, "kpe and q_pe rows must be 16-byte aligned");
     if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
+    if ((rc = plan_splits(args, paged, nullptr, Path::Mla, num_splits, pl)) != AD_OK) return rc;
+    *p = base_params(args, *pl);
+    p->q2 = q_pe;
+    p->k2 = kpe;
+    for (int i = 0; i < 3; ++i) {
+        p->q2_s[i] = q_pe_stride[i];
+        p->k2_s[i] = kpe_stride[i];
+    }
+    p->block_table = paged->block_table;
+    p->bt_stride = paged->bt_stride;
+    p->page_shift = log2_exact(paged->page_size);
+    p->row_blocks = mla_row_blocks(args);
+    return AD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3], const void *q_pe,
+                    const int64_t q_pe_stride[3], const ad_paged *paged, int32_t num_splits, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    Plan pl{};
+    ad::PartialParams p{};
+    int rc = mla_prepare(args, kpe, kpe_stride, q_pe, q_pe_stride, paged, num_splits, true, &pl, &p);
+    if (rc != AD_OK) return rc;
+    if (args->batch == 0) return ok();
     if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
-    Plan pl{};
-    if ((rc = plan_splits(args, paged, nullptr, Path::Mla, num_splits, &pl)) != AD_OK) return rc;
     size_t lse_off = 0;
     const size_t need = partial_bytes(args, pl.splits, &lse_off);
     if (workspace_bytes < need)
         return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
     float *po = static_cast<float *>(workspace);
     float *plse = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
-    ad::PartialParams p = base_params(args, pl);
-    p.q2 = q_pe;
-    p.k2 = kpe;
-    for (int i = 0; i < 3; ++i) {
-        p.q2_s[i] = q_pe_stride[i];
-        p.k2_s[i] = kpe_stride[i];
-    }
-    p.block_table = paged->block_table;
-    p.bt_stride = paged->bt_stride;
-    p.page_shift = log2_exact(paged->page_size);
-    p.row_blocks = mla_row_blocks(args);
     p.write_empty = 0;
     p.part_o = po;
     p.part_lse = plse;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = ad::launch_partial_mla(p, s);
     if (e != hipSuccess) return hip_fail(e, "MLA split-KV launch");
+    // Splits past a sequence's end wrote nothing: row b merges only ceil(L_b / chunk) of them.
     rc = run_merge(args, po, plse, pl.splits, true, pl.chunk, s);
     return rc == AD_OK ? ok() : rc;
+}
+
+int attn_decode_mla_splitkv(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3],
+                            const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,
+                            int32_t num_splits, float *part_o, float *part_lse, void *stream) {
+    Plan pl{};
+    ad::PartialParams p{};
+    int rc = mla_prepare(args, kpe, kpe_stride, q_pe, q_pe_stride, paged, num_splits, false, &pl, &p);
+    if (rc != AD_OK) return rc;
+    if (args->batch == 0) return ok();
+    if (!part_o || !part_lse) return fail(AD_E_NULL, "part_o or part_lse is NULL");
+    if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_lse) & 3u))
+        return fail(AD_E_ALIGN, "part_o must be 16-byte and part_lse 4-byte aligned");
+    p.write_empty = 1;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    hipError_t e = ad::launch_partial_mla(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "MLA split-KV launch");
+    return ok();
 }
 
 const char *attn_decode_last_error(void) { return g_error.c_str(); }

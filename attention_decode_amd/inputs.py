@@ -75,27 +75,43 @@ class Workload:
                 setattr(out, f, t.to(device))
         return _finish(out)
 
-    def kv_bytes(self) -> int:
-        """Bytes of K and V (MLA: ckv + kpe once) that a decode step must read: each key once per
-        KV head if it is inside the sequence, inside a listed block (block-sparse cache), and
-        visible to at least one query row under the causal / sliding-window bounds."""
+    def kv_bytes_by_group(self) -> list:
+        """Bytes of K and V (MLA: ckv + kpe once) that a decode step must read, per (sequence, KV
+        head) as [B][Hkv] (MLA: one latent head): each key once if it is inside the sequence,
+        inside a listed block (block-sparse cache), and visible to at least one query row under
+        the causal / sliding-window bounds."""
         es = torch.finfo(self.dtype).bits // 8
         lens = [int(x) for x in self.seq_lens.to("cpu")]
         per_tok = self.head_dim_qk * es if self.kind == "mla" else (self.head_dim_qk + self.head_dim_v) * es
         heads = 1 if self.kind == "mla" else self.num_kv_heads
-        total = 0
+        out = []
         for b, L in enumerate(lens):
-            hi = L                                                   # newest query sits at L - 1
+            hi = L                                                                 # newest query sits at L - 1
             lo = max(0, L - self.q_len - self.window + 1) if self.window else 0   # oldest key of the first query
-            if self.num_blocks is None:
-                total += max(0, hi - lo) * heads
-                continue
+            row = []
             for h in range(heads):
-                n = int(self.num_blocks[b, h])
-                for blk in self.block_idx[b, h, :n].tolist():
-                    a, z = max(blk * self.block_size, lo), min((blk + 1) * self.block_size, hi)
-                    total += max(0, z - a)
-        return total * per_tok
+                if self.num_blocks is None:
+                    n = max(0, hi - lo)
+                else:
+                    n = 0
+                    for blk in self.block_idx[b, h, :int(self.num_blocks[b, h])].tolist():
+                        n += max(0, min((blk + 1) * self.block_size, hi) - max(blk * self.block_size, lo))
+                row.append(n * per_tok)
+            out.append(row)
+        return out
+
+    def kv_bytes(self) -> int:
+        """Total of kv_bytes_by_group: the algorithmic KV bytes of one decode step."""
+        return sum(sum(r) for r in self.kv_bytes_by_group())
+
+    def flops(self) -> int:
+        """Multiply-adds x 2 of one step over the visible keys: q.k (head_dim_qk) and p.v (head_dim_v)
+        for every query row of each KV head."""
+        es = torch.finfo(self.dtype).bits // 8
+        per_tok = self.head_dim_qk * es if self.kind == "mla" else (self.head_dim_qk + self.head_dim_v) * es
+        keys = self.kv_bytes() // per_tok
+        rows_per_head = self.q_len * (self.num_q_heads if self.kind == "mla" else self.num_q_heads // self.num_kv_heads)
+        return keys * rows_per_head * (self.head_dim_qk + self.head_dim_v) * 2
 
 
 # token-major view of each storage tensor: (storage name, permutation) per field

@@ -1,7 +1,9 @@
 """Decode-attention benchmark: KV-read GB/s (fraction of HBM peak) and µs per decode step.
 
-Default workload: paged GQA, bf16, batch 64, 32 q / 8 KV heads, head dim 128, page 16, ragged
-seq lens uniform in [128, 8192] over a randomly permuted page pool (seeded, synthetic).
+Default workload (3): paged GQA, bf16, batch 64, 32 q / 8 KV heads, head dim 128, page 16, ragged
+seq lens uniform in [128, 8192] over a randomly permuted page pool (seeded, synthetic). The other
+workloads (--workload 1..5) are the tiny fp32 MHA step, contiguous GQA, block-sparse speculative
+decode and MLA; every one runs the same way.
 
 One step = the whole hot path on inputs already resident in HBM: split planning (host, done once),
 the partial split-KV pass, and the LSE merge, launched through the C ABI on torch's current
@@ -9,10 +11,12 @@ stream. W untimed warm-up steps, then exactly K timed steps bracketed by synchro
 Consecutive steps rotate over enough copies of the KV cache to exceed the 256 MB last-level cache,
 so every step reads its KV from HBM.
 
-`value` = algorithmic KV bytes per step (only keys inside each sequence, K and V once) / step time.
-`roofline` prices the dominant kernel (the partial pass) alone: the same algorithmic bytes over
-its average duration, measured with HIP events recorded on its launch stream around every timed
-launch. `cpu_baseline` times the fp64 oracle on a bounded sample of the same workload on the host.
+`value` = algorithmic KV bytes per step (keys inside each sequence, inside listed blocks and
+visible to some query row; K and V once per KV head, the MLA latent + rotary rows once) / step
+time. `roofline` prices the dominant kernel (the partial pass) alone: the same algorithmic bytes
+over its average duration, measured with HIP events recorded on its launch stream around every
+timed launch; the MLA line adds the matrix-core rate of the same launches. `cpu_baseline` times
+the fp64 oracle on a bounded sample of the same workload on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N] [--no-cpu-baseline]
 """
@@ -28,9 +32,19 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, published
 METRIC = "KV-read GB/s (% of HBM peak) and µs per decode step, GQA bf16 paged"
 LLC_BYTES = 256 << 20
+
+# dominant kernel of each workload: (traffic record tag, kernel name)
+KERNELS = {
+    1: ("partial_valu_contiguous_f32", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
+    2: ("partial_valu_contiguous", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
+    3: ("partial_valu_paged", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
+    4: ("partial_mfma_sparse", "partial_mfma_kernel (split-KV partial pass, matrix cores)"),
+    5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores)"),
+}
 
 
 def log(msg):
@@ -51,14 +65,21 @@ class Step:
         B, Q, Hq, Dv = w.batch, w.q_len, w.num_q_heads, w.head_dim_v
         self.out = torch.empty(B, Q, Hq, Dv, dtype=w.dtype, device=dev)
         self.lse = torch.empty(B, Q, Hq, dtype=torch.float32, device=dev)
+        common = dict(scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max, causal=w.causal,
+                      window=w.window, out=self.out, lse=self.lse)
         self.sets = []
         for c in range(copies):
-            k = w.k if c == 0 else w.k.clone()  # .clone() of a strided view keeps its strides
-            v = w.v if c == 0 else w.v.clone()
-            a = _abi.make_args(w.q, k, v, scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max,
-                               causal=w.causal, window=w.window, out=self.out, lse=self.lse)
-            self.sets.append((a, k, v))
-        self.paged = _abi.make_paged(w.block_table, w.page_size) if w.kind == "paged" else None
+            # .clone() of a strided view keeps its strides
+            if w.kind == "mla":
+                ckv = w.k if c == 0 else w.k.clone()
+                kpe = w.kpe if c == 0 else w.kpe.clone()
+                a = _abi.make_args(w.q, ckv, None, head_dim_qk=w.head_dim_qk, **common)
+                self.sets.append((a, ckv, kpe))
+            else:
+                k = w.k if c == 0 else w.k.clone()
+                v = w.v if c == 0 else w.v.clone()
+                self.sets.append((_abi.make_args(w.q, k, v, **common), k, v))
+        self.paged = _abi.make_paged(w.block_table, w.page_size) if w.kind in ("paged", "mla") else None
         self.sparse = _abi.make_sparse(w.num_blocks, w.block_idx, w.block_size) if w.num_blocks is not None else None
         self.splits, self.chunk = _abi.attn_decode_plan(self.sets[0][0], self.paged, self.sparse)
         if w.num_splits:
@@ -67,27 +88,41 @@ class Step:
         self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
 
     def partial(self, i):
-        a = self.sets[i % len(self.sets)][0]
-        self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.part_o, self.part_lse)
+        a, k, x = self.sets[i % len(self.sets)]
+        if self.w.kind == "mla":
+            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
+        else:
+            self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.part_o, self.part_lse)
 
     def merge(self):
         self.abi.attn_decode_merge(self.part_o, self.part_lse, self.splits, self.out, self.lse)
 
 
+def oracle_kwargs(w):
+    """Arguments of the oracle call for a CPU workload (everything but the row selection)."""
+    kw = dict(scale=w.scale, seq_lens=w.seq_lens, causal=w.causal, window=w.window)
+    if w.kind in ("paged", "mla"):
+        kw.update(block_table=w.block_table, page_size=w.page_size)
+    if w.num_blocks is not None:
+        kw.update(num_blocks=w.num_blocks, block_idx=w.block_idx, block_size=w.block_size)
+    if w.kind == "mla":
+        kw.update(q2=w.q_pe, k2=w.kpe)
+    return kw
+
+
 def cpu_baseline(w_cpu, budget_s=12.0):
-    """The fp64 oracle, as it stands, on whole (b, KV head) groups of the workload until about
-    budget_s seconds of host work; reported in the metric's unit (algorithmic KV GB/s)."""
+    """The fp64 oracle, as it stands, on whole (sequence, KV head) groups of the workload (all
+    their query rows) until about budget_s seconds of host work; reported in the metric's unit
+    (algorithmic KV GB/s)."""
     import oracle
 
     orc = oracle.load()
-    Hq, Hkv, Q = w_cpu.num_q_heads, w_cpu.num_kv_heads, w_cpu.q_len
+    Hq, Q = w_cpu.num_q_heads, w_cpu.q_len
+    Hkv = 1 if w_cpu.kind == "mla" else w_cpu.num_kv_heads
     G = Hq // Hkv
-    es = 2 if w_cpu.dtype.itemsize == 2 else 4
-    per_tok = (w_cpu.head_dim_qk + w_cpu.head_dim_v) * es
-    lens = [int(x) for x in w_cpu.seq_lens]
-    kw = dict(scale=w_cpu.scale, seq_lens=w_cpu.seq_lens, causal=w_cpu.causal, window=w_cpu.window)
-    if w_cpu.kind == "paged":
-        kw.update(block_table=w_cpu.block_table, page_size=w_cpu.page_size)
+    by_group = w_cpu.kv_bytes_by_group()
+    kw = oracle_kwargs(w_cpu)
+    v = w_cpu.k if w_cpu.kind == "mla" else w_cpu.v
     done_bytes, elapsed, groups = 0, 0.0, 0
     order = [(b, h) for b in range(w_cpu.batch) for h in range(Hkv)]
     i = 0
@@ -98,9 +133,9 @@ def cpu_baseline(w_cpu, budget_s=12.0):
         sel = order[i:i + n]
         rows = [(b * Q + t) * Hq + h * G + g for (b, h) in sel for t in range(Q) for g in range(G)]
         t0 = time.perf_counter()
-        orc.attend(w_cpu.q, w_cpu.k, w_cpu.v, rows=rows, **kw)
+        orc.attend(w_cpu.q, w_cpu.k, v, rows=rows, **kw)
         elapsed += time.perf_counter() - t0
-        done_bytes += sum(lens[b] * per_tok for (b, h) in sel)
+        done_bytes += sum(by_group[b][h] for (b, h) in sel)
         groups += n
         i = (i + n) % len(order)
     return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": orc.threads(),
@@ -133,7 +168,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, choices=sorted(KERNELS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -169,10 +204,9 @@ def main():
     w_cpu = inputs.make(args.workload)
     w = w_cpu.to("cuda")
     kv_bytes = w_cpu.kv_bytes()
-    footprint = w.k.untyped_storage().nbytes() + (w.v.untyped_storage().nbytes() if w.v is not w.k else 0)
+    flops = w_cpu.flops()
+    footprint = sum(t.untyped_storage().nbytes() for name, t in w.storage.items() if name != "q" and name != "q_pe")
     copies = max(1, math.ceil((1 << 30) / footprint) + 1) if footprint < (1 << 30) else 2
-    if w.kind == "mla":
-        raise SystemExit("the MLA workload is benchmarked with its own entry point (not wired here yet)")
     step = Step(w, copies)
     log(f"workload {w.name}: {kv_bytes / 1e6:.1f} MB KV/step, splits {step.splits} x {step.chunk} keys, "
         f"{copies} cache copies ({footprint / 1e6:.0f} MB each)")
@@ -201,10 +235,28 @@ def main():
     kern_avg = sum(kern_ms) / K
     gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (kern_avg * 1e-3) / 1e9
+    tflops = flops / (kern_avg * 1e-3) / 1e12
     log(f"step {ms_step * 1e3:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); partial kernel avg "
         f"{kern_avg * 1e3:.1f} us (p10 {kern_ms[K // 10] * 1e3:.1f}, p90 {kern_ms[(9 * K) // 10] * 1e3:.1f}) "
-        f"-> {achieved:.0f} GB/s")
+        f"-> {achieved:.0f} GB/s, {tflops:.0f} TFLOP/s")
 
+    tag, kname = KERNELS[args.workload]
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(tag),
+                "kernel": kname, "kernel_avg_us": round(kern_avg * 1e3, 3)}
+    if w.kind == "mla":
+        roofline["mfma_tflops"] = round(tflops, 1)
+        roofline["mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
+    config = {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+              "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v, "q_len": w.q_len,
+              "kv_tokens": int(w_cpu.seq_lens.sum()), "kv_bytes_per_step": kv_bytes, "flops_per_step": flops,
+              "splits": step.splits, "split_keys": step.chunk, "cache_copies_rotated": copies}
+    if w.page_size:
+        config["page_size"] = w.page_size
+    if w.num_blocks is not None:
+        config["sparse_block"] = w.block_size
+    if w.causal or w.window:
+        config.update(causal=bool(w.causal), window=w.window)
     result = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -219,16 +271,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
-        "data": "synthetic (seeded N(0,1) bf16 Q/K/V, seeded ragged lengths and page permutation)",
-        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-                   "head_dim": w.head_dim_qk, "q_len": w.q_len, "page_size": w.page_size,
-                   "kv_tokens": int(w_cpu.seq_lens.sum()), "kv_bytes_per_step": kv_bytes,
-                   "splits": step.splits, "split_keys": step.chunk, "cache_copies_rotated": copies},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": load_traffic(f"partial_valu_{w.kind}"),
-                     "kernel": "partial_valu_kernel (split-KV partial pass)",
-                     "kernel_avg_us": round(kern_avg * 1e3, 3)},
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded ragged lengths, page permutations and block lists)",
+        "config": config,
+        "roofline": roofline,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample ...")

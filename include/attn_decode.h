@@ -144,7 +144,9 @@ size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *pa
  *   part_lse [batch, q_len, num_q_heads, num_splits] fp32, natural log; a split with no visible
  *            key gets o_s = 0, lse_s = -inf (mslk splitk_kernels.py: zeros when l == 0).
  * args->out and args->lse are ignored. num_splits in [1, AD_MAX_SPLITS]; 0 = the planner's
- * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, G * q_len <= 64.
+ * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, any G * q_len (bf16 with
+ * more than 8 rows per KV head runs on the matrix cores, 32 rows per work unit; otherwise the
+ * vector ALUs take up to 8 rows per work unit).
  */
 int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                         int32_t num_splits, float *part_o, float *part_lse, void *stream);
@@ -184,6 +186,17 @@ int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t
 int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3],
                     const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,
                     int32_t num_splits, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * MLA partial pass alone: the first half of attn_decode_mla with the same arguments, writing
+ * caller-owned partials in the layout of attn_decode_splitkv (part_o [batch, q_len, num_q_heads,
+ * num_splits, 512], part_lse [batch, q_len, num_q_heads, num_splits]), every slot included (a
+ * split past a short sequence's end gets o = 0, lse = -inf). attn_decode_merge finishes the step.
+ * args->out and args->lse are ignored.
+ */
+int attn_decode_mla_splitkv(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3],
+                            const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,
+                            int32_t num_splits, float *part_o, float *part_lse, void *stream);
 
 /* Message for the calling thread's last non-OK return ("" if none). Valid until the thread's
  * next call into the library. */

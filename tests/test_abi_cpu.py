@@ -231,6 +231,20 @@ def test_mla_rejections():
     a.head_dim_qk = 576
     a.dtype = _abi.AD_F32
     assert call(a) == -5
+    a.dtype = _abi.AD_BF16
+    # the partial-pass-only entry point: same checks, then its own partial buffers
+    po = torch.zeros(4096, dtype=torch.float32)
+
+    def call_split(args, part_o=po.data_ptr(), part_lse=po.data_ptr(), kpe_p=kpe.data_ptr()):
+        return L.attn_decode_mla_splitkv(ctypes.byref(args), kpe_p, _abi._s3(kpe), qpe.data_ptr(), _abi._s3(qpe),
+                                         ctypes.byref(pg), 2, part_o, part_lse, None)
+
+    assert call_split(a, kpe_p=None) == -1
+    assert call_split(a, part_o=None) == -1
+    assert call_split(a, part_o=po.data_ptr() + 4) == -4
+    assert call_split(a, part_lse=po.data_ptr() + 2) == -4
+    a.head_dim_v = 256
+    assert call_split(a) == -5
 
 
 def test_errors_raise_in_python():
