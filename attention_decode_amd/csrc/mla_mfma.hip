@@ -14,9 +14,9 @@
 //     registers as the B operand of S^T = K Q^T and its 32 x 512 fp32 output in the accumulation
 //     registers. The KV tile (32 keys x 1152 B) is shared by the 4 waves through LDS, so HBM
 //     delivers each key once per unit and LDS feeds the matrix cores.
-//   * Tiles are copied HBM -> LDS with global_load_lds_dwordx4 (no register staging) into a
-//     3-slot ring: while tile i is computed, tiles i+1 and i+2 are in flight. Each slot is its own
-//     LDS object and the loop is unrolled by 3, so the compiler knows which copies a read depends
+//   * Tiles are copied HBM -> LDS with buffer_load ... lds (no register staging) into a 4-slot
+//     ring: while tile i is computed, tiles i+1 .. i+3 are in flight. Each slot is its own LDS
+//     object and the loop is unrolled by 4, so the compiler knows which copies a read depends
 //     on; a wave waits for its own copies of tile i (vmcnt) and a barrier publishes everybody's.
 //   * A key row in LDS is 72 chunks of 16 B (64 latent + 8 rotary); chunk c of key k sits at
 //     position c ^ f(k). With f(k) = 4*bit1(k) + bits2..3(k), the score operand reads
@@ -50,9 +50,9 @@ constexpr int kRowsPerWave = 32;
 constexpr int kRows = kWaves * kRowsPerWave;      // query rows per work unit
 constexpr int kTile = 32;                         // keys per tile
 constexpr int kLatent = 512, kRope = 64;
-constexpr int kLatBytes = kTile * kLatent * 2;    // latent region of a ring slot: 32 rows x 1 KB
-constexpr int kSlotBytes = kLatBytes + kTile * kRope * 2;  // + rotary region: 32 rows x 128 B
-constexpr int kCopiesPerWave = kTile / kWaves + 1;  // latent rows (one 1-KB copy each) + one rotary copy
+constexpr int kLatBytes = kTile * kLatent * 2;    // latent part of a ring slot: 32 rows x 1 KB
+constexpr int kRopeBytes = kTile * kRope * 2;     // rotary part: 32 rows x 128 B
+constexpr int kCopiesPerWave = kTile / kWaves + 1;  // latent row copies + one rotary copy, per tile and wave
 constexpr int kKs = (kLatent + kRope) / 16;       // k-steps (16 values) of the score product
 constexpr int kLatKs = kLatent / 16;
 constexpr int kSlabs = kLatent / 32;              // 32-column slabs of the output
@@ -66,9 +66,12 @@ constexpr int kAccSlabs = kSlabs - 1;
 // goes further makes the work group recompute its unit exactly: one pass for every row's true
 // max, then the main pass with that max as the reference. The accumulators are never rescaled.
 constexpr float kHeadroom = 64.f;
+constexpr int kPipe = 4;  // LDS operand reads in flight ahead of the matrix products
 
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// Buffer descriptor word 3 for raw (untyped, unswizzled) buffer accesses on the gfx9 family.
+constexpr int kBufferFlags = 0x00020000;
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -92,10 +95,17 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
                                                    0, 0, 0);
 }
 
-// LDS layout of a ring slot. Latent chunk c (16 B) of key k sits at k*1024 + 16*(c ^ F(k)); rotary
-// chunk c of key k at kLatBytes + k*128 + 16*(c ^ Hr(k)). With these permutations the score
+// LDS layout of a ring slot. Latent chunk c (16 B) of key k sits at k*1024 + 16*(c ^ F(k)) of the
+// slot's latent object; rotary chunk c of key k at k*128 + 16*(c ^ Hr(k)) of its rotary object. With these permutations the score
 // operand reads (ds_read_b128: 16 keys, one chunk) and the transposing value reads
 // (ds_read_b64_tr_b16: 4 keys x 4 chunks per 32 lanes) hit distinct banks.
+// The 64-bit value held as (hi, lo) words in lane `l`. The lane read returns a signed int: each
+// word is widened as unsigned, or a low word with bit 31 set would fill the high word with ones.
+__device__ __forceinline__ uint64_t lane_u64(uint32_t hi, uint32_t lo, int l) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, l) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, l);
+}
+
 __device__ __forceinline__ int swz_lat(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
 __device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
 
@@ -128,9 +138,16 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     }
 
     __shared__ int s_map[kMapCapacity];
-    __shared__ __attribute__((aligned(16))) unsigned char s_kv0[kSlotBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char s_kv1[kSlotBytes];
-    __shared__ __attribute__((aligned(16))) unsigned char s_kv2[kSlotBytes];
+    // Ring slots: separate LDS objects, so that the compiler can tell which copies a read or a
+    // store depends on (the rotary parts are written by ordinary stores, never by copies).
+    __shared__ __attribute__((aligned(16))) unsigned char s_lat0[kLatBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_lat1[kLatBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_lat2[kLatBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_lat3[kLatBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_rope0[kRopeBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_rope1[kRopeBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_rope2[kRopeBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char s_rope3[kRopeBytes];
     __shared__ float s_x[kWaves][kRowsPerWave];  // per-row exchange inside a wave
     __shared__ int s_flag[kWaves];
 
@@ -173,29 +190,47 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     const uint16_t *ckv = static_cast<const uint16_t *>(p.k);
     const uint16_t *kpe = static_cast<const uint16_t *>(p.k2);
 
-    // ---- copy tile [base, base + 32) of the split into a ring slot. Wave w copies the latent
-    // rows of keys w, w+4, .., w+28 (one 1-KB copy each: lane i brings chunk i ^ F(key)) and the
-    // rotary rows of keys 8w .. 8w+7 (lane i: key 8w + i/8, chunk (i%8) ^ Hr(key)). Keys past
-    // the split read the unit's query row instead.
-    auto issue = [&](lds_u8 *slot, int base) {
+    // ---- copy tile [base, base + 32) of the split into a ring slot, HBM -> LDS with
+    // buffer_load ... lds (no register staging). Wave w copies the latent rows of keys w, w+4, ..,
+    // w+28 (one 1-KB copy per row, lane i bringing chunk i ^ F(key)) and the rotary rows of keys
+    // 8w .. 8w+7 (lane i: key 8w + i/8, chunk (i%8) ^ Hr(key)). Those 8 keys lie in one page:
+    // tiles start at multiples of 16 and pages hold 16, 32 or 64 keys. Every descriptor covers
+    // only rows the copy may read, so the hardware range check confines it: a latent row is
+    // 1 KB, a rotary group ends after its last key inside the split; lanes beyond read zeros
+    // (the scores of those keys are masked). Latent rows past the split read the unit's query
+    // row instead. The buffer form of the LDS copy matters: the compiler treats the global form
+    // as a possible LDS access of unknown order and would make every LDS read wait for all.
+    const int64_t rope_stride = p.k2_s[1] * 2;  // bytes between the rotary rows of two slots of a page
+    auto issue = [&](lds_u8 *lat_slot, lds_u8 *rope_slot, int base) {
+        // Row addresses of key base + i in lane i (i < 32), computed once per tile on the vector
+        // unit; each copy takes its row with a lane read. Keys past the split get the query row.
+        const int vl = base + (lane & 31);
+        const int vlc = min(vl, t1 - 1);
+        const int64_t pg = s_map[(vlc >> map_shift) - map_first];
+        const int sl = vlc & map_mask;
+        const uint64_t lat_row = vl < t1 ? (uint64_t)(ckv + pg * p.k_s[0] + sl * p.k_s[1]) : (uint64_t)safe_n;
+        const uint64_t rope_row = vl < t1 ? (uint64_t)(kpe + pg * p.k2_s[0] + sl * p.k2_s[1]) : (uint64_t)safe_p;
+        const uint32_t lat_lo = (uint32_t)lat_row, lat_hi = (uint32_t)(lat_row >> 32);
+        const uint32_t rope_lo = (uint32_t)rope_row, rope_hi = (uint32_t)(rope_row >> 32);
 #pragma unroll
         for (int j = 0; j < kTile / kWaves; ++j) {
             const int kk = wave + kWaves * j;  // uniform
-            const int v = base + kk;
-            const int vc = min(v, t1 - 1);
-            const int64_t page = __builtin_amdgcn_readfirstlane(s_map[(vc >> map_shift) - map_first]);
-            const uint16_t *row = v < t1 ? ckv + page * p.k_s[0] + (vc & map_mask) * p.k_s[1] : safe_n;
-            __builtin_amdgcn_global_load_lds(row + ((lane ^ swz_lat(kk)) << 3),
-                                             (__attribute__((address_space(3))) void *)(slot + kk * 1024), 16, 0, 0);
+            const uint64_t row = lane_u64(lat_hi, lat_lo, kk);
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, kLatent * 2, kBufferFlags);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(lat_slot + kk * 1024), 16, (lane ^ swz_lat(kk)) << 4,
+                0, 0, 0);
         }
+        const int v0 = base + 8 * wave;  // uniform: first key of this wave's rotary group
+        const int nv = min(max(t1 - v0, 0), 8);
+        const uint64_t row = lane_u64(rope_hi, rope_lo, 8 * wave);
         const int k = 8 * wave + (lane >> 3);
-        const int v = base + k;
-        const int vc = min(v, t1 - 1);
-        const int64_t page = s_map[(vc >> map_shift) - map_first];
-        const uint16_t *row = v < t1 ? kpe + page * p.k2_s[0] + (vc & map_mask) * p.k2_s[1] : safe_p;
-        __builtin_amdgcn_global_load_lds(row + (((lane & 7) ^ swz_rope(k)) << 3),
-                                         (__attribute__((address_space(3))) void *)(slot + kLatBytes + wave * 1024), 16,
-                                         0, 0);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)row, (short)0, nv > 0 ? (int)((nv - 1) * rope_stride) + kRope * 2 : 0, kBufferFlags);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void *)(rope_slot + wave * 1024), 16,
+            (int)((lane >> 3) * rope_stride) + (((lane & 7) ^ swz_rope(k)) << 4), 0, 0, 0);
     };
 
     // Per-lane LDS offsets inside a slot; every read adds a compile-time offset that fits the DS
@@ -211,7 +246,7 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
 #pragma unroll
         for (int i = 0; i < 8; ++i) k_off[i] = col * 1024 + (((2 * i + half) ^ swz_lat(col)) << 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r_off[i] = kLatBytes + col * 128 + (((2 * i + half) ^ swz_rope(col)) << 4);
+        for (int i = 0; i < 4; ++i) r_off[i] = col * 128 + (((2 * i + half) ^ swz_rope(col)) << 4);
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd)
 #pragma unroll
@@ -235,15 +270,24 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     clear();
 
     // Scores of tile `base` (base-2 units, masked) for row col, 16 keys of this lane.
-    auto scores = [&](const lds_u8 *cur, int base, float (&sv)[16]) {
+    // LDS operand reads run kPipe matrix products ahead of their use: a read issued right before
+    // the product that needs it would stall every product for the full LDS latency.
+    auto k_operand = [&](const lds_u8 *cur, const lds_u8 *rcur, int ks) -> u32x4 {
+        const lds_u8 *at = ks < kLatKs ? cur + k_off[ks & 7] + 256 * (ks >> 3) : rcur + r_off[ks - kLatKs];
+        return *(const __attribute__((address_space(3))) u32x4 *)at;
+    };
+    auto scores = [&](const lds_u8 *cur, const lds_u8 *rcur, int base, float (&sv)[16]) {
         f32x16 sc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sc[j] = 0.f;
+        u32x4 ka[kPipe];
+#pragma unroll
+        for (int i = 0; i < kPipe; ++i) ka[i] = k_operand(cur, rcur, i);
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
-            const int off = ks < kLatKs ? k_off[ks & 7] + 256 * (ks >> 3) : r_off[ks - kLatKs];
-            const u32x4 a = *(const __attribute__((address_space(3))) u32x4 *)(cur + off);
-            sc = mfma(a, qb[ks], sc);
+            __builtin_amdgcn_sched_barrier(0);
+            sc = mfma(ka[ks % kPipe], qb[ks], sc);
+            if (ks + kPipe < kKs) ka[ks % kPipe] = k_operand(cur, rcur, ks + kPipe);
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) sv[j] = sc[j] * p.scale_log2;
@@ -258,9 +302,21 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         }
     };
 
-    auto compute = [&](const lds_u8 *cur, int base) {
+    auto v_operand = [&](const lds_u8 *cur, int t, int s) -> u32x4 {
+        s16x4 part[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd)
+            part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(cur + v_off[4 * rd + (s & 3)] + (16 * t + 8 * rd) * 1024 +
+                                                            256 * (s >> 2)));
+        return __builtin_bit_cast(u32x4, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto compute = [&](const lds_u8 *cur, const lds_u8 *rcur, int base) {
         float sv[16];
-        scores(cur, base, sv);
+        scores(cur, rcur, base, sv);
+        u32x4 vb_pipe[kPipe];  // first value operands, loading while the softmax runs
+#pragma unroll
+        for (int i = 0; i < kPipe; ++i) vb_pipe[i] = v_operand(cur, i / kAccSlabs, i % kAccSlabs);
         float mx = sv[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
@@ -277,60 +333,62 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
             lf += p0 + p1;
         }
-        auto v_operand = [&](int t, int s) -> u32x4 {
-            s16x4 part[2];
-#pragma unroll
-            for (int rd = 0; rd < 2; ++rd)
-                part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(cur + v_off[4 * rd + (s & 3)] +
-                                                                (16 * t + 8 * rd) * 1024 + 256 * (s >> 2)));
-            return __builtin_bit_cast(u32x4, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
-        };
+        // products in order: (t, s) for s < kAccSlabs, t = 0 then 1; then the summed slab, t = 0, 1
+        constexpr int kProducts = 2 * kSlabs;
+        auto prod_t = [](int i) { return i < 2 * kAccSlabs ? i / kAccSlabs : i - 2 * kAccSlabs; };
+        auto prod_s = [](int i) { return i < 2 * kAccSlabs ? i % kAccSlabs : kAccSlabs; };
         u32x4 pa[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) pa[t] = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+        f32x16 part;
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int s = 0; s < kAccSlabs; ++s) o[s] = mfma(pa[t], v_operand(t, s), o[s]);
-#pragma unroll
-        for (int s = kAccSlabs; s < kSlabs; ++s) {
-            f32x16 part = mfma(pa[0], v_operand(0, s), f32x16{});
-            part = mfma(pa[1], v_operand(1, s), part);
-            o[s] += part;
+        for (int i = 0; i < kProducts; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int t = prod_t(i), s = prod_s(i);
+            const u32x4 vb = vb_pipe[i % kPipe];
+            if (i + kPipe < kProducts) vb_pipe[i % kPipe] = v_operand(cur, prod_t(i + kPipe), prod_s(i + kPipe));
+            if (s < kAccSlabs)
+                o[s] = mfma(pa[t], vb, o[s]);
+            else
+                part = mfma(pa[t], vb, t == 0 ? f32x16{} : part);
         }
+        o[kAccSlabs] += part;
     };
 
-    auto max_only = [&](const lds_u8 *cur, int base) {
+    auto max_only = [&](const lds_u8 *cur, const lds_u8 *rcur, int base) {
         float sv[16];
-        scores(cur, base, sv);
+        scores(cur, rcur, base, sv);
         float mx = sv[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
         m = fmaxf(m, pair_max(mx));
     };
 
-    // The ring over the split: before tile `base` is used, each wave waits for its own copies of
-    // it (vmcnt: the copies of the next tile may stay in flight) and a barrier publishes all of
-    // them; the barrier also ends every read of the slot the copy of tile base + 64 then
-    // overwrites. Copies past the end read the query row, so every step issues the same number of
-    // copies and the vmcnt count is exact. At the end every copy has landed and every read is done.
+    // The ring over the split (4 slots, 3 tiles in flight): before tile `base` is used, each wave
+    // waits for its own copies of it (vmcnt: the copies of the next two tiles may stay in flight)
+    // and a barrier publishes all of them; the barrier also ends every read of the slot the copy
+    // of tile base + 3*32 then overwrites. Copies past the end read nothing or the query row, so
+    // every step issues the same number of copies and the vmcnt count is exact. At the end every
+    // copy has landed and every read is done.
     auto run = [&](auto body) {
-        lds_u8 *k0 = (lds_u8 *)s_kv0, *k1 = (lds_u8 *)s_kv1, *k2 = (lds_u8 *)s_kv2;
-        auto step = [&](lds_u8 *cur, lds_u8 *nxt, int base) -> bool {
+        lds_u8 *l0 = (lds_u8 *)s_lat0, *l1 = (lds_u8 *)s_lat1, *l2 = (lds_u8 *)s_lat2, *l3 = (lds_u8 *)s_lat3;
+        lds_u8 *q0 = (lds_u8 *)s_rope0, *q1 = (lds_u8 *)s_rope1, *q2 = (lds_u8 *)s_rope2, *q3 = (lds_u8 *)s_rope3;
+        auto step = [&](lds_u8 *cur, lds_u8 *qcur, lds_u8 *nxt, lds_u8 *qnxt, int base) -> bool {
             if (base >= t1) return false;  // uniform
-            __builtin_amdgcn_s_waitcnt(vmcnt_only(kCopiesPerWave));
+            __builtin_amdgcn_s_waitcnt(vmcnt_only(2 * kCopiesPerWave));
             asm volatile("s_barrier" ::: "memory");
-            issue(nxt, base + 2 * kTile);
-            body(cur, base);
+            issue(nxt, qnxt, base + 3 * kTile);
+            body(cur, qcur, base);
             return true;
         };
-        issue(k0, t0);
-        issue(k1, t0 + kTile);
-        for (int base = t0;; base += 3 * kTile) {
-            if (!step(k0, k2, base)) break;
-            if (!step(k1, k0, base + kTile)) break;
-            if (!step(k2, k1, base + 2 * kTile)) break;
+        issue(l0, q0, t0);
+        issue(l1, q1, t0 + kTile);
+        issue(l2, q2, t0 + 2 * kTile);
+        for (int base = t0;; base += 4 * kTile) {
+            if (!step(l0, q0, l3, q3, base)) break;
+            if (!step(l1, q1, l0, q0, base + kTile)) break;
+            if (!step(l2, q2, l1, q1, base + 2 * kTile)) break;
+            if (!step(l3, q3, l2, q2, base + 3 * kTile)) break;
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
         __syncthreads();
