@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <climits>
 #include <cmath>
 #include <string>
 
@@ -428,6 +429,8 @@ int mla_prepare(const ad_decode_args *args, const void *kpe, const int64_t kpe_s
     if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
     if ((rc = plan_splits(args, paged, nullptr, Path::Mla, num_splits, pl)) != AD_OK) return rc;
+    if ((int64_t)pl->splits * mla_row_blocks(args) * args->batch > INT32_MAX)
+        return fail(AD_E_RANGE, "batch x row blocks x splits exceeds the launch grid");
     *p = base_params(args, *pl);
     p->q2 = q_pe;
     p->k2 = kpe;
