@@ -76,6 +76,8 @@ def lib():
         L.attn_decode_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_decode.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_paged.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_mla.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
@@ -85,7 +87,7 @@ def lib():
                                               P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p]
         L.attn_decode_last_error.restype = ctypes.c_char_p
-        for fn in ("attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
+        for fn in ("attn_decode", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
                    "attn_decode_mla", "attn_decode_mla_splitkv"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
@@ -190,6 +192,15 @@ def attn_decode_merge(part_o, part_lse, num_splits, out, lse=None, stream=None):
     _check("attn_decode_merge",
            lib().attn_decode_merge(_ptr(part_o), _ptr(part_lse), num_splits, B, Q, Hq, Dv, _DTYPE[out.dtype],
                                    _ptr(out), I64x3(*out.stride()[:3]), _ptr(lse), _stream(stream)))
+
+
+def attn_decode(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, num_splits: int, workspace,
+                stream=None):
+    """One-launch decode step; `workspace` (uint8 device tensor) must be zero-filled before its first use."""
+    _check("attn_decode",
+           lib().attn_decode(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                             ctypes.byref(sparse) if sparse else None, num_splits, _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def attn_decode_paged(args: DecodeArgs, paged: Paged, num_splits: int, workspace, stream=None):

@@ -42,6 +42,14 @@ struct PartialParams {
     int32_t write_empty;        // 1: splits past the end still write (0, -inf); 0: they do nothing
     float *part_o;              // [rows][num_splits][head_dim_v]
     float *part_lse;            // [rows][num_splits]
+    // One launch per step: when counters is set, the last split of each work unit (b, KV head,
+    // row block) to finish merges the unit's rows into out / lse. counters[unit] counts arrivals;
+    // zero before the launch, and zero again after it.
+    uint32_t *counters;
+    void *out;
+    int64_t out_s[3];
+    int32_t out_dtype;
+    float *lse;
     // MLA second score part (rope): q_pe rows and kpe rows, 64 columns
     const void *q2;
     int64_t q2_s[3];

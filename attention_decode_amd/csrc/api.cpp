@@ -257,6 +257,67 @@ size_t partial_bytes(const ad_decode_args *a, int S, size_t *lse_offset) {
     return o + align256(rows * S * sizeof(float));
 }
 
+// Work units of the partial pass: (b, KV head, row block), or (b, row block) for MLA.
+int64_t work_units(const ad_decode_args *a, Path path) {
+    if (path == Path::Mla) return (int64_t)a->batch * mla_row_blocks(a);
+    return (int64_t)a->batch * a->num_kv_heads * row_plan(a).blocks;
+}
+
+// Workspace of a whole decode step: a fixed region of arrival counters (one per work unit of the
+// single-launch merge) first, then the partial outputs and LSEs. The counter region has the same
+// place and size for every shape and split count, so partials never land on counters and one
+// zero fill lasts for the workspace's life.
+constexpr size_t kCounterBytes = size_t(1) << 20;
+constexpr int64_t kMaxUnits = (int64_t)(kCounterBytes / sizeof(uint32_t));
+
+size_t step_bytes(const ad_decode_args *a, int S, size_t *lse_offset) {
+    size_t lse = 0;
+    const size_t n = kCounterBytes + partial_bytes(a, S, &lse);
+    if (lse_offset) *lse_offset = kCounterBytes + lse;
+    return n;
+}
+
+// Whether attn_decode merges inside the partial pass (one launch) or with the merge kernel. The
+// in-pass merge makes every work group wait for its stores and an atomic round trip before it
+// leaves, and puts the unit's merge behind its last split; a merge launch costs a few
+// microseconds of launch gap and its own run. One launch wins when the grid is a single round
+// (at most one group per compute unit, so no group waits for a slot) and the units are the vector
+// path's few rows; otherwise two launches. AD_FUSED_MERGE=0/1 forces the choice (testing aid).
+int fuse_merge(const ad_decode_args *a, Path path, int S, bool *fused) {
+    const int force = env_int("AD_FUSED_MERGE");
+    const char *set = getenv("AD_FUSED_MERGE");
+    if (set && *set) {
+        *fused = force != 0;
+        return AD_OK;
+    }
+    int cus = 0;
+    int rc = device_cus(&cus);
+    if (rc != AD_OK) return rc;
+    *fused = !row_plan(a).mfma && work_units(a, path) * S <= cus;
+    return AD_OK;
+}
+
+// Fills the cache addressing of p for a paged cache or a block list (contiguous otherwise) and
+// returns the kernel mode.
+int kv_mode(ad::PartialParams &p, const ad_paged *paged, const ad_sparse *sparse) {
+    if (sparse) {
+        p.num_blocks = sparse->num_blocks;
+        p.block_idx = sparse->block_idx;
+        p.nb_s[0] = sparse->nb_stride[0];
+        p.nb_s[1] = sparse->nb_stride[1];
+        for (int i = 0; i < 3; ++i) p.ix_s[i] = sparse->idx_stride[i];
+        p.block_shift = log2_exact(sparse->block_size);
+        return ad::KV_SPARSE;
+    }
+    if (paged) {
+        p.block_table = paged->block_table;
+        p.bt_stride = paged->bt_stride;
+        p.page_shift = log2_exact(paged->page_size);
+        return ad::KV_PAGED;
+    }
+    return ad::KV_CONTIG;
+}
+
 int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, bool count_by_len, int chunk,
               hipStream_t stream) {
     ad::MergeParams m{};
@@ -307,7 +368,7 @@ size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *pa
     Plan pl{};
     if (plan_splits(args, paged, nullptr, path, num_splits, &pl) != AD_OK) return 0;
     ok();
-    return partial_bytes(args, pl.splits, nullptr);
+    return step_bytes(args, pl.splits, nullptr);
 }
 
 int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
@@ -327,21 +388,7 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
     if ((rc = plan_splits(args, paged, sparse, paged ? Path::Paged : Path::Contig, num_splits, &pl)) != AD_OK)
         return rc;
     ad::PartialParams p = base_params(args, pl);
-    int mode = ad::KV_CONTIG;
-    if (sparse) {
-        mode = ad::KV_SPARSE;
-        p.num_blocks = sparse->num_blocks;
-        p.block_idx = sparse->block_idx;
-        p.nb_s[0] = sparse->nb_stride[0];
-        p.nb_s[1] = sparse->nb_stride[1];
-        for (int i = 0; i < 3; ++i) p.ix_s[i] = sparse->idx_stride[i];
-        p.block_shift = log2_exact(sparse->block_size);
-    } else if (paged) {
-        mode = ad::KV_PAGED;
-        p.block_table = paged->block_table;
-        p.bt_stride = paged->bt_stride;
-        p.page_shift = log2_exact(paged->page_size);
-    }
+    const int mode = kv_mode(p, paged, sparse);
     p.write_empty = 1;
     p.part_o = part_o;
     p.part_lse = part_lse;
@@ -377,38 +424,64 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
     return rc == AD_OK ? ok() : rc;
 }
 
-int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits, void *workspace,
-                      size_t workspace_bytes, void *stream) {
-    int rc = check_args(args, Path::Paged, true);
+int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    const Path path = paged ? Path::Paged : Path::Contig;
+    int rc = check_args(args, path, true);
     if (rc != AD_OK) return rc;
+    if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
     if (args->batch == 0) return ok();
-    if ((rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
     if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
     if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
-    if (args->batch == 0) return ok();
     Plan pl{};
-    if ((rc = plan_splits(args, paged, nullptr, Path::Paged, num_splits, &pl)) != AD_OK) return rc;
+    if ((rc = plan_splits(args, paged, sparse, path, num_splits, &pl)) != AD_OK) return rc;
+    if ((int64_t)args->batch * args->q_len * args->num_q_heads > INT_MAX)
+        return fail(AD_E_UNSUPPORTED, "batch x q_len x num_q_heads must stay below 2^31");
+    if (work_units(args, path) > kMaxUnits)
+        return fail(AD_E_UNSUPPORTED, "%lld work units (batch x KV heads x query-row blocks) exceed %lld",
+                    (long long)work_units(args, path), (long long)kMaxUnits);
     size_t lse_off = 0;
-    const size_t need = partial_bytes(args, pl.splits, &lse_off);
+    const size_t need = step_bytes(args, pl.splits, &lse_off);
     if (workspace_bytes < need)
-        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
-    float *po = static_cast<float *>(workspace);
-    float *plse = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
+        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed for %d splits",
+                    workspace_bytes, need, pl.splits);
+    char *ws = static_cast<char *>(workspace);
     ad::PartialParams p = base_params(args, pl);
-    p.block_table = paged->block_table;
-    p.bt_stride = paged->bt_stride;
-    p.page_shift = log2_exact(paged->page_size);
-    p.write_empty = 0;
-    p.part_o = po;
-    p.part_lse = plse;
+    const int mode = kv_mode(p, paged, sparse);
+    p.part_o = reinterpret_cast<float *>(ws + kCounterBytes);
+    p.part_lse = reinterpret_cast<float *>(ws + lse_off);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_partial(args, p, ad::KV_PAGED, s);
-    if (e != hipSuccess) return hip_fail(e, "paged split-KV launch");
-    // Splits past a sequence's end wrote nothing: row b merges only ceil(L_b / chunk) of them.
-    rc = run_merge(args, po, plse, pl.splits, true, pl.chunk, s);
+    bool fused = false;
+    if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
+    if (fused) {
+        p.write_empty = 0;
+        p.counters = reinterpret_cast<uint32_t *>(ws);
+        p.out = args->out;
+        for (int i = 0; i < 3; ++i) p.out_s[i] = args->out_stride[i];
+        p.out_dtype = args->dtype == AD_BF16 ? ad::DT_BF16 : ad::DT_F32;
+        p.lse = args->lse;
+        hipError_t e = launch_partial(args, p, mode, s);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+        return ok();
+    }
+    // Two launches. A block list's length varies per (b, KV head), so every split slot is written
+    // and merged; otherwise splits past a sequence's end write nothing and row b merges only
+    // ceil(L_b / chunk) of them.
+    p.write_empty = sparse ? 1 : 0;
+    hipError_t e = launch_partial(args, p, mode, s);
+    if (e != hipSuccess) return hip_fail(e, "split-KV launch");
+    rc = run_merge(args, p.part_o, p.part_lse, pl.splits, !sparse, pl.chunk, s);
     return rc == AD_OK ? ok() : rc;
+}
+
+int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    if (!paged) return fail(AD_E_NULL, "paged is NULL");
+    return attn_decode(args, paged, nullptr, num_splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"
@@ -460,10 +533,11 @@ int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t k
     if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
     if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
     size_t lse_off = 0;
-    const size_t need = partial_bytes(args, pl.splits, &lse_off);
+    const size_t need = step_bytes(args, pl.splits, &lse_off);
     if (workspace_bytes < need)
         return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
-    float *po = static_cast<float *>(workspace);
+    // the partials go where every whole-step entry puts them: after the counter region
+    float *po = reinterpret_cast<float *>(static_cast<char *>(workspace) + kCounterBytes);
     float *plse = reinterpret_cast<float *>(static_cast<char *>(workspace) + lse_off);
     p.write_empty = 0;
     p.part_o = po;

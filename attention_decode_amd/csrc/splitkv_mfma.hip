@@ -38,6 +38,7 @@
 //     (TensorRT-LLM mha.cu computeRowSum; FlashInfer mla.cuh compute_mla_pv); the LSE uses the
 //     fp32 sum.
 #include "ad_internal.h"
+#include "fused_merge.h"
 
 #include <limits.h>
 #include <math.h>
@@ -120,6 +121,10 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     };
 
     if (t0 >= t1) {  // uniform
+        if (p.counters) {  // fused merge: only a unit without keys writes here (out = 0, lse = -inf)
+            if (vlen <= 0 && split == 0) fused_write_empty<kThreads, D>(p, nr, out_row);
+            return;
+        }
         if (p.write_empty) {
             for (int i = tid; i < nr * Dv; i += kThreads) {
                 const int r = i / Dv, d = i - r * Dv;
@@ -368,10 +373,17 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
             acc += s_all[(w * kRows + r) * D + d] * f;
         }
         const int64_t row = out_row(r);
-        p.part_o[(row * S + split) * Dv + d] = lsum > 0.f ? acc / lsum : 0.f;
+        // agent-scope stores: a merging group on another XCD reads them (fused merge)
+        store_partial(p.part_o + (row * S + split) * Dv + d, lsum > 0.f ? acc / lsum : 0.f);
         if (d == 0)
-            p.part_lse[row * S + split] =
-                lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY;
+            store_partial(p.part_lse + row * S + split,
+                          lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY);
+    }
+    if (p.counters) {  // one launch per step: the unit's last split merges (s_buf is free now)
+        const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
+        constexpr int kPerThread = (kRows * D + kThreads - 1) / kThreads;
+        fused_arrive_merge<kThreads, D, kPerThread>(p, blockIdx.z * gridDim.y + blockIdx.y, nsplit, nr, out_row,
+                                                 reinterpret_cast<float *>(s_buf));
     }
 }
 

@@ -37,6 +37,7 @@
 //     valid, finite memory) and their probability is exactly 0, so NaN/Inf in unused cache slots
 //     cannot leak into the result.
 #include "ad_internal.h"
+#include "fused_merge.h"
 
 #include <limits.h>
 #include <math.h>
@@ -143,6 +144,10 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     };
 
     if (t0 >= t1) {  // uniform over the work group
+        if (p.counters) {  // fused merge: only a unit without keys writes here (out = 0, lse = -inf)
+            if (vlen <= 0 && split == 0) fused_write_empty<kThreads, D>(p, nr, out_row);
+            return;
+        }
         if (p.write_empty) {
             for (int i = tid; i < nr * Dv; i += kThreads) {
                 const int r = i / Dv, d = i - r * Dv;
@@ -448,10 +453,17 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
             o += s_acc[w][r][d] * f;
         }
         const int64_t row = out_row(r);
-        p.part_o[(row * S + split) * Dv + d] = lsum > 0.f ? o / lsum : 0.f;
+        // agent-scope stores: a merging group on another XCD reads them (fused merge)
+        store_partial(p.part_o + (row * S + split) * Dv + d, lsum > 0.f ? o / lsum : 0.f);
         if (d == 0)
-            p.part_lse[row * S + split] =
-                lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY;
+            store_partial(p.part_lse + row * S + split,
+                          lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY);
+    }
+    if (p.counters) {  // one launch per step: the unit's last split merges (s_acc is free now)
+        const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
+        constexpr int kPerThread = (RP * D + kThreads - 1) / kThreads;
+        fused_arrive_merge<kThreads, D, kPerThread>(p, blockIdx.z * gridDim.y + blockIdx.y, nsplit, nr, out_row,
+                                                 &s_acc[0][0][0]);
     }
 }
 

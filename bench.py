@@ -84,18 +84,28 @@ class Step:
         self.splits, self.chunk = _abi.attn_decode_plan(self.sets[0][0], self.paged, self.sparse)
         if w.num_splits:
             self.splits = w.num_splits
-        self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
-        self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+        # GQA caches: one launch per step (attn_decode: the last split of each work unit merges),
+        # in a workspace zero-filled once. MLA: the partial pass, then the merge kernel.
+        self.fused = w.kind != "mla"
+        if self.fused:
+            nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits)
+            self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        else:
+            self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
+            self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
 
     def partial(self, i):
+        """The step's partial pass (the whole step where the merge is fused into it)."""
         a, k, x = self.sets[i % len(self.sets)]
-        if self.w.kind == "mla":
-            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
+        if self.fused:
+            self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
         else:
-            self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.part_o, self.part_lse)
+            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
 
     def merge(self):
-        self.abi.attn_decode_merge(self.part_o, self.part_lse, self.splits, self.out, self.lse)
+        """The separate merge launch, where the step has one."""
+        if not self.fused:
+            self.abi.attn_decode_merge(self.part_o, self.part_lse, self.splits, self.out, self.lse)
 
 
 def oracle_kwargs(w):

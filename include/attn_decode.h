@@ -129,9 +129,13 @@ typedef struct ad_sparse {
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                      int32_t *num_splits, int32_t *chunk);
 
-/* Bytes of workspace attn_decode_paged / attn_decode_mla need for `num_splits` splits
- * (0: the planner's choice): rows * splits * (head_dim_v + 1) * 4, 256-byte aligned parts.
- * Returns 0 for arguments the calls would reject. */
+/* Bytes of workspace attn_decode / attn_decode_paged / attn_decode_mla need for `num_splits`
+ * splits (0: the planner's choice; with a block list, pass the count attn_decode_plan returns for
+ * it). Layout, the same for every entry point, shape and split count: AD_COUNTER_BYTES of arrival
+ * counters (one 4-byte counter per work unit = sequence x KV head x block of query rows, at most
+ * AD_COUNTER_BYTES / 4 units per call), then the partials, rows * splits * (head_dim_v + 1) * 4
+ * bytes in 256-byte aligned parts. Returns 0 for arguments the calls would reject. */
+#define AD_COUNTER_BYTES (1u << 20)
 size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits);
 
 /*
@@ -164,12 +168,29 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
                       void *out, const int64_t out_stride[3], float *lse, void *stream);
 
 /*
- * Whole decode step over a paged cache: partial pass + merge, writing args->out / args->lse.
+ * Whole decode step, writing args->out / args->lse: the partial pass of attn_decode_splitkv
+ * (contiguous cache, paged cache or a block list over a contiguous cache) and the merge of
+ * attn_decode_merge, in ONE launch where that is faster: the last split of each work unit to
+ * finish merges the unit's splits (same arithmetic, same order: the result is the two-launch
+ * result bit for bit), elected by a counter per work unit that wraps back to zero on the last
+ * arrival (the multi-block mode of TensorRT-LLM xqa mha.cu: a semaphore increment picks the last
+ * CTA, which merges). One launch is used when the step is a single round of work groups on the
+ * vector path (at most one group per compute unit, at most 8 query rows per unit), else the
+ * partial pass and the merge kernel run as two launches in the same workspace. Environment
+ * AD_FUSED_MERGE=0 / 1 forces two launches / one launch (testing aid).
  * workspace: device memory of at least attn_decode_workspace_size(args, paged, num_splits)
- * bytes, 256-byte aligned, scratch for the partials (contents on return are unspecified).
- * num_splits 0 = the planner's choice. Ragged seq_lens are handled per sequence: a split past
- * the end of its sequence does no work.
+ * bytes, 256-byte aligned. Its first AD_COUNTER_BYTES MUST be zero before its first use (zero
+ * the allocation once); every call leaves them zero and writes its partials only after them, so
+ * the workspace is reused as is by any later call, of any shape or split count, and by
+ * attn_decode_mla. One workspace serves one call at a time (calls that overlap on it race).
+ * num_splits 0 = the planner's choice. Ragged seq_lens are handled per sequence: a split past the
+ * end of its sequence does no work, and a sequence without keys gets out = 0, lse = -inf. More
+ * than AD_COUNTER_BYTES / 4 work units: AD_E_UNSUPPORTED.
  */
+int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* attn_decode over a paged cache (paged must not be NULL); the same workspace contract. */
 int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits,
                       void *workspace, size_t workspace_bytes, void *stream);
 
@@ -181,7 +202,9 @@ int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t
  *                the same latent rows, so args->v must be NULL or equal to args->k.
  *   q_pe         [batch, q_len, num_q_heads, 64] with strides q_pe_stride {b, t, hq}
  *   kpe          [pages, page_size, 1, 64] with strides kpe_stride {page, slot, head}
- * The score is scale * (q_nope . ckv_j + q_pe . kpe_j). Workspace as for attn_decode_paged.
+ * The score is scale * (q_nope . ckv_j + q_pe . kpe_j). Partial pass + merge (two launches);
+ * workspace of attn_decode_workspace_size bytes, 256-byte aligned; the call needs no initial
+ * contents, writes only after the counter region and leaves that region as it found it.
  */
 int attn_decode_mla(const ad_decode_args *args, const void *kpe, const int64_t kpe_stride[3],
                     const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,

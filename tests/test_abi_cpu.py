@@ -18,12 +18,12 @@ HEADER = os.path.join(ROOT, "include", "attn_decode.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(attn_decode_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(attn_decode(?:_\w+)?)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
+    for n in ("attn_decode", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
               "attn_decode_workspace_size", "attn_decode_plan", "attn_decode_last_error"):
         assert n in names
 
@@ -101,7 +101,8 @@ def test_many_rows_per_kv_head_pass_validation():
         q, k, v, out = _tensors(dtype=dtype, Hq=Hq, Hkv=1, Q=Q)
         a = _abi.make_args(q, k, v, scale=0.1, out=out)
         rows = 2 * Q * Hq
-        expect = -(-rows * 2 * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
+        # the fixed arrival-counter region, then partial outputs and partial LSEs
+        expect = (1 << 20) + -(-rows * 2 * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
         assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, 2) == expect
 
 
@@ -139,7 +140,7 @@ def test_splitkv_rejects_bad_block_lists():
     assert _splitkv(a, sparse=sp) == -1
 
 
-def _paged_call(a, pg, ws_bytes=1 << 20, ws_ptr=None, S=2):
+def _paged_call(a, pg, ws_bytes=1 << 21, ws_ptr=None, S=2):
     ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8)
     base = ws.data_ptr() + (-ws.data_ptr()) % 256
     return _abi.lib().attn_decode_paged(ctypes.byref(a), ctypes.byref(pg) if pg else None, S,
@@ -176,9 +177,41 @@ def test_paged_rejects_small_workspace():
     bt = torch.zeros(2, 4, dtype=torch.int32)
     a = _abi.make_args(q, pool, pool, scale=0.1, kv_len_max=64, out=out)
     pg = _abi.make_paged(bt, 16)
-    # 2 splits: rows 16 * 2 * 128 * 4 = 16 KiB of partial outputs + 256 B of LSEs
-    assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), 2) == 16384 + 256
-    assert _paged_call(a, pg, ws_bytes=16384)[0] == -6
+    # 2 splits: the 1 MiB arrival-counter region, then rows 16 * 2 * 128 * 4 = 16 KiB of partial
+    # outputs + 256 B of LSEs
+    need = (1 << 20) + 16384 + 256
+    assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), 2) == need
+    assert _paged_call(a, pg, ws_bytes=need - 1)[0] == -6
+
+
+def _decode_call(a, pg=None, sp=None, ws_bytes=1 << 21, ws_ptr=None, S=2):
+    ws = torch.zeros(ws_bytes + 256, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    return _abi.lib().attn_decode(ctypes.byref(a), ctypes.byref(pg) if pg else None, ctypes.byref(sp) if sp else None,
+                                  S, base if ws_ptr is None else ws_ptr, ws_bytes, None), ws
+
+
+def test_decode_rejections():
+    """The one-launch entry checks its workspace, split count, output and cache arguments on the host."""
+    a, keep = _args()
+    assert _decode_call(a, ws_ptr=0)[0] == -6
+    ws = torch.zeros((1 << 21) + 512, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    assert _abi.lib().attn_decode(ctypes.byref(a), None, None, 2, base + 16, 1 << 21, None) == -4
+    need = _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, 2)
+    assert need > 0
+    assert _decode_call(a, ws_bytes=need - 256)[0] == -6
+    assert _decode_call(a, S=-1)[0] == -7
+    assert _decode_call(a, S=_abi.AD_MAX_SPLITS + 1)[0] == -7
+    nb = torch.zeros(2, 2, dtype=torch.int32)
+    sp = _abi.make_sparse(nb, torch.zeros(2, 2, 4, dtype=torch.int32), 24)
+    assert _decode_call(a, sp=sp)[0] == -7
+    pg = _abi.make_paged(torch.zeros(2, 4, dtype=torch.int32), 16)
+    sp = _abi.make_sparse(nb, torch.zeros(2, 2, 4, dtype=torch.int32), 16)
+    assert _decode_call(a, pg=pg, sp=sp)[0] == -5
+    a.out = None
+    assert _decode_call(a)[0] == -1
+    assert ad.attn_decode_last_error() != ""
 
 
 def test_merge_rejections():

@@ -39,7 +39,7 @@ def test_workload1_partials(orc):
     say("[gpu] workload 1 partials")
     w = inputs.make(1)
     wg = w.to("cuda")
-    step = DecodeStep(wg)
+    step = DecodeStep(wg, fused=False)
     assert step.splits == 4
     step()
     torch.cuda.synchronize()
