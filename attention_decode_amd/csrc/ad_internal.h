@@ -57,6 +57,26 @@ struct PartialParams {
     int64_t k2_s[3];
 };
 
+// Work-group placement of the GQA partial passes: a 1-D grid of (units x splits) groups, unit =
+// (b, KV head, row block), with the split index slowest. The dispatcher deals group L to XCD
+// L % 8, so every XCD gets an equal share of every split index (the later splits of a ragged
+// batch are often empty, and a split-fastest order would pile the full ones onto some XCDs), and
+// the fullest splits are dispatched first.
+struct UnitId {
+    int split, unit, rb, h, b;
+};
+__device__ __forceinline__ UnitId decode_unit(const PartialParams &p) {
+    const int units = p.batch * p.num_kv_heads * p.row_blocks;
+    UnitId u;
+    u.split = blockIdx.x / units;
+    u.unit = blockIdx.x - u.split * units;
+    u.rb = u.unit % p.row_blocks;
+    const int bh = u.unit / p.row_blocks;
+    u.h = bh % p.num_kv_heads;
+    u.b = bh / p.num_kv_heads;
+    return u;
+}
+
 struct MergeParams {
     const float *part_o;
     const float *part_lse;

@@ -184,6 +184,8 @@ int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
     return sp ? (int64_t)sp->max_blocks * sp->block_size : (int64_t)a->kv_len_max;
 }
 
+constexpr int64_t kRaggedChunk = 2048;  // keys per split at most, when lengths may be ragged
+
 int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
                 Plan *out) {
     const int64_t span = key_span(a, sp);
@@ -200,6 +202,10 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         // caches), doubled until every compute unit has a work group, never below 256 keys each.
         S = span >= 2048 ? 2 : 1;
         while (units * S < cus && span / (2 * S) >= 256 && S * 2 <= AD_MAX_SPLITS) S *= 2;
+        // Per-sequence lengths may be ragged: splits of at most kRaggedChunk keys keep the longest
+        // work group near the average share of a compute unit (a uniform cache is best served by
+        // the fewest splits that fill the compute units, as above).
+        if (a->seq_lens) S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, kRaggedChunk)), AD_MAX_SPLITS);
     }
     int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
     chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);
@@ -244,6 +250,8 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
 hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mode, hipStream_t stream) {
     const Rows rows = row_plan(a);
     p.row_blocks = rows.blocks;
+    // one work group per (split, b, KV head, row block) on a 1-D grid
+    if ((int64_t)p.num_splits * a->batch * a->num_kv_heads * rows.blocks > INT_MAX) return hipErrorInvalidConfiguration;
     if (rows.mfma) return ad::launch_partial_mfma(p, a->head_dim_qk, mode, stream);
     return ad::launch_partial_valu(p, a->dtype, a->head_dim_qk, rows.per_unit, mode, stream);
 }

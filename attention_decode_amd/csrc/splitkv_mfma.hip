@@ -101,8 +101,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     constexpr int kSlabs = D / 32; // 32-column slabs of the output
     constexpr int kRowBytes = D * 2;
 
-    const int split = blockIdx.x;
-    const int rb = blockIdx.y % p.row_blocks, h = blockIdx.y / p.row_blocks, b = blockIdx.z;
+    const UnitId wu = decode_unit(p);
+    const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
@@ -382,14 +382,14 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     if (p.counters) {  // one launch per step: the unit's last split merges (s_buf is free now)
         const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
         constexpr int kPerThread = (kRows * D + kThreads - 1) / kThreads;
-        fused_arrive_merge<kThreads, D, kPerThread>(p, blockIdx.z * gridDim.y + blockIdx.y, nsplit, nr, out_row,
+        fused_arrive_merge<kThreads, D, kPerThread>(p, wu.unit, nsplit, nr, out_row,
                                                  reinterpret_cast<float *>(s_buf));
     }
 }
 
 template <int D, int MODE>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
-    dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
+    const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
     hipLaunchKernelGGL((partial_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

@@ -121,8 +121,8 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                   "a step must stay inside one page / listed block (both are >= 16 keys)");
     static_assert(!kBf16 || U % 2 == 0, "bf16 P.V pairs keys");
 
-    const int split = blockIdx.x;
-    const int rb = blockIdx.y % p.row_blocks, h = blockIdx.y / p.row_blocks, b = blockIdx.z;
+    const UnitId wu = decode_unit(p);
+    const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps step bases scalar
     const int slot = lane / LPT, c = lane % LPT;
@@ -462,7 +462,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     if (p.counters) {  // one launch per step: the unit's last split merges (s_acc is free now)
         const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
         constexpr int kPerThread = (RP * D + kThreads - 1) / kThreads;
-        fused_arrive_merge<kThreads, D, kPerThread>(p, blockIdx.z * gridDim.y + blockIdx.y, nsplit, nr, out_row,
+        fused_arrive_merge<kThreads, D, kPerThread>(p, wu.unit, nsplit, nr, out_row,
                                                  &s_acc[0][0][0]);
     }
 }
@@ -472,7 +472,7 @@ hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int kRowLanes = D * (int)sizeof(T) / 16;
     constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
     constexpr int U = AD_VALU_KEYS_PER_SLOT;
-    dim3 grid(p.num_splits, p.num_kv_heads * p.row_blocks, p.batch);
+    const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
     hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }

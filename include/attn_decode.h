@@ -122,9 +122,10 @@ typedef struct ad_sparse {
  * on the calls below) to *num_splits, and the tokens per split to *chunk (either may be NULL).
  * `paged` and `sparse` are nullable and select the path; MLA is selected by head_dim_qk == 576
  * with head_dim_v == 512. The choice fills every compute unit with work units of a few hundred
- * tokens (cf. TensorRT-LLM xqa launchMHA: sub-sequences = min(SMs / (batch * kv heads),
- * tiles per sequence)). Environment AD_NUM_SPLITS forces the count (testing aid, cf. xqa's
- * XQA_NB_SUB_SEQ).
+ * tokens or more (cf. TensorRT-LLM xqa launchMHA: sub-sequences = min(SMs / (batch * kv heads),
+ * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
+ * keeps splits at most 2048 keys long, so that no work group is much longer than the average.
+ * Environment AD_NUM_SPLITS forces the count (testing aid, cf. xqa's XQA_NB_SUB_SEQ).
  */
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                      int32_t *num_splits, int32_t *chunk);
