@@ -78,6 +78,7 @@ def lib():
                                         ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p, ctypes.c_void_p]
         L.attn_decode.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_launches.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, P(ctypes.c_int32)]
         L.attn_decode_paged.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_mla.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
@@ -87,7 +88,7 @@ def lib():
                                               P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p]
         L.attn_decode_last_error.restype = ctypes.c_char_p
-        for fn in ("attn_decode", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
+        for fn in ("attn_decode", "attn_decode_launches", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
                    "attn_decode_mla", "attn_decode_mla_splitkv"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
@@ -201,6 +202,15 @@ def attn_decode(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, nu
            lib().attn_decode(ctypes.byref(args), ctypes.byref(paged) if paged else None,
                              ctypes.byref(sparse) if sparse else None, num_splits, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_launches(args: DecodeArgs, paged: Paged | None = None, sparse: Sparse | None = None,
+                         num_splits: int = 0) -> int:
+    n = ctypes.c_int32()
+    _check("attn_decode_launches",
+           lib().attn_decode_launches(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                                      ctypes.byref(sparse) if sparse else None, num_splits, ctypes.byref(n)))
+    return n.value
 
 
 def attn_decode_paged(args: DecodeArgs, paged: Paged, num_splits: int, workspace, stream=None):

@@ -486,6 +486,27 @@ int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_spar
     return rc == AD_OK ? ok() : rc;
 }
 
+int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                         int32_t num_splits, int32_t *launches) {
+    if (!launches) return fail(AD_E_NULL, "launches is NULL");
+    const Path path = paged ? Path::Paged : Path::Contig;
+    int rc = check_args(args, path, false);
+    if (rc != AD_OK) return rc;
+    if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
+    if (args->batch == 0) {
+        *launches = 0;
+        return ok();
+    }
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, sparse, path, num_splits, &pl)) != AD_OK) return rc;
+    bool fused = false;
+    if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
+    *launches = fused ? 1 : 2;
+    return ok();
+}
+
 int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits, void *workspace,
                       size_t workspace_bytes, void *stream) {
     if (!paged) return fail(AD_E_NULL, "paged is NULL");

@@ -38,12 +38,12 @@ METRIC = "KV-read GB/s (% of HBM peak) and µs per decode step, GQA bf16 paged"
 LLC_BYTES = 256 << 20
 
 # dominant kernel of each workload: (traffic record tag, kernel name)
-KERNELS = {
-    1: ("partial_valu_contiguous_f32", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
-    2: ("partial_valu_contiguous", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
-    3: ("partial_valu_paged", "partial_valu_kernel (split-KV partial pass, vector ALUs)"),
-    4: ("partial_mfma_sparse", "partial_mfma_kernel (split-KV partial pass, matrix cores)"),
-    5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores)"),
+KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (timed together per step)
+    1: ("partial_valu_contiguous_f32", "partial_valu_kernel, merge fused in (one launch per step)"),
+    2: ("partial_valu_contiguous", "partial_valu_kernel, merge fused in (one launch per step)"),
+    3: ("partial_valu_paged", "partial_valu_kernel + merge_kernel (two launches per step)"),
+    4: ("partial_mfma_sparse", "partial_mfma_kernel + merge_kernel (two launches per step)"),
+    5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
 }
 
 
@@ -90,9 +90,30 @@ class Step:
         if self.fused:
             nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits)
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+            self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
+            kind = "partial_mfma_kernel" if "mfma" in KERNELS.get(w.config, ("", ""))[1] else "partial_valu_kernel"
+            if self.launches == 1:
+                self.kernel_name = f"{kind} (merge inside; the whole step)"
+            else:  # the partial pass alone, into buffers of its own
+                self.kernel_name = f"{kind} (partial pass alone; the merge kernel follows it in a step)"
+                self.kpart_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
+                self.kpart_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
         else:
+            self.launches = 2
+            self.kernel_name = "mla_partial_kernel (partial pass alone; the merge kernel follows it in a step)"
             self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
             self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+
+    def kernel(self, i):
+        """The step's dominant kernel alone: the partial pass (with the merge inside it where
+        attn_decode makes one launch)."""
+        a, k, x = self.sets[i % len(self.sets)]
+        if self.launches == 1:
+            self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
+        elif self.fused:
+            self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.kpart_o, self.kpart_lse)
+        else:
+            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
 
     def partial(self, i):
         """The step's partial pass (the whole step where the merge is fused into it)."""
@@ -225,35 +246,49 @@ def main():
     for i in range(args.warmup):
         step.partial(i)
         step.merge()
+        step.kernel(i)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # 1) the headline: K whole steps back to back, one pair of events around them all
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         step.partial(i)
-        ev[i][1].record(stream)
         step.merge()
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_ms.sort()
-    kern_avg = sum(kern_ms) / K
+    # 2) the dominant kernel: K launches of it alone back to back (its average duration)
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record(stream)
+    for i in range(K):
+        step.kernel(i)
+    k1.record(stream)
+    torch.cuda.synchronize()
+    kern_avg = k0.elapsed_time(k1) / K
+    # 3) its spread: the same launches, each between its own events (which add their own time)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        step.kernel(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
     gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (kern_avg * 1e-3) / 1e9
     tflops = flops / (kern_avg * 1e-3) / 1e12
-    log(f"step {ms_step * 1e3:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); partial kernel avg "
-        f"{kern_avg * 1e3:.1f} us (p10 {kern_ms[K // 10] * 1e3:.1f}, p90 {kern_ms[(9 * K) // 10] * 1e3:.1f}) "
-        f"-> {achieved:.0f} GB/s, {tflops:.0f} TFLOP/s")
+    log(f"step {ms_step * 1e3:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); {step.kernel_name} "
+        f"alone {kern_avg * 1e3:.1f} us -> {achieved:.0f} GB/s, {tflops:.0f} TFLOP/s (one launch between events: "
+        f"p10 {kern_ms[K // 10] * 1e3:.1f}, p50 {kern_ms[K // 2] * 1e3:.1f}, p90 {kern_ms[(9 * K) // 10] * 1e3:.1f} us)")
 
     tag, kname = KERNELS[args.workload]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(tag),
-                "kernel": kname, "kernel_avg_us": round(kern_avg * 1e3, 3)}
+                "kernel": step.kernel_name, "kernel_avg_us": round(kern_avg * 1e3, 3),
+                "kernel_event_us_p10_p50_p90": [round(kern_ms[K // 10] * 1e3, 2), round(kern_ms[K // 2] * 1e3, 2),
+                                                round(kern_ms[(9 * K) // 10] * 1e3, 2)]}
     if w.kind == "mla":
         roofline["mfma_tflops"] = round(tflops, 1)
         roofline["mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)

@@ -191,6 +191,13 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
 int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/* Number of kernel launches attn_decode makes for these arguments and num_splits (0 = the
+ * planner's choice): 1 when the merge runs inside the partial pass, 2 when the merge kernel
+ * follows, 0 for an empty batch (e.g. to plan graph capture, or to time the partial kernel on
+ * its own). Checks the arguments as attn_decode does (out is not needed). */
+int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                         int32_t num_splits, int32_t *launches);
+
 /* attn_decode over a paged cache (paged must not be NULL); the same workspace contract. */
 int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits,
                       void *workspace, size_t workspace_bytes, void *stream);

@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_decode", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
+    for n in ("attn_decode", "attn_decode_launches", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
               "attn_decode_workspace_size", "attn_decode_plan", "attn_decode_last_error"):
         assert n in names
 
@@ -285,3 +285,20 @@ def test_errors_raise_in_python():
     with pytest.raises(_abi.ADError) as e:
         _abi.attn_decode_splitkv(a, None, None, 2, torch.zeros(16), torch.zeros(16))
     assert e.value.code == -3 and "multiple" in str(e.value)
+
+
+def test_launch_count_query(monkeypatch):
+    """attn_decode_launches reports one launch (merge inside the partial pass) or two (merge kernel
+    after it), as AD_FUSED_MERGE forces here (no device query is made then), 0 for an empty batch,
+    and checks its arguments like attn_decode."""
+    a, keep = _args()
+    monkeypatch.setenv("AD_FUSED_MERGE", "1")
+    assert ad.attn_decode_launches(a, None, None, 2) == 1
+    monkeypatch.setenv("AD_FUSED_MERGE", "0")
+    assert ad.attn_decode_launches(a, None, None, 2) == 2
+    b, keep2 = _args(batch=0)
+    assert ad.attn_decode_launches(b, None, None, 2) == 0
+    assert _abi.lib().attn_decode_launches(ctypes.byref(a), None, None, 2, None) == -1
+    a.head_dim_qk = 96
+    with pytest.raises(_abi.ADError):
+        ad.attn_decode_launches(a, None, None, 2)
