@@ -10,6 +10,9 @@ Layout conventions (all element strides, last dimension contiguous):
   k, k2, v       contiguous cache: [batch, kv_len, num_kv_heads, dim]
                  paged cache:      [num_pages, page_size, num_kv_heads, dim] + block_table
 Any tensor may be a permuted view (for example a head-major cache viewed token-major).
+A quantised cache passes k and v as uint8 OCP E4M3 bytes with k_scale / v_scale: fp32
+[batch, kv_len, num_kv_heads] (paged: [num_pages, page_size, num_kv_heads]) views of the row
+scales, any strides (zero strides broadcast one scale).
 """
 from __future__ import annotations
 
@@ -24,8 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "oracle.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
 
-F64, F32, BF16 = 0, 1, 2
-_TYPE = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16}
+F64, F32, BF16, E4M3 = 0, 1, 2, 3
+_TYPE = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16, torch.uint8: E4M3}
 
 
 class Problem(ctypes.Structure):
@@ -46,6 +49,8 @@ class Problem(ctypes.Structure):
         ("block_idx", ctypes.c_void_p), ("idx_stride", ctypes.c_int64 * 3), ("block_size", ctypes.c_int32),
         ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("key_lo", ctypes.c_int32), ("key_hi", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("ks_stride", ctypes.c_int64 * 3),
+        ("v_scale", ctypes.c_void_p), ("vs_stride", ctypes.c_int64 * 3),
     ]
 
 
@@ -100,7 +105,7 @@ class Oracle:
     def attend(self, q, k, v, *, scale: float, seq_lens=None, kv_len: int | None = None,
                q2=None, k2=None, block_table=None, page_size: int = 0,
                num_blocks=None, block_idx=None, block_size: int = 0,
-               causal: bool = False, window: int = 0, key_range=None, rows=None):
+               causal: bool = False, window: int = 0, key_range=None, rows=None, k_scale=None, v_scale=None):
         """Returns (out, lse) as float64 numpy arrays.
 
         out is [batch, q_len, num_q_heads, dim_v] (or [len(rows), dim_v] when rows is given) and
@@ -110,8 +115,10 @@ class Oracle:
         keep = [q, k, v, q2, k2]
         B, Q, Hq, Dqk = q.shape
         Hkv = k.shape[2]
-        if q.dtype not in _TYPE or k.dtype not in _TYPE or v.dtype != k.dtype:
+        if q.dtype not in _TYPE or k.dtype not in _TYPE or v.dtype != k.dtype or q.dtype == torch.uint8:
             raise ValueError("unsupported element types")
+        if (k.dtype == torch.uint8) != (k_scale is not None and v_scale is not None):
+            raise ValueError("an fp8 (uint8) cache needs k_scale and v_scale, and only it takes them")
         P = Problem()
         P.batch, P.q_len, P.num_q_heads, P.num_kv_heads = B, Q, Hq, Hkv
         P.dim_qk, P.dim_v = Dqk, v.shape[3]
@@ -147,6 +154,13 @@ class Oracle:
             P.num_blocks, P.nb_stride = nb.data_ptr(), (ctypes.c_int64 * 2)(*nb.stride())
             P.block_idx, P.idx_stride = ix.data_ptr(), (ctypes.c_int64 * 3)(*ix.stride())
             P.block_size = int(block_size)
+        if k_scale is not None:
+            ks, vs = self._cpu(k_scale), self._cpu(v_scale)
+            if ks.dtype != torch.float32 or vs.dtype != torch.float32 or ks.dim() != 3 or vs.dim() != 3:
+                raise ValueError("k_scale / v_scale must be 3-D float32 views")
+            keep += [ks, vs]
+            P.k_scale, P.ks_stride = ks.data_ptr(), (ctypes.c_int64 * 3)(*ks.stride())
+            P.v_scale, P.vs_stride = vs.data_ptr(), (ctypes.c_int64 * 3)(*vs.stride())
         P.causal, P.window = int(bool(causal)), int(window)
         if key_range is None:
             P.key_lo, P.key_hi = 0, -1

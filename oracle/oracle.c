@@ -46,7 +46,16 @@
  *   paged:      base + block_table[b][j / page_size]*st[0] + (j % page_size)*st[1] + hkv*st[2]
  *               (mslk splitk_kernels.py paged branch; TensorRT-LLM xqa page list)
  * The last dimension is contiguous. Elements are fp64, fp32 or bf16 (raw 16-bit patterns), all
- * widened exactly to fp64.
+ * widened exactly to fp64, or, for K and V only, fp8 bytes of a quantised cache (see below).
+ *
+ * Quantised cache (TensorRT-LLM xqa mha.cu: an e4m3 cache with one kvCacheScale for K and V;
+ * mslk splitk_kernels.py, _process_fp8_quantization: row-wise fp8 with a scale per row): every K
+ * (V) element is an OCP E4M3 byte, decoded exactly and multiplied by the fp32 scale of its row,
+ * k_scale[kv_row(scale strides, b, hkv, j)] (the scale array is indexed like the cache rows; a zero
+ * stride broadcasts, all zero is one scale per tensor). The attention then runs on those values.
+ * E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits): exponent field e > 0 gives
+ * (1 + m/8) 2^(e-7), e = 0 gives the subnormal m 2^-9, and S.1111.111 is NaN (no infinities), so
+ * the largest finite magnitude is 1.75 * 2^8 = 448.
  *
  * oracle_merge() is the LSE-weighted combine of per-split (o_s, lse_s) pairs written out in fp64
  * (mslk splitk_kernels.py, _splitK_reduce): M = max_s lse_s, w_s = exp(lse_s - M),
@@ -63,7 +72,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2 };
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_E4M3 = 3 };
 
 typedef struct {
     int32_t batch, q_len, num_q_heads, num_kv_heads;
@@ -84,12 +93,30 @@ typedef struct {
     const int32_t *block_idx; int64_t idx_stride[3]; int32_t block_size;
     int32_t causal, window;
     int32_t key_lo, key_hi; /* key_hi < 0: no range restriction */
+    /* kv_type ORC_E4M3: fp32 scale of every K / V row, indexed like the rows */
+    const float *k_scale; int64_t ks_stride[3];
+    const float *v_scale; int64_t vs_stride[3];
 } oracle_problem;
+
+/* Value of one OCP E4M3 byte, from the format's definition. */
+static double e4m3(uint8_t x)
+{
+    const int sign = x >> 7, e = (x >> 3) & 15, m = x & 7;
+    double mag;
+    if (e == 15 && m == 7)
+        mag = NAN;
+    else if (e == 0)
+        mag = ldexp((double)m, -9);
+    else
+        mag = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
 
 static double widen(const void *base, int32_t type, int64_t i)
 {
     if (type == ORC_F64) return ((const double *)base)[i];
     if (type == ORC_F32) return (double)((const float *)base)[i];
+    if (type == ORC_E4M3) return e4m3(((const uint8_t *)base)[i]);
     /* bf16 is the upper half of an IEEE binary32 pattern */
     uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
     float f;
@@ -133,8 +160,9 @@ static double score(const oracle_problem *P, int64_t b, int64_t t, int64_t hq, i
     double acc = 0.0;
     int64_t qo = b * P->q_stride[0] + t * P->q_stride[1] + hq * P->q_stride[2];
     int64_t ko = kv_row(P, P->k_stride, b, hkv, j);
+    const double ks = P->kv_type == ORC_E4M3 ? (double)P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)] : 1.0;
     for (int64_t d = 0; d < P->dim_qk; d++)
-        acc += widen(P->q, P->q_type, qo + d) * widen(P->k, P->kv_type, ko + d);
+        acc += widen(P->q, P->q_type, qo + d) * (widen(P->k, P->kv_type, ko + d) * ks);
     if (P->dim_qk2 > 0) {
         int64_t qo2 = b * P->q2_stride[0] + t * P->q2_stride[1] + hq * P->q2_stride[2];
         int64_t ko2 = kv_row(P, P->k2_stride, b, hkv, j);
@@ -154,6 +182,8 @@ static int check_problem(const oracle_problem *P)
     if (P->block_table && P->page_size <= 0) return -1;
     if (P->num_blocks && (!P->block_idx || P->block_size <= 0)) return -1;
     if (P->window < 0) return -1;
+    if (P->q_type == ORC_E4M3) return -1;
+    if (P->kv_type == ORC_E4M3 && (!P->k_scale || !P->v_scale || P->dim_qk2 > 0)) return -1;
     return 0;
 }
 
@@ -225,8 +255,10 @@ int oracle_attend(const oracle_problem *P, const int64_t *rows, int64_t nrows, d
             if (!vis[j]) continue;
             double w = exp(s[j] - m);
             int64_t vo = kv_row(P, P->v_stride, b, hkv, j);
+            const double vs =
+                P->kv_type == ORC_E4M3 ? (double)P->v_scale[kv_row(P, P->vs_stride, b, hkv, j)] : 1.0;
             l += w;
-            for (int64_t d = 0; d < P->dim_v; d++) o[d] += w * widen(P->v, P->kv_type, vo + d);
+            for (int64_t d = 0; d < P->dim_v; d++) o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);
         }
         for (int64_t d = 0; d < P->dim_v; d++) o[d] /= l;
         lse[i] = m + log(l);

@@ -361,11 +361,129 @@ def pin_key_order_invariance(orc):
     _close(a[1], b_[1], what="lse")
 
 
+
+# ------------------------------------------------------------------ fp8 (E4M3) cache
+def _e4m3_lib(bytes_u8):
+    """Library decode of OCP E4M3 bytes (torch.float8_e4m3fn), widened to fp64."""
+    return bytes_u8.view(torch.float8_e4m3fn).double()
+
+
+def _fp8_one_key(orc, v_bytes, k_bytes, ks, vs, q):
+    """One sequence, one KV head, one visible key: out = dequantised v row, lse = its logit."""
+    Dk, Dv = k_bytes.numel(), v_bytes.numel()
+    k = k_bytes.reshape(1, 1, 1, Dk)
+    v = v_bytes.reshape(1, 1, 1, Dv)
+    kscale = torch.tensor([ks], dtype=torch.float32).reshape(1, 1, 1)
+    vscale = torch.tensor([vs], dtype=torch.float32).reshape(1, 1, 1)
+    return orc.attend(q, k, v, scale=0.7, seq_lens=torch.tensor([1], dtype=torch.int32),
+                      k_scale=kscale, v_scale=vscale)
+
+
+def pin_e4m3_decode_library(orc):
+    """Every non-NaN E4M3 byte, as a value row behind one visible key, comes back as PyTorch's
+    float8_e4m3fn decoding times the row scale; the logit uses the key bytes' decoding times the
+    key scale."""
+    allb = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    finite = allb[(allb & 0x7F) != 0x7F]  # 254 bytes: S.1111.111 is NaN
+    g = _gen(31)
+    kb = finite[torch.randperm(finite.numel(), generator=g)[:40]]
+    q = _randn(g, 1, 1, 2, 40) * 0.01
+    for ks, vs in ((1.0, 1.0), (0.375, 2.5), (3.0, 0.0078125)):
+        out, lse = _fp8_one_key(orc, finite, kb, ks, vs, q)
+        _close(out[0, 0, 0], (_e4m3_lib(finite) * vs).numpy(), tol=0.0, what="dequantised values")
+        for h in range(2):
+            s = 0.7 * float((q[0, 0, h] * (_e4m3_lib(kb) * ks)).sum())
+            assert abs(lse[0, 0, h] - s) <= 1e-12 * max(1.0, abs(s)), "logit of the dequantised key"
+
+
+def pin_e4m3_closed_forms(orc):
+    """Values the E4M3 definition fixes: 0x38 = 1, 0xC0 = -2, 0x7E = 448 (largest), 0x08 = 2^-6
+    (smallest normal), 0x01 = 2^-9 (smallest subnormal), 0x80 = 0x00 = 0, 0x39 = 1.125, 0x07 =
+    7 * 2^-9, and 0x7F / 0xFF are NaN."""
+    codes = torch.tensor([0x38, 0xC0, 0x7E, 0x08, 0x01, 0x80, 0x00, 0x39, 0x07], dtype=torch.int32).to(torch.uint8)
+    want = [1.0, -2.0, 448.0, 2.0 ** -6, 2.0 ** -9, -0.0, 0.0, 1.125, 7 * 2.0 ** -9]
+    q = torch.zeros(1, 1, 1, 4, dtype=torch.float64)
+    kb = torch.tensor([0x38] * 4, dtype=torch.int32).to(torch.uint8)
+    out, _ = _fp8_one_key(orc, codes, kb, 1.0, 1.0, q)
+    assert out[0, 0, 0].tolist() == want, out[0, 0, 0].tolist()  # (an output of -0 reads as +0)
+    nan_row = torch.tensor([0x7F, 0xFF, 0x38], dtype=torch.int32).to(torch.uint8)
+    out, _ = _fp8_one_key(orc, nan_row, kb, 1.0, 1.0, q)
+    assert math.isnan(out[0, 0, 0, 0]) and math.isnan(out[0, 0, 0, 1]) and out[0, 0, 0, 2] == 1.0
+
+
+def _fp8_cache(g, B, L, Hkv, D):
+    """Random E4M3 bytes (no NaN codes) for K and V, plus positive row scales for each, the K
+    scales stored head-major and the V scales token-major (different strides)."""
+    def bytes_():
+        x = torch.randint(0, 256, (B, L, Hkv, D), generator=g, dtype=torch.int32)
+        x = torch.where((x & 0x7F) == 0x7F, x - 1, x)
+        return x.to(torch.uint8)
+    k, v = bytes_(), bytes_()
+    ks = (torch.rand(B, Hkv, L, generator=g, dtype=torch.float64) * 0.1 + 0.01).float().permute(0, 2, 1)
+    vs = (torch.rand(B, L, Hkv, generator=g, dtype=torch.float64) * 0.1 + 0.01).float()
+    return k, v, ks, vs
+
+
+def pin_fp8_equals_dequantised(orc):
+    """Attention over an E4M3 cache with row scales equals attention over the fp64 cache built by
+    PyTorch's decoding times the scales (GQA, ragged lengths, causal + window, two query tokens)."""
+    g = _gen(32)
+    B, Q, Hq, Hkv, D, L = 3, 2, 4, 2, 16, 23
+    k, v, ks, vs = _fp8_cache(g, B, L, Hkv, D)
+    q = _randn(g, B, Q, Hq, D) * 0.05
+    lens = torch.tensor([23, 5, 17], dtype=torch.int32)
+    kd = _e4m3_lib(k) * ks.double()[..., None]
+    vd = _e4m3_lib(v) * vs.double()[..., None]
+    a = orc.attend(q, k, v, scale=0.8, seq_lens=lens, causal=True, window=9, k_scale=ks, v_scale=vs)
+    b = orc.attend(q, kd, vd, scale=0.8, seq_lens=lens, causal=True, window=9)
+    _close(a[0], b[0], tol=1e-12, what="out")
+    _close(a[1], b[1], tol=1e-12, what="lse")
+
+
+def pin_fp8_paged_and_broadcast(orc):
+    """An E4M3 cache and its scales scattered over a permuted page pool give the contiguous result
+    bit for bit; one scale per tensor given with zero strides equals a full scale array holding
+    that value everywhere."""
+    g = _gen(33)
+    B, Q, Hq, Hkv, D, P = 2, 1, 4, 2, 8, 4
+    lens = [11, 6]
+    L = max(lens)
+    k, v, ks, vs = _fp8_cache(g, B, L, Hkv, D)
+    q = _randn(g, B, Q, Hq, D) * 0.05
+    npb = [(x + P - 1) // P for x in lens]
+    perm = torch.randperm(sum(npb) + 2, generator=g)
+    kp = torch.full((sum(npb) + 2, P, Hkv, D), 0x7F, dtype=torch.uint8)  # NaN where nothing belongs
+    vp = kp.clone()
+    ksp = torch.full((sum(npb) + 2, P, Hkv), float("nan"), dtype=torch.float32)
+    vsp = ksp.clone()
+    bt = torch.full((B, max(npb)), -1, dtype=torch.int32)
+    i = 0
+    for b in range(B):
+        for p in range(npb[b]):
+            phys = int(perm[i])
+            i += 1
+            bt[b, p] = phys
+            n = min(P, lens[b] - p * P)
+            kp[phys, :n], vp[phys, :n] = k[b, p * P:p * P + n], v[b, p * P:p * P + n]
+            ksp[phys, :n], vsp[phys, :n] = ks[b, p * P:p * P + n], vs[b, p * P:p * P + n]
+    sl = torch.tensor(lens, dtype=torch.int32)
+    a = orc.attend(q, k, v, scale=0.9, seq_lens=sl, k_scale=ks, v_scale=vs)
+    b_ = orc.attend(q, kp, vp, scale=0.9, seq_lens=sl, block_table=bt, page_size=P, k_scale=ksp, v_scale=vsp)
+    assert np.array_equal(a[0], b_[0]) and np.array_equal(a[1], b_[1]), "paged fp8 != contiguous fp8"
+    one_k = torch.tensor([0.03125], dtype=torch.float32).reshape(1, 1, 1).expand(B, L, Hkv)
+    one_v = torch.tensor([0.0625], dtype=torch.float32).reshape(1, 1, 1).expand(B, L, Hkv)
+    c = orc.attend(q, k, v, scale=0.9, seq_lens=sl, k_scale=one_k, v_scale=one_v)
+    d = orc.attend(q, k, v, scale=0.9, seq_lens=sl, k_scale=one_k.contiguous(), v_scale=one_v.contiguous())
+    assert one_k.stride() == (0, 0, 0)
+    assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1]), "broadcast scale != full array"
+
+
 ALL_PINS = [
     pin_library_attention, pin_library_causal_window, pin_library_block_list, pin_golden_visibility,
     pin_one_visible_key, pin_identical_keys, pin_constant_values, pin_large_logits, pin_empty_rows,
     pin_paged_equals_contiguous, pin_layout_and_rows, pin_widening, pin_mla_two_part_score,
     pin_merge_closed_form, pin_merge_identities, pin_split_then_merge, pin_key_order_invariance,
+    pin_e4m3_decode_library, pin_e4m3_closed_forms, pin_fp8_equals_dequantised, pin_fp8_paged_and_broadcast,
 ]
 
 

@@ -33,8 +33,8 @@ MUTANTS = [
     ("page slot index", "(j % P->page_size) * st[1]", "(j / P->page_size) * st[1]"),
     ("page table index", "P->block_table[b * P->bt_stride + j / P->page_size]",
      "P->block_table[b * P->bt_stride + j % P->page_size]"),
-    ("values read from keys", "o[d] += w * widen(P->v, P->kv_type, vo + d);",
-     "o[d] += w * widen(P->k, P->kv_type, vo + d);"),
+    ("values read from keys", "o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);",
+     "o[d] += w * (widen(P->k, P->kv_type, vo + d) * vs);"),
     ("bf16 widening", "<< 16;", "<< 15;"),
     ("block id off by one", "+ i * P->idx_stride[2]] == blk)", "+ i * P->idx_stride[2]] == blk + 1)"),
     ("block of key", "int64_t blk = j / P->block_size;", "int64_t blk = j % P->block_size;"),
@@ -49,6 +49,18 @@ MUTANTS = [
     ("q token stride", "t * P->q_stride[1]", "t * P->q_stride[2]"),
     ("running max", "if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
     ("merge normalisation", "for (int32_t d = 0; d < dim_v; d++) o[d] /= W;", ""),
+    ("e4m3 exponent bias", "mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
+    ("e4m3 subnormal scale", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
+    ("e4m3 mantissa step", "1.0 + m / 8.0", "1.0 + m / 16.0"),
+    ("e4m3 sign dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e4m3 nan code", "if (e == 15 && m == 7)", "if (e == 15)"),
+    ("key scale dropped", "* (widen(P->k, P->kv_type, ko + d) * ks);", "* widen(P->k, P->kv_type, ko + d);"),
+    ("value scale dropped", "o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);",
+     "o[d] += w * widen(P->v, P->kv_type, vo + d);"),
+    ("key scale from value scales", "(double)P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)]",
+     "(double)P->v_scale[kv_row(P, P->ks_stride, b, hkv, j)]"),
+    ("key scale strides", "P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)]",
+     "P->k_scale[kv_row(P, P->vs_stride, b, hkv, j)]"),
 ]
 
 _CHILD = """
