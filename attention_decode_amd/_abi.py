@@ -16,6 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libattn_decode.so")
 
 AD_F32, AD_BF16 = 0, 1
+AD_KV_SAME, AD_KV_FP8_E4M3 = 0, 1
+AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA = 0, 1, 2
 AD_MAX_SPLITS = 256
 STATUS = {0: "AD_OK", -1: "AD_E_NULL", -2: "AD_E_DTYPE", -3: "AD_E_SHAPE", -4: "AD_E_ALIGN",
           -5: "AD_E_UNSUPPORTED", -6: "AD_E_WORKSPACE", -7: "AD_E_RANGE"}
@@ -37,6 +39,9 @@ class DecodeArgs(ctypes.Structure):
         ("causal", ctypes.c_int32), ("window", ctypes.c_int32),
         ("out", ctypes.c_void_p), ("out_stride", I64x3),
         ("lse", ctypes.c_void_p),
+        ("kv_format", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p), ("k_scale_stride", I64x3),
+        ("v_scale", ctypes.c_void_p), ("v_scale_stride", I64x3),
     ]
 
 
@@ -79,6 +84,7 @@ def lib():
         L.attn_decode.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_launches.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, P(ctypes.c_int32)]
+        L.attn_decode_kernel.argtypes = [P(DecodeArgs), P(ctypes.c_int32)]
         L.attn_decode_paged.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                         ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_mla.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
@@ -88,7 +94,7 @@ def lib():
                                               P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p]
         L.attn_decode_last_error.restype = ctypes.c_char_p
-        for fn in ("attn_decode", "attn_decode_launches", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
+        for fn in ("attn_decode", "attn_decode_launches", "attn_decode_kernel", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
                    "attn_decode_mla", "attn_decode_mla_splitkv"):
             getattr(L, fn).restype = ctypes.c_int
         _LIB = L
@@ -121,8 +127,9 @@ def _stream(stream):
 
 
 def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, window=0, out=None, lse=None,
-              head_dim_qk=None):
-    """Fill an ad_decode_args from tensors (q [B,Q,Hq,D]; k/v token-major 4-D views)."""
+              head_dim_qk=None, k_scale=None, v_scale=None):
+    """Fill an ad_decode_args from tensors (q [B,Q,Hq,D]; k/v token-major 4-D views). uint8 k / v
+    are an E4M3 cache, with k_scale / v_scale fp32 3-D views indexed like the cache rows."""
     a = DecodeArgs()
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -139,6 +146,12 @@ def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, w
     a.seq_lens = _ptr(seq_lens)
     a.kv_len_max = int(k.shape[1] if kv_len_max is None else kv_len_max)
     a.causal, a.window = int(bool(causal)), int(window)
+    if k.dtype == torch.uint8:
+        if k_scale is None or v_scale is None or k_scale.dim() != 3 or v_scale.dim() != 3:
+            raise ValueError("an E4M3 (uint8) cache needs 3-D k_scale and v_scale")
+        a.kv_format = AD_KV_FP8_E4M3
+        a.k_scale, a.k_scale_stride = _ptr(k_scale), I64x3(*k_scale.stride())
+        a.v_scale, a.v_scale_stride = _ptr(v_scale), I64x3(*v_scale.stride())
     if out is not None:
         a.out, a.out_stride = _ptr(out), _s3(out)
     a.lse = _ptr(lse)
@@ -211,6 +224,17 @@ def attn_decode_launches(args: DecodeArgs, paged: Paged | None = None, sparse: S
            lib().attn_decode_launches(ctypes.byref(args), ctypes.byref(paged) if paged else None,
                                       ctypes.byref(sparse) if sparse else None, num_splits, ctypes.byref(n)))
     return n.value
+
+
+KERNEL_NAMES = {0: "partial_valu_kernel", 1: "partial_mfma_kernel", 2: "mla_partial_kernel"}
+
+
+def attn_decode_kernel(args: DecodeArgs) -> int:
+    """AD_KERNEL_VECTOR / AD_KERNEL_MATRIX / AD_KERNEL_MLA: the partial-pass kernel the calls run
+    (KERNEL_NAMES maps it to the kernel's name in a profile)."""
+    k = ctypes.c_int32()
+    _check("attn_decode_kernel", lib().attn_decode_kernel(ctypes.byref(args), ctypes.byref(k)))
+    return k.value
 
 
 def attn_decode_paged(args: DecodeArgs, paged: Paged, num_splits: int, workspace, stream=None):

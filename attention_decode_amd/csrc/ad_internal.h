@@ -50,6 +50,13 @@ struct PartialParams {
     int64_t out_s[3];
     int32_t out_dtype;
     float *lse;
+    // Quantised cache: k / v hold OCP E4M3 bytes (k_s / v_s count bytes), each element times the
+    // fp32 scale of its row, k_scale[b|page * ks_s[0] + token|slot * ks_s[1] + h * ks_s[2]].
+    int32_t kv_fp8;
+    const float *k_scale;
+    int64_t ks_s[3];
+    const float *v_scale;
+    int64_t vs_s[3];
     // MLA second score part (rope): q_pe rows and kpe rows, 64 columns
     const void *q2;
     int64_t q2_s[3];

@@ -76,6 +76,8 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
     if (a->window < 0) return fail(AD_E_RANGE, "window must be >= 0");
     if (a->causal != 0 && a->causal != 1) return fail(AD_E_RANGE, "causal must be 0 or 1");
     if (!(std::isfinite(a->scale))) return fail(AD_E_RANGE, "scale must be finite");
+    if (a->kv_format != AD_KV_SAME && a->kv_format != AD_KV_FP8_E4M3)
+        return fail(AD_E_DTYPE, "kv_format %d is not AD_KV_SAME or AD_KV_FP8_E4M3", a->kv_format);
     if (a->batch == 0) return AD_OK;  // nothing is read or written: no pointer is needed
     if (path == Path::Mla) {
         if (a->dtype != AD_BF16) return fail(AD_E_UNSUPPORTED, "MLA supports bf16 only");
@@ -83,18 +85,27 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
             return fail(AD_E_UNSUPPORTED, "MLA needs head_dim_qk 576, head_dim_v 512 and one KV head");
         if (a->v && a->v != a->k)
             return fail(AD_E_UNSUPPORTED, "MLA reads values from the latent cache: v must be NULL or equal k");
+        if (a->kv_format != AD_KV_SAME) return fail(AD_E_UNSUPPORTED, "MLA does not take a quantised cache");
     } else {
         if (a->head_dim_qk != a->head_dim_v) return fail(AD_E_UNSUPPORTED, "head_dim_qk must equal head_dim_v");
         if (a->head_dim_qk != 64 && a->head_dim_qk != 128)
             return fail(AD_E_UNSUPPORTED, "head dim %d not supported (64 or 128)", a->head_dim_qk);
         if (!a->v) return fail(AD_E_NULL, "v is NULL");
+        if (a->kv_format == AD_KV_FP8_E4M3) {
+            if (a->dtype != AD_BF16) return fail(AD_E_UNSUPPORTED, "an fp8 cache is read with bf16 q and out");
+            if (a->head_dim_qk != 128) return fail(AD_E_UNSUPPORTED, "an fp8 cache needs head dim 128");
+            if (!a->k_scale || !a->v_scale) return fail(AD_E_NULL, "k_scale or v_scale is NULL");
+            if ((reinterpret_cast<uintptr_t>(a->k_scale) & 3u) || (reinterpret_cast<uintptr_t>(a->v_scale) & 3u))
+                return fail(AD_E_ALIGN, "k_scale and v_scale must be 4-byte aligned");
+        }
     }
     if (!a->q || !a->k) return fail(AD_E_NULL, "q or k is NULL");
     const int es = elem_bytes(a->dtype);
+    const int kv_es = a->kv_format == AD_KV_FP8_E4M3 ? 1 : es;  // bytes per K / V element
     if (!aligned16(a->q) || !aligned16(a->k) || (a->v && !aligned16(a->v)))
         return fail(AD_E_ALIGN, "q, k and v must be 16-byte aligned");
-    if (!strides_aligned(a->q_stride, es) || !strides_aligned(a->k_stride, es) ||
-        (a->v && !strides_aligned(a->v_stride, es)))
+    if (!strides_aligned(a->q_stride, es) || !strides_aligned(a->k_stride, kv_es) ||
+        (a->v && !strides_aligned(a->v_stride, kv_es)))
         return fail(AD_E_ALIGN, "q/k/v strides must keep every row 16-byte aligned");
     if (need_out) {
         if (!a->out) return fail(AD_E_NULL, "out is NULL");
@@ -129,8 +140,9 @@ int check_sparse(const ad_sparse *sp) {
 int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, 128); }
 
 // Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
-// units: the matrix-core kernel takes 32 rows per unit (bf16 with more than 8 rows), the vector
-// kernel up to 8. AD_PARTIAL_KERNEL=valu|mfma overrides the choice (bf16 only for mfma).
+// units: the matrix-core kernel takes 32 rows per unit (bf16 with more than 8 rows, and any fp8
+// cache), the vector kernel up to 8 (4 with an fp8 cache). AD_PARTIAL_KERNEL=valu|mfma overrides
+// the choice (bf16 only).
 struct Rows {
     bool mfma;
     int per_unit;  // rows one unit holds (the vector kernel's padded row count)
@@ -140,14 +152,18 @@ struct Rows {
 Rows row_plan(const ad_decode_args *a) {
     const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
     const char *force = getenv("AD_PARTIAL_KERNEL");
-    bool mfma = a->dtype == AD_BF16 && r > 8;
+    // an fp8 cache takes the matrix cores by default (the vector path converts too slowly)
+    const bool fp8 = a->kv_format == AD_KV_FP8_E4M3;
+    bool mfma = a->dtype == AD_BF16 && (r > 8 || fp8);
     if (force && a->dtype == AD_BF16) {
         if (!strcmp(force, "mfma")) mfma = true;
         if (!strcmp(force, "valu")) mfma = false;
     }
     Rows x{};
     x.mfma = mfma;
-    x.per_unit = mfma ? 32 : (r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8);
+    // an fp8 unit takes at most 4 rows (8 would exceed a lane's registers)
+    const int valu_max = a->kv_format == AD_KV_FP8_E4M3 ? 4 : 8;
+    x.per_unit = mfma ? 32 : std::min(valu_max, r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8);
     x.blocks = (int)cdiv(r, x.per_unit);
     return x;
 }
@@ -244,6 +260,15 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
     p.window = a->window;
     p.num_splits = pl.splits;
     p.chunk = pl.chunk;
+    if (a->kv_format == AD_KV_FP8_E4M3) {
+        p.kv_fp8 = 1;
+        p.k_scale = a->k_scale;
+        p.v_scale = a->v_scale;
+        for (int i = 0; i < 3; ++i) {
+            p.ks_s[i] = a->k_scale_stride[i];
+            p.vs_s[i] = a->v_scale_stride[i];
+        }
+    }
     return p;
 }
 
@@ -253,7 +278,7 @@ hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mod
     // one work group per (split, b, KV head, row block) on a 1-D grid
     if ((int64_t)p.num_splits * a->batch * a->num_kv_heads * rows.blocks > INT_MAX) return hipErrorInvalidConfiguration;
     if (rows.mfma) return ad::launch_partial_mfma(p, a->head_dim_qk, mode, stream);
-    return ad::launch_partial_valu(p, a->dtype, a->head_dim_qk, rows.per_unit, mode, stream);
+    return ad::launch_partial_valu(p, a->dtype, a->head_dim_qk, rows.per_unit, mode, stream);  // fp8: p.kv_fp8
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -289,8 +314,9 @@ size_t step_bytes(const ad_decode_args *a, int S, size_t *lse_offset) {
 // in-pass merge makes every work group wait for its stores and an atomic round trip before it
 // leaves, and puts the unit's merge behind its last split; a merge launch costs a few
 // microseconds of launch gap and its own run. One launch wins when the grid is a single round
-// (at most one group per compute unit, so no group waits for a slot) and the units are the vector
-// path's few rows; otherwise two launches. AD_FUSED_MERGE=0/1 forces the choice (testing aid).
+// (at most one group per compute unit, so no group waits for a slot) and a unit holds few rows
+// (at most 8, so its merge is short); otherwise two launches. AD_FUSED_MERGE=0/1 forces the
+// choice (testing aid).
 int fuse_merge(const ad_decode_args *a, Path path, int S, bool *fused) {
     const int force = env_int("AD_FUSED_MERGE");
     const char *set = getenv("AD_FUSED_MERGE");
@@ -301,7 +327,9 @@ int fuse_merge(const ad_decode_args *a, Path path, int S, bool *fused) {
     int cus = 0;
     int rc = device_cus(&cus);
     if (rc != AD_OK) return rc;
-    *fused = !row_plan(a).mfma && work_units(a, path) * S <= cus;
+    const Rows rows = row_plan(a);
+    const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
+    *fused = std::min(r, rows.per_unit) <= 8 && work_units(a, path) * S <= cus;
     return AD_OK;
 }
 
@@ -504,6 +532,16 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
     bool fused = false;
     if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
     *launches = fused ? 1 : 2;
+    return ok();
+}
+
+int attn_decode_kernel(const ad_decode_args *args, int32_t *kind) {
+    if (!kind) return fail(AD_E_NULL, "kind is NULL");
+    if (!args) return fail(AD_E_NULL, "args is NULL");
+    const bool mla = args->head_dim_qk == 576 && args->head_dim_v == 512;
+    const int rc = check_args(args, mla ? Path::Mla : Path::Contig, false);
+    if (rc != AD_OK) return rc;
+    *kind = mla ? AD_KERNEL_MLA : row_plan(args).mfma ? AD_KERNEL_MATRIX : AD_KERNEL_VECTOR;
     return ok();
 }
 

@@ -37,6 +37,13 @@
 //   * P is rounded to bf16 for the P.V product and the output normaliser sums the rounded values
 //     (TensorRT-LLM mha.cu computeRowSum; FlashInfer mla.cuh compute_mla_pv); the LSE uses the
 //     fp32 sum.
+//   * An fp8 (OCP E4M3) cache with fp32 row scales (TensorRT-LLM mha.cu, kvCacheScale; mslk
+//     splitk_kernels.py, _process_fp8_quantization): a lane loads its key's bytes as 16-byte
+//     pieces at 32j + 16*half and converts each into two k-steps of bf16 operands exactly; Q is
+//     loaded in the same head-dim order (the reduction order over the head dim is free as long
+//     as both operands share it). V is converted into the same bf16 LDS tile. The key scales
+//     multiply the fp32 scores; the value scales go into P before its bf16 rounding, and the
+//     normaliser sums the rounded products divided by their scales again.
 #include "ad_internal.h"
 #include "fused_merge.h"
 
@@ -83,6 +90,16 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {  // round to
     return __builtin_bit_cast(uint32_t, r);
 }
 
+// Two OCP E4M3 bytes of w (bytes 0-1, or 2-3 with HI) as a bf16 pair (exact), as a 32-bit word.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pair(uint32_t w) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// 8 E4M3 bytes (two words) as 8 bf16 values, in order.
+__device__ __forceinline__ u32x4 e4m3_x8(uint32_t w0, uint32_t w1) {
+    return u32x4{e4m3_pair<false>(w0), e4m3_pair<true>(w0), e4m3_pair<false>(w1), e4m3_pair<true>(w1)};
+}
+
 __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
@@ -95,11 +112,12 @@ __device__ __forceinline__ int swz(int k) {
     return ((2 * (k & 7)) | ((k >> 3) & 1)) & (D / 8 - 1);
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool FP8>
 __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialParams p) {
     constexpr int kKs = D / 16;    // k-steps of the score product
     constexpr int kSlabs = D / 32; // 32-column slabs of the output
-    constexpr int kRowBytes = D * 2;
+    constexpr int kRowBytes = D * 2;  // one bf16 row of the LDS V tile
+    constexpr int kLoads = FP8 ? kKs / 2 : kKs;  // 16-byte pieces of K (and of V) per lane and key
 
     const UnitId wu = decode_unit(p);
     const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
@@ -140,6 +158,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     __shared__ __attribute__((aligned(16))) unsigned char s_buf[kWaves * kRows * D * 4];
     __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
     __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
+    // fp8 cache: the scales of a wave's 32 tile keys, read back in the score accumulator's key order
+    __shared__ __attribute__((aligned(16))) float s_ks[FP8 ? kWaves : 1][kTile], s_vs[FP8 ? kWaves : 1][kTile];
 
     const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
     const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
@@ -165,7 +185,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
         if (col < nr) {
             const uint16_t *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
 #pragma unroll
-            for (int ks = 0; ks < kKs; ++ks) qb[ks] = ld16(qr + 16 * ks + 8 * half);
+            for (int ks = 0; ks < kKs; ++ks)  // fp8: the head-dim order of the fp8 K operand
+                qb[ks] = ld16(qr + (FP8 ? 32 * (ks / 2) + 16 * half + 8 * (ks % 2) : 16 * ks + 8 * half));
             const int qpos = L - Q + t;
             if (p.causal) hi_r = qpos + 1;
             if (p.window) lo_r = qpos - p.window + 1;
@@ -185,27 +206,39 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
 
     // ---- key addressing: virtual key index v (position in the split's key range) -> logical
     // position and row offsets. Only called with v < t1.
-    const uint16_t *kbase = static_cast<const uint16_t *>(p.k) + (int64_t)h * p.k_s[2];
-    const uint16_t *vbase = static_cast<const uint16_t *>(p.v) + (int64_t)h * p.v_s[2];
+    using KV = std::conditional_t<FP8, uint8_t, uint16_t>;  // one K / V element
+    const KV *kbase = static_cast<const KV *>(p.k) + (int64_t)h * p.k_s[2];
+    const KV *vbase = static_cast<const KV *>(p.v) + (int64_t)h * p.v_s[2];
+    const float *ksbase = p.k_scale + (int64_t)h * p.ks_s[2];  // fp8: row scales, indexed like the rows
+    const float *vsbase = p.v_scale + (int64_t)h * p.vs_s[2];
     if constexpr (MODE != KV_PAGED) {
         kbase += b * p.k_s[0];
         vbase += b * p.v_s[0];
+        if constexpr (FP8) {
+            ksbase += b * p.ks_s[0];
+            vsbase += b * p.vs_s[0];
+        }
     }
     auto logical = [&](int v) -> int {
         if constexpr (MODE == KV_SPARSE) return (s_map[(v >> map_shift) - map_first] << map_shift) + (v & map_mask);
         return v;
     };
-    const uint16_t *safe = qbase;  // finite, always readable, at least D elements
+    // finite (bf16), always readable, at least D elements; an fp8 cache's bytes read from it may
+    // be NaN codes, which never reach the sums (masked scores, zeroed values)
+    const KV *safe = reinterpret_cast<const KV *>(qbase);
 
     struct Buf {
-        u32x4 k[kKs];
-        u32x4 v[kKs];
+        u32x4 k[kLoads];
+        u32x4 v[kLoads];
+        float ks, vs;  // fp8: this lane's key scales as loaded (any value for a key that is not read)
+        bool live;     // fp8: this lane's key is read
         int base;
     };
     auto fetch = [&](Buf &f, int base) {
         f.base = base;
         const int v = base + col;
-        const uint16_t *kp = safe, *vp = safe;
+        const KV *kp = safe, *vp = safe;
+        const float *ksp = p.k_scale, *vsp = p.v_scale;  // the arrays' first scales: always readable
         if (v < t1) {
             if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
                 if (v >= lo_min && v < hi_max) {
@@ -213,19 +246,38 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
                     const int slot = v & map_mask;
                     kp = kbase + page * p.k_s[0] + slot * p.k_s[1];
                     vp = vbase + page * p.v_s[0] + slot * p.v_s[1];
+                    if constexpr (FP8) {
+                        ksp = ksbase + page * p.ks_s[0] + slot * p.ks_s[1];
+                        vsp = vsbase + page * p.vs_s[0] + slot * p.vs_s[1];
+                    }
                 }
             } else {
                 const int pos = logical(v);
                 if (pos < L && pos >= lo_min && pos < hi_max) {
                     kp = kbase + (int64_t)pos * p.k_s[1];
                     vp = vbase + (int64_t)pos * p.v_s[1];
+                    if constexpr (FP8) {
+                        ksp = ksbase + (int64_t)pos * p.ks_s[1];
+                        vsp = vsbase + (int64_t)pos * p.vs_s[1];
+                    }
                 }
             }
         }
+        if constexpr (FP8) {
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) f.k[ks] = ld16(kp + 16 * ks + 8 * half);
+            for (int j = 0; j < kLoads; ++j) f.k[j] = ld16(kp + 32 * j + 16 * half);
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) f.v[ks] = ld16(vp + 16 * ks + 8 * half);
+            for (int j = 0; j < kLoads; ++j) f.v[j] = ld16(vp + 32 * j + 16 * half);
+            // used only once this buffer is current (a select here would wait for the prefetch)
+            f.ks = *ksp;
+            f.vs = *vsp;
+            f.live = kp != safe;
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) f.k[ks] = ld16(kp + 16 * ks + 8 * half);
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) f.v[ks] = ld16(vp + 16 * ks + 8 * half);
+        }
     };
 
     lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;  // this wave's V tile
@@ -243,20 +295,57 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
         for (int j = 0; j < 16; ++j) o[s][j] = 0.f;
 
     auto compute = [&](const Buf &cur, bool full) {
-        // V tile -> LDS (row col, chunk 2ks + half)
+        // V tile -> LDS (row col, chunk 2ks + half); fp8: converted to bf16, chunks 4j + 2*half (+1)
+        if constexpr (FP8) {
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks)
-            *(__attribute__((address_space(3))) u32x4 *)(vw + col * kRowBytes + (((2 * ks + half) ^ swz<D>(col)) << 4)) =
-                cur.v[ks];
+            for (int j = 0; j < kLoads; ++j) {
+                u32x4 w = cur.v[j];
+                if (!full && !cur.live) w = u32x4{0, 0, 0, 0};  // a key that is not read may hold NaN codes
+                const int c0 = 4 * j + 2 * half;
+                *(__attribute__((address_space(3))) u32x4 *)(vw + col * kRowBytes + ((c0 ^ swz<D>(col)) << 4)) =
+                    e4m3_x8(w[0], w[1]);
+                *(__attribute__((address_space(3))) u32x4 *)(vw + col * kRowBytes + (((c0 + 1) ^ swz<D>(col)) << 4)) =
+                    e4m3_x8(w[2], w[3]);
+            }
+            if (half == 0) {  // a key that is not read takes scale 0
+                s_ks[wave][col] = cur.live ? cur.ks : 0.f;
+                s_vs[wave][col] = cur.live ? cur.vs : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks)
+                *(__attribute__((address_space(3))) u32x4 *)(vw + col * kRowBytes + (((2 * ks + half) ^ swz<D>(col)) << 4)) =
+                    cur.v[ks];
+        }
         // S^T = K Q^T
         f32x16 sc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sc[j] = 0.f;
+        if constexpr (FP8) {
 #pragma unroll
-        for (int ks = 0; ks < kKs; ++ks) sc = mfma(cur.k[ks], qb[ks], sc);
+            for (int j = 0; j < kLoads; ++j) {
+                const u32x4 w = cur.k[j];
+                sc = mfma(e4m3_x8(w[0], w[1]), qb[2 * j], sc);
+                sc = mfma(e4m3_x8(w[2], w[3]), qb[2 * j + 1], sc);
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) sc = mfma(cur.k[ks], qb[ks], sc);
+        }
         float sv[16];
+        f32x4 vs4[FP8 ? 4 : 1];  // fp8: value scales of this lane's keys 8*q4 + 4*half + e
+        if constexpr (FP8) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) sv[j] = sc[j] * p.scale_log2;
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const f32x4 k4 = *(const f32x4 *)&s_ks[wave][8 * q4 + 4 * half];
+                vs4[q4] = *(const f32x4 *)&s_vs[wave][8 * q4 + 4 * half];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[4 * q4 + e] = sc[4 * q4 + e] * (p.scale_log2 * k4[e]);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) sv[j] = sc[j] * p.scale_log2;
+        }
         if (!full) {  // uniform
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
@@ -297,8 +386,16 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float p0 = exp2_fast(sv[2 * i] - ms), p1 = exp2_fast(sv[2 * i + 1] - ms);  // exp2(-inf) = 0
-            pk[i] = pack_bf16(p0, p1);
-            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
+            if constexpr (FP8) {  // value scales into P; normaliser from the rounded products / scales
+                const float vs0 = vs4[i / 2][(2 * i) % 4], vs1 = vs4[i / 2][(2 * i + 1) % 4];
+                pk[i] = pack_bf16(p0 * vs0, p1 * vs1);
+                const float r0 = __uint_as_float(pk[i] << 16), r1 = __uint_as_float(pk[i] & 0xFFFF0000u);
+                l += (vs0 != 0.f ? r0 * __builtin_amdgcn_rcpf(vs0) : p0) +
+                     (vs1 != 0.f ? r1 * __builtin_amdgcn_rcpf(vs1) : p1);
+            } else {
+                pk[i] = pack_bf16(p0, p1);
+                l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
+            }
             lf += p0 + p1;
         }
         // O += P V over the tile's two 16-key k-steps
@@ -387,25 +484,29 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool FP8>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
-    hipLaunchKernelGGL((partial_mfma_kernel<D, MODE>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_mfma_kernel<D, MODE, FP8>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool FP8 = false>
 hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
     switch (mode) {
-        case KV_CONTIG: return launch_t<D, KV_CONTIG>(p, s);
-        case KV_PAGED: return launch_t<D, KV_PAGED>(p, s);
-        default: return launch_t<D, KV_SPARSE>(p, s);
+        case KV_CONTIG: return launch_t<D, KV_CONTIG, FP8>(p, s);
+        case KV_PAGED: return launch_t<D, KV_PAGED, FP8>(p, s);
+        default: return launch_t<D, KV_SPARSE, FP8>(p, s);
     }
 }
 
 }  // namespace
 
 hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream) {
+    if (p.kv_fp8) {  // the host admits an fp8 cache with head dim 128 only
+        if (head_dim != 128) return hipErrorInvalidValue;
+        return by_mode<128, true>(p, mode, stream);
+    }
     return head_dim == 64 ? by_mode<64>(p, mode, stream) : by_mode<128>(p, mode, stream);
 }
 

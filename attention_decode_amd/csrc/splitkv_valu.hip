@@ -63,16 +63,6 @@ constexpr float kLazyRescale = 8.f;  // log2 units
 #define AD_VALU_KEYS_PER_SLOT 2
 #endif
 
-template <typename T>
-struct Elem;
-template <>
-struct Elem<float> {
-    static constexpr int kPer16 = 4;
-};
-template <>
-struct Elem<uint16_t> {  // bf16 bit patterns
-    static constexpr int kPer16 = 8;
-};
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -107,14 +97,25 @@ __device__ __forceinline__ bf16x2 pack_bf16(float lo, float hi) {  // round to n
 __device__ __forceinline__ float dot2(bf16x2 a, bf16x2 b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
 }
+// Two OCP E4M3 bytes of w (bytes 0-1, or 2-3 with HI) as a bf16 pair, exactly (every E4M3 value
+// is a bf16 value; the conversion's own scale is 1).
+template <bool HI>
+__device__ __forceinline__ bf16x2 e4m3_pair(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
 
-template <typename T, int D, int RP, int MODE, int U, int LPT>
+// FP8: k and v hold OCP E4M3 bytes with fp32 row scales (bf16 queries); K / V elements are then
+// bytes, each lane still owns 16 of a row, and its query values for them are two 16-B words.
+template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8>
 __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
     constexpr bool kBf16 = sizeof(T) == 2;
-    constexpr int kPer16 = Elem<T>::kPer16;
+    static_assert(!FP8 || kBf16, "an fp8 cache is read with bf16 queries");
+    using KV = std::conditional_t<FP8, uint8_t, T>;           // one K / V element
+    constexpr int kPer16 = 16 / (int)sizeof(KV);              // K / V elements per 16-B piece
     constexpr int kSlots = 64 / LPT;                          // rows per wave-wide load
-    constexpr int kPieces = D * (int)sizeof(T) / (16 * LPT);  // 16-B pieces per lane per row
+    constexpr int kPieces = D * (int)sizeof(KV) / (16 * LPT);  // 16-B pieces per lane per row
     constexpr int kEPL = kPieces * kPer16;                    // elements per lane per row
+    constexpr int kQv = FP8 ? 2 * kPieces : kPieces;          // 16-B query words per lane per row
     constexpr int kStep = kSlots * U;                         // keys per wave per step
     static_assert(kPieces >= 1, "row too short for the lanes sharing it");
     static_assert(MODE == KV_CONTIG || (kStep <= 16 && 16 % kStep == 0),
@@ -179,7 +180,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 
     // ---- query rows of this unit: row r0 + r = t*G + g (hq = h*G + g)
     const T *qbase = static_cast<const T *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
-    u32x4 qv[RP][kPieces];
+    u32x4 qv[RP][kQv];
     int lo[RP], hi[RP];  // visible key positions of row r: [lo, hi)
     int lo_max = INT_MIN, hi_min = INT_MAX;
 #pragma unroll
@@ -194,10 +195,18 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         }
         const T *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
 #pragma unroll
-        for (int i = 0; i < kPieces; ++i) qv[r][i] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < kQv; ++i) qv[r][i] = u32x4{0, 0, 0, 0};
         if (r < nr) {
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) qv[r][i] = ld16(qr + (i * LPT + c) * kPer16);
+            for (int i = 0; i < kPieces; ++i) {
+                const T *src = qr + (i * LPT + c) * kPer16;  // the lane's elements of piece i
+                if constexpr (FP8) {
+                    qv[r][2 * i] = ld16(src);
+                    qv[r][2 * i + 1] = ld16(src + 8);
+                } else {
+                    qv[r][i] = ld16(src);
+                }
+            }
         }
     }
     float qf[kBf16 ? 1 : RP][kBf16 ? 1 : kEPL];  // fp32 queries, prescaled by scale*log2(e)
@@ -211,13 +220,22 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     }
 
     // ---- key addressing
-    const T *kbase = static_cast<const T *>(p.k) + (int64_t)h * p.k_s[2];
-    const T *vbase = static_cast<const T *>(p.v) + (int64_t)h * p.v_s[2];
+    const KV *kbase = static_cast<const KV *>(p.k) + (int64_t)h * p.k_s[2];
+    const KV *vbase = static_cast<const KV *>(p.v) + (int64_t)h * p.v_s[2];
+    // row scales of an fp8 cache, indexed like the rows
+    const float *ksbase = p.k_scale + (int64_t)h * p.ks_s[2];
+    const float *vsbase = p.v_scale + (int64_t)h * p.vs_s[2];
     if constexpr (MODE != KV_PAGED) {
         kbase += b * p.k_s[0];
         vbase += b * p.v_s[0];
+        if constexpr (FP8) {
+            ksbase += b * p.ks_s[0];
+            vsbase += b * p.vs_s[0];
+        }
     }
-    const T *safe = qbase;  // a finite, always-readable row for lanes whose key is not visible
+    // an always-readable row for lanes whose key is not visible (the unit's own query row; for
+    // an fp8 cache its bytes may decode to NaN, which the arithmetic keeps away from the sums)
+    const KV *safe = reinterpret_cast<const KV *>(qbase);
     const int map_mask = (1 << map_shift) - 1;
     const int lane_piece = c * kPer16;
 
@@ -237,6 +255,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     struct Buf {
         u32x4 k[U][kPieces];
         u32x4 v[U][kPieces];
+        float ks[U], vs[U];  // fp8 cache: the keys' row scales as loaded (used only where val[u])
         bool val[U];
         int base, pos0;
     };
@@ -244,8 +263,9 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     auto fetch = [&](Buf &f, int base) {
         f.base = base;
         int pos0 = base;
-        const T *krow = kbase;
-        const T *vrow = vbase;
+        const KV *krow = kbase;
+        const KV *vrow = vbase;
+        const float *ksrow = ksbase, *vsrow = vsbase;
         const bool live = base < t1;  // uniform; a step past the end reads the safe row only
         if (live) {
             if constexpr (MODE == KV_PAGED) {
@@ -253,12 +273,20 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 const int slot0 = base & map_mask;
                 krow = kbase + page * p.k_s[0] + slot0 * p.k_s[1];
                 vrow = vbase + page * p.v_s[0] + slot0 * p.v_s[1];
+                if constexpr (FP8) {
+                    ksrow = ksbase + page * p.ks_s[0] + slot0 * p.ks_s[1];
+                    vsrow = vsbase + page * p.vs_s[0] + slot0 * p.vs_s[1];
+                }
             } else {
                 if constexpr (MODE == KV_SPARSE)
                     pos0 = (__builtin_amdgcn_readfirstlane(s_map[(base >> map_shift) - map_first]) << map_shift) +
                            (base & map_mask);
                 krow = kbase + (int64_t)pos0 * p.k_s[1];
                 vrow = vbase + (int64_t)pos0 * p.v_s[1];
+                if constexpr (FP8) {
+                    ksrow = ksbase + (int64_t)pos0 * p.ks_s[1];
+                    vsrow = vsbase + (int64_t)pos0 * p.vs_s[1];
+                }
             }
         }
         f.pos0 = pos0;
@@ -267,8 +295,15 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
             const int off = u * kSlots + slot;  // key offset inside the step
             bool valid = live && base + off < t1;
             if constexpr (MODE == KV_SPARSE) valid = valid && pos0 + off < L;
-            const T *kp = valid ? krow + off * p.k_s[1] : safe;
-            const T *vp = valid ? vrow + off * p.v_s[1] : safe;
+            const KV *kp = valid ? krow + off * p.k_s[1] : safe;
+            const KV *vp = valid ? vrow + off * p.v_s[1] : safe;
+            if constexpr (FP8) {
+                // A key that is not read loads the array's first scale (always inside the array,
+                // though it may belong to an unused row and hold anything); the arithmetic gives it
+                // scale 0 once this buffer is current (a select here would wait for the prefetch).
+                f.ks[u] = *(valid ? ksrow + off * p.ks_s[1] : p.k_scale);
+                f.vs[u] = *(valid ? vsrow + off * p.vs_s[1] : p.v_scale);
+            }
             f.val[u] = valid;
 #pragma unroll
             for (int i = 0; i < kPieces; ++i) f.k[u][i] = ld16(kp + i * LPT * kPer16 + lane_piece);
@@ -283,10 +318,27 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         float sc[U][RP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            bf16x2 kp8[FP8 ? kPieces : 1][8];  // fp8 cache: the keys' bytes as bf16 pairs, once per key
+            if constexpr (FP8) {
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w = cur.k[u][i][j];
+                        kp8[i][2 * j] = e4m3_pair<false>(w);
+                        kp8[i][2 * j + 1] = e4m3_pair<true>(w);
+                    }
+            }
 #pragma unroll
             for (int r = 0; r < RP; ++r) {
                 float d = 0.f;
-                if constexpr (kBf16) {
+                if constexpr (FP8) {
+#pragma unroll
+                    for (int i = 0; i < kPieces; ++i)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            d = dot2(as_bf16x2(qv[r][2 * i + e / 4][e % 4]), kp8[i][e], d);
+                } else if constexpr (kBf16) {
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
 #pragma unroll
@@ -298,7 +350,10 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                         for (int j = 0; j < 4; ++j) d += qf[r][i * 4 + j] * as_f32(cur.k[u][i][j]);
                 }
                 d = slot_sum<LPT>(d);
-                if constexpr (kBf16) d *= p.scale_log2;
+                if constexpr (FP8)
+                    d *= p.scale_log2 * (cur.val[u] ? cur.ks[u] : 0.f);
+                else if constexpr (kBf16)
+                    d *= p.scale_log2;
                 if constexpr (kMasked) {
                     const int pos = cur.pos0 + u * kSlots + slot;
                     const bool vis = cur.val[u] && pos >= lo[r] && pos < hi[r];
@@ -337,7 +392,51 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
             for (int u = 0; u < U; ++u) sc[u][r] = exp2_fast(sc[u][r] - ms);  // exp2(-inf) = 0
         }
-        if constexpr (kBf16) {
+        if constexpr (FP8) {
+            // P.V over key pairs (u, u+1): each key's V scale goes into its probability before the
+            // bf16 rounding, and the normaliser sums the rounded products divided by their scales
+            // again, so that a row's weights sum exactly as they are multiplied into acc (as the
+            // bf16 path sums its rounded P); a zero scale contributes its probability itself. The
+            // LSE keeps the fp32 sum of the unrounded probabilities.
+#pragma unroll
+            for (int u = 0; u < U; u += 2) {
+                const float vs0 = cur.val[u] ? cur.vs[u] : 0.f, vs1 = cur.val[u + 1] ? cur.vs[u + 1] : 0.f;
+                const float inv0 = __builtin_amdgcn_rcpf(vs0), inv1 = __builtin_amdgcn_rcpf(vs1);
+                bf16x2 pk[RP];
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    pk[r] = pack_bf16(sc[u][r] * vs0, sc[u + 1][r] * vs1);
+                    const uint32_t w = __builtin_bit_cast(uint32_t, pk[r]);
+                    const float r0 = __uint_as_float(w << 16), r1 = __uint_as_float(w & 0xFFFF0000u);
+                    l[r] += (vs0 != 0.f ? r0 * inv0 : sc[u][r]) + (vs1 != 0.f ? r1 * inv1 : sc[u + 1][r]);
+                    lf[r] += sc[u][r] + sc[u + 1][r];
+                }
+#pragma unroll
+                for (int i = 0; i < kPieces; ++i) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        uint32_t w0 = cur.v[u][i][j], w1 = cur.v[u + 1][i][j];  // elements 4j..4j+3
+                        if constexpr (kMasked) {  // a key that was not read may hold NaN codes: 0 * NaN
+                            w0 = cur.val[u] ? w0 : 0u;
+                            w1 = cur.val[u + 1] ? w1 : 0u;
+                        }
+                        // bytes interleaved by key: (u[4j], u1[4j], u[4j+1], u1[4j+1]), then 4j+2, 4j+3
+                        const uint32_t a = __builtin_amdgcn_perm(w1, w0, 0x05010400u);
+                        const uint32_t bq = __builtin_amdgcn_perm(w1, w0, 0x07030602u);
+                        const bf16x2 v0 = e4m3_pair<false>(a), v1 = e4m3_pair<true>(a);
+                        const bf16x2 v2 = e4m3_pair<false>(bq), v3 = e4m3_pair<true>(bq);
+#pragma unroll
+                        for (int r = 0; r < RP; ++r) {
+                            float *o = &acc[r][i * 16 + 4 * j];
+                            o[0] = dot2(pk[r], v0, o[0]);
+                            o[1] = dot2(pk[r], v1, o[1]);
+                            o[2] = dot2(pk[r], v2, o[2]);
+                            o[3] = dot2(pk[r], v3, o[3]);
+                        }
+                    }
+                }
+            }
+        } else if constexpr (kBf16) {
             const bf16x2 ones = as_bf16x2(0x3F803F80u);
 #pragma unroll
             for (int u = 0; u < U; u += 2) {
@@ -467,32 +566,36 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     }
 }
 
-template <typename T, int D, int RP, int MODE>
+template <typename T, int D, int RP, int MODE, bool FP8>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
-    constexpr int kRowLanes = D * (int)sizeof(T) / 16;
+    constexpr int kRowLanes = D * (FP8 ? 1 : (int)sizeof(T)) / 16;
     constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
     constexpr int U = AD_VALU_KEYS_PER_SLOT;
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
-    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int RP>
+template <typename T, int D, int RP, bool FP8>
 hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
     switch (mode) {
-        case KV_CONTIG: return launch_t<T, D, RP, KV_CONTIG>(p, s);
-        case KV_PAGED: return launch_t<T, D, RP, KV_PAGED>(p, s);
-        default: return launch_t<T, D, RP, KV_SPARSE>(p, s);
+        case KV_CONTIG: return launch_t<T, D, RP, KV_CONTIG, FP8>(p, s);
+        case KV_PAGED: return launch_t<T, D, RP, KV_PAGED, FP8>(p, s);
+        default: return launch_t<T, D, RP, KV_SPARSE, FP8>(p, s);
     }
 }
 
-template <typename T, int D>
+// An fp8 unit holds at most 4 rows (the host plans so): 8 rows would need more registers than a
+// lane has, and those instantiations are not built.
+template <typename T, int D, bool FP8 = false>
 hipError_t by_rows(const PartialParams &p, int rows_padded, int mode, hipStream_t s) {
+    constexpr int kMaxRows = FP8 ? 4 : 8;
+    if (rows_padded > kMaxRows) return hipErrorInvalidValue;
     switch (rows_padded) {
-        case 1: return by_mode<T, D, 1>(p, mode, s);
-        case 2: return by_mode<T, D, 2>(p, mode, s);
-        case 4: return by_mode<T, D, 4>(p, mode, s);
-        default: return by_mode<T, D, 8>(p, mode, s);
+        case 1: return by_mode<T, D, 1, FP8>(p, mode, s);
+        case 2: return by_mode<T, D, 2, FP8>(p, mode, s);
+        case 4: return by_mode<T, D, 4, FP8>(p, mode, s);
+        default: return by_mode<T, D, kMaxRows, FP8>(p, mode, s);
     }
 }
 
@@ -500,6 +603,10 @@ hipError_t by_rows(const PartialParams &p, int rows_padded, int mode, hipStream_
 
 hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, int rows_padded, int mode,
                                hipStream_t stream) {
+    if (p.kv_fp8) {  // the host admits an fp8 cache with bf16 queries and head dim 128 only
+        if (dtype != DT_BF16 || head_dim != 128) return hipErrorInvalidValue;
+        return by_rows<uint16_t, 128, true>(p, rows_padded, mode, stream);
+    }
     if (dtype == DT_F32) {
         return head_dim == 64 ? by_rows<float, 64>(p, rows_padded, mode, stream)
                               : by_rows<float, 128>(p, rows_padded, mode, stream);

@@ -3,9 +3,10 @@
 This module draws inputs only: shapes, random values, page permutations, block lists. It holds
 none of the attention arithmetic, and both the HIP path and the CPU reference read the tensors it
 returns. Every draw comes from ``torch.Generator('cpu')`` seeded with ``1000 + config`` (or the
-given seed) in a fixed order, so the same workload is produced on any machine.
+given seed) in a fixed order, so the same workload is produced on any machine. An fp8 cache is
+quantised here, as input preparation (the library and the CPU reference only dequantise it).
 
-The five workloads (sizes of the decode benchmarks this library is measured on):
+The workloads (sizes of the decode benchmarks this library is measured on; 6 is the fp8 form of 3):
 
 1. tiny MHA: B=1, 8 q heads = 8 KV heads, D=64, 1 query, KV len 512 contiguous, fp32,
    scale 1/8, forced 4 KV splits then merge.
@@ -16,6 +17,8 @@ The five workloads (sizes of the decode benchmarks this library is measured on):
    len 32768, bf16, KV blocks of 128 listed per (b, KV head), causal + sliding window 4096.
 5. MLA: B=32, 128 q heads on one latent KV head, q/k dim 576 (512 latent + 64 rope), v dim 512
    (the latent), KV len 8192, bf16, paged with page 64, scale 1/sqrt(192).
+6. workload 3 with its cache quantised to OCP E4M3 (fp8) bytes with one fp32 scale per (token, KV
+   head) row for K and for V (the same lengths and values before quantisation).
 
 Cache layouts: a contiguous cache is stored head-major ``[B, Hkv, L, D]``; a paged pool is stored
 ``[pages, Hkv, page_size, D]``. Both are handed out as token-major *views* ``[B, L, Hkv, D]`` /
@@ -29,7 +32,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-NUM_CONFIGS = 5
+NUM_CONFIGS = 6
 
 
 @dataclass
@@ -63,6 +66,12 @@ class Workload:
     # MLA second score part
     q_pe: torch.Tensor | None = None   # [B, Q, Hq, 64]
     kpe: torch.Tensor | None = None    # [pages, page, 1, 64]
+    # quantised cache: "fp8" = k / v hold OCP E4M3 bytes, with fp32 row scales (views indexed like
+    # the cache rows: [B, L, Hkv] contiguous, [pages, page, Hkv] paged; zero strides for one scale
+    # per tensor)
+    kv_format: str = "same"
+    k_scale: torch.Tensor | None = None
+    v_scale: torch.Tensor | None = None
     storage: dict = field(default_factory=dict)
 
     def to(self, device) -> "Workload":
@@ -80,9 +89,8 @@ class Workload:
         head) as [B][Hkv] (MLA: one latent head): each key once if it is inside the sequence,
         inside a listed block (block-sparse cache), and visible to at least one query row under
         the causal / sliding-window bounds."""
-        es = torch.finfo(self.dtype).bits // 8
         lens = [int(x) for x in self.seq_lens.to("cpu")]
-        per_tok = self.head_dim_qk * es if self.kind == "mla" else (self.head_dim_qk + self.head_dim_v) * es
+        per_tok = self.bytes_per_key()
         heads = 1 if self.kind == "mla" else self.num_kv_heads
         out = []
         for b, L in enumerate(lens):
@@ -100,6 +108,17 @@ class Workload:
             out.append(row)
         return out
 
+    def bytes_per_key(self) -> int:
+        """Bytes one key costs per KV head: its K and V rows (MLA: ckv + kpe once), plus its two
+        fp32 row scales when an fp8 cache has one scale per row."""
+        es = 1 if self.kv_format == "fp8" else torch.finfo(self.dtype).bits // 8
+        if self.kind == "mla":
+            return self.head_dim_qk * es
+        per = (self.head_dim_qk + self.head_dim_v) * es
+        if self.kv_format == "fp8" and self.k_scale is not None and self.k_scale.stride() != (0, 0, 0):
+            per += 8
+        return per
+
     def kv_bytes(self) -> int:
         """Total of kv_bytes_by_group: the algorithmic KV bytes of one decode step."""
         return sum(sum(r) for r in self.kv_bytes_by_group())
@@ -107,9 +126,7 @@ class Workload:
     def flops(self) -> int:
         """Multiply-adds x 2 of one step over the visible keys: q.k (head_dim_qk) and p.v (head_dim_v)
         for every query row of each KV head."""
-        es = torch.finfo(self.dtype).bits // 8
-        per_tok = self.head_dim_qk * es if self.kind == "mla" else (self.head_dim_qk + self.head_dim_v) * es
-        keys = self.kv_bytes() // per_tok
+        keys = self.kv_bytes() // self.bytes_per_key()
         rows_per_head = self.q_len * (self.num_q_heads if self.kind == "mla" else self.num_q_heads // self.num_kv_heads)
         return keys * rows_per_head * (self.head_dim_qk + self.head_dim_v) * 2
 
@@ -130,13 +147,40 @@ def _randn(g, shape, dtype):
 def _finish(w: Workload) -> Workload:
     for f, (src, perm) in _VIEWS[w.kind].items():
         setattr(w, f, w.storage[src].permute(*perm) if perm else w.storage[src])
+    for f in ("k_scale", "v_scale"):  # row scales of an fp8 cache, stored head-major like the cache
+        t = w.storage.get(f)
+        if t is not None:
+            rows = tuple(w.k.shape[:3])
+            setattr(w, f, t.reshape(1, 1, 1).expand(*rows) if t.numel() == 1 else t.permute(0, 2, 1))
     return w
+
+
+E4M3_MAX = 448.0  # largest finite OCP E4M3 magnitude
+
+
+def quantize_e4m3(x: torch.Tensor, per: str):
+    """Input preparation for an fp8 cache: OCP E4M3 bytes of x / scale (round to nearest even,
+    PyTorch's float8_e4m3fn cast) and the fp32 scales, one per row of the last dimension
+    (per="token": amax of the row / 448) or one for the tensor (per="tensor")."""
+    x = x.float()
+    if per == "token":
+        amax = x.abs().amax(dim=-1)
+        scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        q = x / scale[..., None]
+    elif per == "tensor":
+        amax = x.abs().max()
+        scale = (amax / E4M3_MAX if amax > 0 else torch.ones(())).reshape(1)
+        q = x / scale
+    else:
+        raise ValueError(per)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale.float().contiguous()
 
 
 def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len,
                q_len=1, dtype=torch.bfloat16, scale=None, seq_lens=None, seed=0,
-               causal=False, window=0, num_splits=None) -> Workload:
-    """Head-major contiguous cache [B, Hkv, L, D]; `seq_lens` (list) may be ragged (<= kv_len)."""
+               causal=False, window=0, num_splits=None, kv_format="same", kv_scales="token") -> Workload:
+    """Head-major contiguous cache [B, Hkv, L, D]; `seq_lens` (list) may be ragged (<= kv_len).
+    kv_format="fp8": K and V are quantised to E4M3 with row (kv_scales="token") or tensor scales."""
     g = torch.Generator().manual_seed(seed)
     q = _randn(g, (batch, q_len, num_q_heads, head_dim), dtype)
     k = _randn(g, (batch, num_kv_heads, kv_len, head_dim), dtype)
@@ -147,20 +191,25 @@ def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, hea
                  num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim_qk=head_dim,
                  head_dim_v=head_dim, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
                  kv_len_max=kv_len, seq_lens=sl, q=None, k=None, v=None, causal=causal, window=window,
-                 num_splits=num_splits)
+                 num_splits=num_splits, kv_format=kv_format)
     w.storage = {"q": q, "k": k, "v": v}
+    if kv_format == "fp8":
+        w.storage["k"], w.storage["k_scale"] = quantize_e4m3(k, kv_scales)
+        w.storage["v"], w.storage["v_scale"] = quantize_e4m3(v, kv_scales)
     return _finish(w)
 
 
 def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
           q_len=1, dtype=torch.bfloat16, scale=None, seed=0, poison=False, max_pages=None,
-          causal=False, window=0, shuffle_pages=True) -> Workload:
+          causal=False, window=0, shuffle_pages=True, kv_format="same", kv_scales="token") -> Workload:
     """Paged cache: pool [pages, Hkv, page_size, D] (head-major pages), block table [B, max_pages].
 
     The logical content of sequence b depends only on the seed and seq_lens; the physical page
     order is a random permutation. With ``poison`` the pool gets ~5% extra pages nobody
     references, every page and tail slot not covered by a sequence holds NaN, the table is padded
-    with -1, and a different permutation is used -- the logical KV is unchanged.
+    with -1, and a different permutation is used -- the logical KV is unchanged. kv_format="fp8":
+    the same logical K and V quantised to E4M3 (row or tensor scales; poisoned slots hold the E4M3
+    NaN code and NaN scales).
     """
     g = torch.Generator().manual_seed(seed)
     sl = torch.as_tensor(seq_lens, dtype=torch.int32)
@@ -193,8 +242,16 @@ def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_
                  num_q_heads=num_q_heads, num_kv_heads=num_kv_heads, head_dim_qk=head_dim,
                  head_dim_v=head_dim, scale=(1.0 / math.sqrt(head_dim)) if scale is None else scale,
                  kv_len_max=mp * page_size, seq_lens=sl, q=None, k=None, v=None,
-                 block_table=bt, page_size=page_size, causal=causal, window=window)
+                 block_table=bt, page_size=page_size, causal=causal, window=window, kv_format=kv_format)
     w.storage = {"q": q, "k": k_pool, "v": v_pool}
+    if kv_format == "fp8":
+        for name_, pool in (("k", k_pool), ("v", v_pool)):
+            live = ~torch.isnan(pool).any(dim=-1)                    # rows that hold a key
+            qbytes, sc = quantize_e4m3(torch.nan_to_num(pool), kv_scales)
+            qbytes[~live] = 0x7F                                       # E4M3 NaN where nothing belongs
+            if kv_scales == "token":
+                sc = torch.where(live, sc, torch.full_like(sc, float("nan")))
+            w.storage[name_], w.storage[name_ + "_scale"] = qbytes, sc
     return _finish(w)
 
 
@@ -209,14 +266,15 @@ def window_block_list(kv_len: int, q_len: int, window: int, block_size: int):
 
 def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len, q_len,
            block_size, blocks, dtype=torch.bfloat16, scale=None, seed=0, causal=True, window=0,
-           poison=False, seq_lens=None) -> Workload:
+           poison=False, seq_lens=None, kv_format="same", kv_scales="token") -> Workload:
     """Contiguous head-major cache with a per-(b, KV head) list of KV blocks: ``blocks`` is one list
     shared by every (b, KV head), or a nested list blocks[b][h] of lists of any lengths (the index
     array is padded with -1, which is never read). With ``poison`` every key outside the listed
     blocks of its own (b, h), and every key at or past seq_lens[b], holds NaN."""
     w = contiguous(config=config, name=name, batch=batch, num_q_heads=num_q_heads,
                    num_kv_heads=num_kv_heads, head_dim=head_dim, kv_len=kv_len, q_len=q_len,
-                   dtype=dtype, scale=scale, seed=seed, causal=causal, window=window, seq_lens=seq_lens)
+                   dtype=dtype, scale=scale, seed=seed, causal=causal, window=window, seq_lens=seq_lens,
+                   kv_format=kv_format, kv_scales=kv_scales)
     if blocks and isinstance(blocks[0], (list, tuple)):
         lists = [[list(blocks[b][h]) for h in range(num_kv_heads)] for b in range(batch)]
     else:
@@ -237,7 +295,12 @@ def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_di
                     keep[blk * block_size:(blk + 1) * block_size] = True
                 keep[int(w.seq_lens[b]):] = False
                 for name_ in ("k", "v"):
-                    w.storage[name_][b, h, ~keep, :] = float("nan")
+                    if w.kv_format == "fp8":  # the E4M3 NaN code, and NaN row scales
+                        w.storage[name_][b, h, ~keep, :] = 0x7F
+                        if w.storage[name_ + "_scale"].numel() > 1:
+                            w.storage[name_ + "_scale"][b, h, ~keep] = float("nan")
+                    else:
+                        w.storage[name_][b, h, ~keep, :] = float("nan")
     return w
 
 
@@ -307,4 +370,11 @@ def make(config: int, *, seed: int | None = None, poison: bool = False) -> Workl
     if config == 5:
         return mla(config=5, name="mla_bf16_paged64", batch=32, num_heads=128, kv_len=8192, page_size=64,
                    dtype=torch.bfloat16, scale=1.0 / math.sqrt(192), seed=s, poison=poison)
+    if config == 6:  # workload 3's lengths and values, the cache quantised to E4M3 with row scales
+        s3 = 1003 if seed is None else seed
+        g = torch.Generator().manual_seed(s3)
+        lens = torch.randint(128, 8193, (64,), generator=g, dtype=torch.int64).tolist()
+        return paged(config=6, name="paged_gqa_fp8_ragged", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, page_size=16, dtype=torch.bfloat16, seed=s3 + 1, poison=poison,
+                     max_pages=512, kv_format="fp8", kv_scales="token")
     raise ValueError(f"unknown workload {config}")

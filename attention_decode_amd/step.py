@@ -32,7 +32,7 @@ class DecodeStep:
         if w.kind == "mla":
             self.args = _abi.make_args(w.q, w.k, None, head_dim_qk=w.head_dim_qk, **common)
         else:
-            self.args = _abi.make_args(w.q, w.k, w.v, **common)
+            self.args = _abi.make_args(w.q, w.k, w.v, k_scale=w.k_scale, v_scale=w.v_scale, **common)
         if w.kind in ("paged", "mla"):
             self.paged = _abi.make_paged(w.block_table, w.page_size)
         if w.num_blocks is not None:

@@ -44,6 +44,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     3: ("partial_valu_paged", "partial_valu_kernel + merge_kernel (two launches per step)"),
     4: ("partial_mfma_sparse", "partial_mfma_kernel + merge_kernel (two launches per step)"),
     5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
+    6: ("partial_mfma_paged_fp8", "partial_mfma_kernel, fp8 cache + merge_kernel (two launches per step)"),
 }
 
 
@@ -78,7 +79,10 @@ class Step:
             else:
                 k = w.k if c == 0 else w.k.clone()
                 v = w.v if c == 0 else w.v.clone()
-                self.sets.append((_abi.make_args(w.q, k, v, **common), k, v))
+                ks, vs = w.k_scale, w.v_scale  # an fp8 cache's row scales rotate with it
+                if c and ks is not None and ks.stride() != (0, 0, 0):
+                    ks, vs = ks.clone(), vs.clone()
+                self.sets.append((_abi.make_args(w.q, k, v, k_scale=ks, v_scale=vs, **common), k, v, ks, vs))
         self.paged = _abi.make_paged(w.block_table, w.page_size) if w.kind in ("paged", "mla") else None
         self.sparse = _abi.make_sparse(w.num_blocks, w.block_idx, w.block_size) if w.num_blocks is not None else None
         self.splits, self.chunk = _abi.attn_decode_plan(self.sets[0][0], self.paged, self.sparse)
@@ -91,7 +95,7 @@ class Step:
             nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits)
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
             self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
-            kind = "partial_mfma_kernel" if "mfma" in KERNELS.get(w.config, ("", ""))[1] else "partial_valu_kernel"
+            kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
             if self.launches == 1:
                 self.kernel_name = f"{kind} (merge inside; the whole step)"
             else:  # the partial pass alone, into buffers of its own
@@ -107,7 +111,7 @@ class Step:
     def kernel(self, i):
         """The step's dominant kernel alone: the partial pass (with the merge inside it where
         attn_decode makes one launch)."""
-        a, k, x = self.sets[i % len(self.sets)]
+        a, k, x = self.sets[i % len(self.sets)][:3]
         if self.launches == 1:
             self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
         elif self.fused:
@@ -117,7 +121,7 @@ class Step:
 
     def partial(self, i):
         """The step's partial pass (the whole step where the merge is fused into it)."""
-        a, k, x = self.sets[i % len(self.sets)]
+        a, k, x = self.sets[i % len(self.sets)][:3]
         if self.fused:
             self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
         else:
@@ -138,6 +142,8 @@ def oracle_kwargs(w):
         kw.update(num_blocks=w.num_blocks, block_idx=w.block_idx, block_size=w.block_size)
     if w.kind == "mla":
         kw.update(q2=w.q_pe, k2=w.kpe)
+    if w.kv_format == "fp8":
+        kw.update(k_scale=w.k_scale, v_scale=w.v_scale)
     return kw
 
 

@@ -55,6 +55,10 @@ extern "C" {
 #define AD_F32 0
 #define AD_BF16 1
 
+/* Cache element formats (ad_decode_args.kv_format). */
+#define AD_KV_SAME 0     /* k and v hold `dtype` elements */
+#define AD_KV_FP8_E4M3 1 /* k and v hold OCP E4M3 bytes with fp32 row scales */
+
 #define AD_MAX_SPLITS 256
 
 /*
@@ -92,6 +96,20 @@ typedef struct ad_decode_args {
     void *out;
     int64_t out_stride[3];
     float *lse;
+    /* Quantised cache (TensorRT-LLM xqa mha.cu: an e4m3 cache with one kvCacheScale; mslk
+     * splitk_kernels.py, _process_fp8_quantization: fp8 rows with a scale per row). With
+     * AD_KV_FP8_E4M3, k and v hold OCP E4M3 bytes (their strides count bytes) and every element
+     * is dequantised as its decoded value times the fp32 scale of its row,
+     * k_scale[b * k_scale_stride[0] + j * k_scale_stride[1] + h * k_scale_stride[2]] (paged:
+     * page, slot, head), likewise for v. Zero strides broadcast; all zero is one scale per tensor,
+     * xqa's form. Supported on the vector path with bf16 q / out and head dim 128, any number of
+     * query rows per KV head (in blocks of at most 4); not with MLA. AD_KV_SAME (a zero-filled
+     * struct) ignores the rest. */
+    int32_t kv_format;
+    const float *k_scale;
+    int64_t k_scale_stride[3];
+    const float *v_scale;
+    int64_t v_scale_stride[3];
 } ad_decode_args;
 
 /* Paged cache: logical page p of sequence b is pool page block_table[b * bt_stride + p]
@@ -150,8 +168,8 @@ size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *pa
  *            key gets o_s = 0, lse_s = -inf (mslk splitk_kernels.py: zeros when l == 0).
  * args->out and args->lse are ignored. num_splits in [1, AD_MAX_SPLITS]; 0 = the planner's
  * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, any G * q_len (bf16 with
- * more than 8 rows per KV head runs on the matrix cores, 32 rows per work unit; otherwise the
- * vector ALUs take up to 8 rows per work unit).
+ * more than 8 rows per KV head, and every fp8 cache, runs on the matrix cores, 32 rows per work
+ * unit; otherwise the vector ALUs take up to 8 rows per work unit; attn_decode_kernel tells which).
  */
 int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                         int32_t num_splits, float *part_o, float *part_lse, void *stream);
@@ -175,8 +193,8 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
  * finish merges the unit's splits (same arithmetic, same order: the result is the two-launch
  * result bit for bit), elected by a counter per work unit that wraps back to zero on the last
  * arrival (the multi-block mode of TensorRT-LLM xqa mha.cu: a semaphore increment picks the last
- * CTA, which merges). One launch is used when the step is a single round of work groups on the
- * vector path (at most one group per compute unit, at most 8 query rows per unit), else the
+ * CTA, which merges). One launch is used when the step is a single round of work groups (at most
+ * one group per compute unit) whose units hold at most 8 query rows, else the
  * partial pass and the merge kernel run as two launches in the same workspace. Environment
  * AD_FUSED_MERGE=0 / 1 forces two launches / one launch (testing aid).
  * workspace: device memory of at least attn_decode_workspace_size(args, paged, num_splits)
@@ -197,6 +215,16 @@ int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_spar
  * its own). Checks the arguments as attn_decode does (out is not needed). */
 int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                          int32_t num_splits, int32_t *launches);
+
+/* Which partial-pass kernel the calls above run for these arguments (e.g. to name it in a
+ * profile): AD_KERNEL_VECTOR (vector ALUs, up to 8 query rows per work unit), AD_KERNEL_MATRIX
+ * (matrix cores, 32 rows per unit: bf16 with more than 8 rows per KV head, and every fp8 cache)
+ * or AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). Honours AD_PARTIAL_KERNEL as the calls
+ * do. Checks the arguments as the calls do (out is not needed). */
+#define AD_KERNEL_VECTOR 0
+#define AD_KERNEL_MATRIX 1
+#define AD_KERNEL_MLA 2
+int attn_decode_kernel(const ad_decode_args *args, int32_t *kind);
 
 /* attn_decode over a paged cache (paged must not be NULL); the same workspace contract. */
 int attn_decode_paged(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits,

@@ -25,6 +25,8 @@ def oracle_of(orc, w, rows=None, key_range=None):
     """Oracle result for a CPU workload (all rows, or the flat row indices given)."""
     kw = dict(scale=w.scale, seq_lens=w.seq_lens, causal=w.causal, window=w.window, rows=rows,
               key_range=key_range)
+    if w.kv_format == "fp8":
+        kw.update(k_scale=w.k_scale, v_scale=w.v_scale)
     if w.kind == "contiguous":
         if w.num_blocks is not None:
             kw.update(num_blocks=w.num_blocks, block_idx=w.block_idx, block_size=w.block_size)

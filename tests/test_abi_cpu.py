@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("attn_decode", "attn_decode_launches", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
+    for n in ("attn_decode", "attn_decode_launches", "attn_decode_kernel", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged", "attn_decode_mla",
               "attn_decode_workspace_size", "attn_decode_plan", "attn_decode_last_error"):
         assert n in names
 
@@ -44,10 +44,28 @@ def test_status_codes_match_header():
 
 
 def test_struct_layouts_match_header_sizes():
-    # ad_decode_args: 7 int32 + float (32 B), then pointer/stride groups, seq_lens, 3 int32, out, lse
-    assert ctypes.sizeof(_abi.DecodeArgs) == 32 + 3 * (8 + 24) + 8 + 4 + 4 + 4 + 4 + 8 + 24 + 8
-    assert ctypes.sizeof(_abi.Paged) == 24
-    assert ctypes.sizeof(_abi.Sparse) == 8 + 8 + 16 + 24 + 8
+    """The ctypes mirrors have the size and field offsets the C compiler gives the header's
+    structs (a C program built against include/attn_decode.h prints them)."""
+    import subprocess
+    import tempfile
+
+    structs = {"ad_decode_args": _abi.DecodeArgs, "ad_paged": _abi.Paged, "ad_sparse": _abi.Sparse}
+    lines = ['#include <stddef.h>', '#include <stdio.h>', '#include "attn_decode.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'    printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'    printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines += ["    return 0;", "}"]
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(src, "w").write("\n".join(lines) + "\n")
+        subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), src, "-o", exe], check=True)
+        out = subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {tuple(x.split()[:2]): int(x.split()[2]) for x in out if x}
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, f"{cname}.{fname}"
 
 
 # ------------------------------------------------------------------------------ rejection paths
@@ -302,3 +320,67 @@ def test_launch_count_query(monkeypatch):
     a.head_dim_qk = 96
     with pytest.raises(_abi.ADError):
         ad.attn_decode_launches(a, None, None, 2)
+
+
+def test_fp8_cache_rejections():
+    """An E4M3 cache: bf16 queries, head dim 128, both scale arrays, 4-byte aligned, not with MLA,
+    and a known kv_format."""
+    q, _, _, out = _tensors()
+    kb = torch.zeros(2, 2, 64, 128, dtype=torch.uint8).permute(0, 2, 1, 3)
+    ks = torch.ones(2, 2, 64, dtype=torch.float32).permute(0, 2, 1)
+    a = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    assert a.kv_format == _abi.AD_KV_FP8_E4M3
+    ws = torch.zeros((1 << 21) + 256, dtype=torch.uint8)
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+
+    def call(args):
+        return _abi.lib().attn_decode(ctypes.byref(args), None, None, 2, base, 1 << 21, None)
+
+    b = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    b.v_scale = None
+    assert call(b) == -1
+    b = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    b.k_scale = b.k_scale + 2
+    assert call(b) == -4
+    b = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    b.kv_format = 7
+    assert call(b) == -2
+    b = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    b.head_dim_qk = b.head_dim_v = 64
+    assert call(b) == -5
+    q32, _, _, out32 = _tensors(dtype=torch.float32)
+    b = _abi.make_args(q32, kb, kb, scale=0.1, out=out32, k_scale=ks, v_scale=ks)
+    assert call(b) == -5
+    b = _abi.make_args(q, kb, kb, scale=0.1, out=out, k_scale=ks, v_scale=ks)
+    b.k_stride[1] = 136  # a byte row pitch that breaks 16-byte alignment
+    assert call(b) == -4
+
+
+def test_kernel_query(monkeypatch):
+    """attn_decode_kernel names the partial-pass kernel: vector ALUs for up to 8 rows per KV head
+    and for fp32, matrix cores for more bf16 rows and for every fp8 cache, the MLA kernel for the
+    576 / 512 head dims; AD_PARTIAL_KERNEL overrides the bf16 choice."""
+    monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+    a, keep = _args()  # 8 / 2 heads: 4 rows per KV head
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    q, k, v, out = _tensors(Hq=64, Hkv=2)
+    assert ad.attn_decode_kernel(_abi.make_args(q, k, v, scale=0.1, out=out)) == ad.AD_KERNEL_MATRIX
+    q32, k32, v32, o32 = _tensors(dtype=torch.float32, Hq=64, Hkv=2)
+    assert ad.attn_decode_kernel(_abi.make_args(q32, k32, v32, scale=0.1, out=o32)) == ad.AD_KERNEL_VECTOR
+    kb = torch.zeros(2, 2, 64, 128, dtype=torch.uint8).permute(0, 2, 1, 3)
+    ks = torch.ones(2, 2, 64, dtype=torch.float32).permute(0, 2, 1)
+    f = _abi.make_args(keep[0], kb, kb, scale=0.1, out=keep[3], k_scale=ks, v_scale=ks)
+    assert ad.attn_decode_kernel(f) == ad.AD_KERNEL_MATRIX
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
+    assert ad.attn_decode_kernel(f) == ad.AD_KERNEL_VECTOR
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX
+    qm = torch.zeros(2, 1, 16, 512, dtype=torch.bfloat16)
+    ckv = torch.zeros(4, 64, 1, 512, dtype=torch.bfloat16)
+    m = _abi.make_args(qm, ckv, None, head_dim_qk=576, scale=0.1)
+    assert ad.attn_decode_kernel(m) == ad.AD_KERNEL_MLA
+    assert ad.KERNEL_NAMES[ad.AD_KERNEL_MLA] == "mla_partial_kernel"
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(a), None) == -1
+    a.head_dim_qk = 96
+    with pytest.raises(_abi.ADError):
+        ad.attn_decode_kernel(a)

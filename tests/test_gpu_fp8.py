@@ -1,0 +1,107 @@
+"""GPU parity of the E4M3 (fp8) cache path against the fp64 oracle on the same seeded inputs,
+through the C ABI: contiguous, paged and block-sparse caches, row and tensor scales, ragged and
+empty sequences, masks, grouped and speculative query rows, split counts, and NaN codes in every
+cache slot that must not be read."""
+import pytest
+import torch
+
+from attention_decode_amd import inputs
+from attention_decode_amd.step import DecodeStep
+from gpu_util import assert_matches, gpu_available, oracle_of, say
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+KERNELS = ["mfma", "valu"]  # the matrix-core default, and the vector form (AD_PARTIAL_KERNEL=valu)
+
+
+def force(monkeypatch, kernel):
+    if kernel == "valu":
+        monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
+    else:
+        monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+
+
+def run(w, num_splits=None, fused=True):
+    step = DecodeStep(w.to("cuda"), num_splits=num_splits, fused=fused)
+    out, lse = step()
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), step
+
+
+def test_workload6_full(orc):
+    say("[gpu] workload 6 (fp8 paged ragged): full size, every row")
+    w = inputs.make(6)
+    out, lse, step = run(w)
+    say(f"  splits {step.splits}")
+    ref_o, ref_l = oracle_of(orc, w)
+    assert_matches(out, lse, ref_o, ref_l, torch.bfloat16, "workload 6")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_workload6_poisoned_bit_identical(monkeypatch, kernel):
+    """NaN codes and NaN scales in unreferenced pages and tail slots change nothing, bit for bit."""
+    force(monkeypatch, kernel)
+    say(f"[gpu] workload 6 poisoned pool, {kernel}")
+    a, la, _ = run(inputs.make(6))
+    b, lb, _ = run(inputs.make(6, poison=True))
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(la, lb)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("scales", ["token", "tensor"])
+@pytest.mark.parametrize("G,Q", [(1, 1), (2, 1), (4, 1), (8, 1), (4, 2), (1, 3), (16, 1), (8, 5)])
+@pytest.mark.parametrize("mask", ["none", "causal_window"])
+def test_contiguous_small(orc, monkeypatch, kernel, scales, G, Q, mask):
+    force(monkeypatch, kernel)
+    causal = mask.startswith("causal")
+    window = 37 if "window" in mask else 0
+    lens = [300, 1, 37, 0, 129]
+    say(f"[gpu] fp8 contiguous {kernel} G={G} Q={Q} {mask} scales={scales}")
+    w = inputs.contiguous(batch=len(lens), num_q_heads=G * 2, num_kv_heads=2, head_dim=128, kv_len=300, q_len=Q,
+                          seed=800 + G * 10 + Q, seq_lens=lens, causal=causal, window=window, kv_format="fp8",
+                          kv_scales=scales)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 3, 7):
+        out, lse, _ = run(w, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, torch.bfloat16, f"S={S}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("page_size", [16, 32, 64])
+def test_paged_small(orc, monkeypatch, kernel, page_size):
+    force(monkeypatch, kernel)
+    lens = [1, 15, 16, 17, 300, 0, 77]
+    say(f"[gpu] fp8 paged {kernel} page={page_size}")
+    w = inputs.paged(seq_lens=lens, num_q_heads=8, num_kv_heads=2, head_dim=128, page_size=page_size,
+                     seed=900 + page_size, kv_format="fp8", poison=True)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 2, 5):
+        out, lse, _ = run(w, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, torch.bfloat16, f"page {page_size} S={S}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_block_sparse(orc, monkeypatch, kernel):
+    force(monkeypatch, kernel)
+    say(f"[gpu] fp8 block-sparse {kernel}, causal, poisoned unlisted blocks")
+    w = inputs.sparse(batch=3, num_q_heads=16, num_kv_heads=2, head_dim=128, kv_len=2048, q_len=2,
+                      block_size=128, blocks=[[[0, 3, 5], []], [[1], [2, 4, 6, 8]], [[7, 9], [15]]],
+                      seed=5, causal=True, window=0, kv_format="fp8", poison=True)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 2, 5):
+        out, lse, _ = run(w, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, torch.bfloat16, f"S={S}")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_one_launch_equals_two_launches(monkeypatch, kernel):
+    """The in-pass merge and the merge kernel give the same bits on an fp8 cache."""
+    force(monkeypatch, kernel)
+    w = inputs.contiguous(batch=5, num_q_heads=8, num_kv_heads=2, head_dim=128, kv_len=300, q_len=1, seed=4,
+                          seq_lens=[300, 1, 37, 0, 129], kv_format="fp8")
+    for S in (1, 3):
+        monkeypatch.setenv("AD_FUSED_MERGE", "1")
+        o1, l1, _ = run(w, num_splits=S)
+        o2, l2, _ = run(w, num_splits=S, fused=False)
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2), f"S={S}"
