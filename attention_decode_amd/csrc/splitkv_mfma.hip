@@ -420,8 +420,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     };
 
     constexpr int kStride = kWaves * kTile;
-    auto iterate = [&](Buf &cur, Buf &nxt) -> bool {
-        if (cur.base >= t1) return false;
+    auto iterate = [&](Buf &cur, Buf &nxt) {
         fetch(nxt, cur.base + kStride);
         __builtin_amdgcn_sched_barrier(0);
         bool full = cur.base + kTile <= t1;
@@ -430,13 +429,22 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
             full = pl - pf == kTile - 1 && pl < L && pf >= lo_max && pl < hi_min;
         }
         compute(cur, full);
-        return true;
     };
 
+    // This wave's tiles start at first + i * kStride < t1. The loop runs pairs of tiles with its
+    // only exit test at the back edge, so the loads in flight are the same on every path into the
+    // loop and the compiler waits for no more of them than a tile needs (an exit test between the
+    // two halves made it wait for every load at the loop head); an odd last tile follows the loop.
+    const int first = t0 + wave * kTile;
+    const int ntiles = first < t1 ? (t1 - first + kStride - 1) / kStride : 0;
     Buf A, B;
-    fetch(A, t0 + wave * kTile);
-    while (iterate(A, B) && iterate(B, A)) {
+    fetch(A, first);
+    int i = 0;
+    for (; i + 2 <= ntiles; i += 2) {
+        iterate(A, B);
+        iterate(B, A);
     }
+    if (i < ntiles) iterate(A, B);
 
     // ---- combine the waves: o_s = acc / l, lse_s = (m + log2 lf) * ln 2
     l = pair_sum(l);
