@@ -13,6 +13,10 @@ Any tensor may be a permuted view (for example a head-major cache viewed token-m
 A quantised cache passes k and v as uint8 OCP E4M3 bytes with k_scale / v_scale: fp32
 [batch, kv_len, num_kv_heads] (paged: [num_pages, page_size, num_kv_heads]) views of the row
 scales, any strides (zero strides broadcast one scale).
+Variable query lengths: with q_starts ([batch + 1] packed token offsets) q (and q2) are packed
+[tokens, num_q_heads, dim], q_len (the largest per-sequence count, the tree-mask row pitch) is
+passed explicitly, and out / lse come back packed as [tokens, num_q_heads, ...]. A tree mask is
+int32/uint32 [token rows, ceil(q_len / 32)] (bit i of a row: draft key i visible).
 """
 from __future__ import annotations
 
@@ -51,6 +55,7 @@ class Problem(ctypes.Structure):
         ("key_lo", ctypes.c_int32), ("key_hi", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p), ("ks_stride", ctypes.c_int64 * 3),
         ("v_scale", ctypes.c_void_p), ("vs_stride", ctypes.c_int64 * 3),
+        ("q_starts", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
     ]
 
 
@@ -105,15 +110,29 @@ class Oracle:
     def attend(self, q, k, v, *, scale: float, seq_lens=None, kv_len: int | None = None,
                q2=None, k2=None, block_table=None, page_size: int = 0,
                num_blocks=None, block_idx=None, block_size: int = 0,
-               causal: bool = False, window: int = 0, key_range=None, rows=None, k_scale=None, v_scale=None):
+               causal: bool = False, window: int = 0, key_range=None, rows=None, k_scale=None, v_scale=None,
+               q_starts=None, q_len: int | None = None, tree_mask=None):
         """Returns (out, lse) as float64 numpy arrays.
 
-        out is [batch, q_len, num_q_heads, dim_v] (or [len(rows), dim_v] when rows is given) and
-        lse has the same leading shape. Rows are flat indices (b*q_len + t)*num_q_heads + hq.
+        out is [batch, q_len, num_q_heads, dim_v] (packed [tokens, num_q_heads, dim_v] with
+        q_starts; [len(rows), dim_v] when rows is given) and lse has the same leading shape. Rows
+        are flat indices n*num_q_heads + hq of token row n = b*q_len + t (q_starts[b] + t).
         """
         q, k, v, q2, k2 = (self._cpu(x) for x in (q, k, v, q2, k2))
         keep = [q, k, v, q2, k2]
-        B, Q, Hq, Dqk = q.shape
+        qs = None
+        if q_starts is not None:  # packed queries: view them as [1, tokens, Hq, D] for the strides
+            qs = self._cpu(q_starts).to(torch.int32).contiguous()
+            keep.append(qs)
+            if q.dim() != 3 or q_len is None:
+                raise ValueError("with q_starts, q is packed [tokens, heads, dim] and q_len is given")
+            q = q.unsqueeze(0)
+            q2 = None if q2 is None else q2.unsqueeze(0)
+            keep += [q, q2]
+        _, Q, Hq, Dqk = q.shape
+        B = q.shape[0]
+        if qs is not None:
+            B, Q = qs.numel() - 1, int(q_len)
         Hkv = k.shape[2]
         if q.dtype not in _TYPE or k.dtype not in _TYPE or v.dtype != k.dtype or q.dtype == torch.uint8:
             raise ValueError("unsupported element types")
@@ -162,14 +181,23 @@ class Oracle:
             P.k_scale, P.ks_stride = ks.data_ptr(), (ctypes.c_int64 * 3)(*ks.stride())
             P.v_scale, P.vs_stride = vs.data_ptr(), (ctypes.c_int64 * 3)(*vs.stride())
         P.causal, P.window = int(bool(causal)), int(window)
+        if qs is not None:
+            P.q_starts = qs.data_ptr()
+        if tree_mask is not None:
+            tm = self._cpu(tree_mask).to(torch.int32).contiguous()
+            if tm.dim() != 2 or tm.shape[1] != (Q + 31) // 32:
+                raise ValueError("tree_mask must be [token rows, ceil(q_len / 32)]")
+            keep.append(tm)
+            P.tree_mask = tm.data_ptr()
         if key_range is None:
             P.key_lo, P.key_hi = 0, -1
         else:
             P.key_lo, P.key_hi = int(key_range[0]), int(key_range[1])
 
         Dv = v.shape[3]
+        tokens = int(qs[-1]) if qs is not None else B * Q
         if rows is None:
-            n = B * Q * Hq
+            n = tokens * Hq
             rows_arr = None
         else:
             rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
@@ -183,6 +211,8 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_attend rejected the problem (rc={rc})")
         if rows is None:
+            if qs is not None:
+                return out.reshape(tokens, Hq, Dv), lse.reshape(tokens, Hq)
             return out.reshape(B, Q, Hq, Dv), lse.reshape(B, Q, Hq)
         return out, lse
 

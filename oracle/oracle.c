@@ -26,7 +26,17 @@
  *                                                              mslk splitk_kernels.py at the end
  *                                                              of _fwd_kernel_splitK)
  *
- * over the visible keys j, with m their largest score. A row with no visible key gets out = 0 and
+ * over the visible keys j, with m their largest score.
+ *
+ * Variable query lengths (TensorRT-LLM xqa mha.cu, qCuSeqLens; mslk splitk_kernels.py,
+ * Seq_starts_q): with q_starts, sequence b has Q_b = q_starts[b+1] - q_starts[b] query tokens
+ * (at most q_len) and its token t is packed row n = q_starts[b] + t of q, out and lse; it sits at
+ * position L - Q_b + t. Without it every sequence has q_len tokens and n = b*q_len + t.
+ *
+ * Tree mask (TensorRT-LLM xqa mha.cu, the SPEC_DEC input mask): the last Q_b keys of sequence b
+ * are its draft tokens, draft key i at position L - Q_b + i. Token row n sees draft key i only if
+ * bit i % 32 of word tree_mask[n * ceil(q_len / 32) + i / 32] is set; the keys before the drafts
+ * are not affected. It combines with the other conditions below (all must hold). A row with no visible key gets out = 0 and
  * lse = -inf (mslk splitk_kernels.py, the l == 0 guard of the split epilogue and the lse_max ==
  * -inf guard of _splitK_reduce).
  *
@@ -39,7 +49,8 @@
  *                                position: TensorRT-LLM xqa mha.cu skips the first len - W cache
  *                                tokens; equal to mslk's WINDOW_LEFT = window - 1);
  *   no block list, or j / block_size is one of the listed blocks of (b, hkv)   (PyTorch Inductor
- *                                flex_decode.py.jinja, KV_NUM_BLKS / KV_IDX).
+ *                                flex_decode.py.jinja, KV_NUM_BLKS / KV_IDX);
+ *   no tree mask, or j < L - Q_b, or the tree-mask bit of (n, j - (L - Q_b)) is set.
  *
  * K and V rows are found through the same address map the cache uses:
  *   contiguous: base + b*st[0] + j*st[1] + hkv*st[2]
@@ -96,6 +107,10 @@ typedef struct {
     /* kv_type ORC_E4M3: fp32 scale of every K / V row, indexed like the rows */
     const float *k_scale; int64_t ks_stride[3];
     const float *v_scale; int64_t vs_stride[3];
+    /* variable query lengths: [batch + 1] packed token offsets (q and q2 rows n use
+     * n * q_stride[1] + hq * q_stride[2]); NULL: q_len tokens per sequence */
+    const int32_t *q_starts;
+    const uint32_t *tree_mask; /* [token rows][ceil(q_len / 32)] words; NULL: none */
 } oracle_problem;
 
 /* Value of one OCP E4M3 byte, from the format's definition. */
@@ -145,26 +160,51 @@ static int block_listed(const oracle_problem *P, int64_t b, int64_t hkv, int64_t
     return 0;
 }
 
+/* Query tokens of sequence b, and the packed row of its token t. */
+static int64_t q_tokens(const oracle_problem *P, int64_t b)
+{
+    return P->q_starts ? (int64_t)P->q_starts[b + 1] - P->q_starts[b] : P->q_len;
+}
+static int64_t q_row(const oracle_problem *P, int64_t b, int64_t t)
+{
+    return P->q_starts ? (int64_t)P->q_starts[b] + t : b * P->q_len + t;
+}
+static int64_t q_offset(const oracle_problem *P, const int64_t st[3], int64_t b, int64_t t, int64_t hq)
+{
+    if (P->q_starts) return q_row(P, b, t) * st[1] + hq * st[2];
+    return b * st[0] + t * st[1] + hq * st[2];
+}
+
+static int tree_allows(const oracle_problem *P, int64_t b, int64_t t, int64_t L, int64_t j)
+{
+    if (!P->tree_mask) return 1;
+    const int64_t first_draft = L - q_tokens(P, b);
+    if (j < first_draft) return 1;
+    const int64_t i = j - first_draft, words = (P->q_len + 31) / 32;
+    return (int)((P->tree_mask[q_row(P, b, t) * words + i / 32] >> (i % 32)) & 1u);
+}
+
 static int key_visible(const oracle_problem *P, int64_t b, int64_t t, int64_t hkv, int64_t L, int64_t j)
 {
-    int64_t pos = L - P->q_len + t;
+    int64_t pos = L - q_tokens(P, b) + t;
     if (j < 0 || j >= L) return 0;
     if (P->key_hi >= 0 && (j < P->key_lo || j >= P->key_hi)) return 0;
     if (P->causal && j > pos) return 0;
     if (P->window > 0 && pos - j >= P->window) return 0;
+    if (!tree_allows(P, b, t, L, j)) return 0;
     return block_listed(P, b, hkv, j);
 }
 
 static double score(const oracle_problem *P, int64_t b, int64_t t, int64_t hq, int64_t hkv, int64_t j)
 {
     double acc = 0.0;
-    int64_t qo = b * P->q_stride[0] + t * P->q_stride[1] + hq * P->q_stride[2];
+    int64_t qo = q_offset(P, P->q_stride, b, t, hq);
     int64_t ko = kv_row(P, P->k_stride, b, hkv, j);
     const double ks = P->kv_type == ORC_E4M3 ? (double)P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)] : 1.0;
     for (int64_t d = 0; d < P->dim_qk; d++)
         acc += widen(P->q, P->q_type, qo + d) * (widen(P->k, P->kv_type, ko + d) * ks);
     if (P->dim_qk2 > 0) {
-        int64_t qo2 = b * P->q2_stride[0] + t * P->q2_stride[1] + hq * P->q2_stride[2];
+        int64_t qo2 = q_offset(P, P->q2_stride, b, t, hq);
         int64_t ko2 = kv_row(P, P->k2_stride, b, hkv, j);
         for (int64_t d = 0; d < P->dim_qk2; d++)
             acc += widen(P->q2, P->q_type, qo2 + d) * widen(P->k2, P->kv_type, ko2 + d);
@@ -184,6 +224,11 @@ static int check_problem(const oracle_problem *P)
     if (P->window < 0) return -1;
     if (P->q_type == ORC_E4M3) return -1;
     if (P->kv_type == ORC_E4M3 && (!P->k_scale || !P->v_scale || P->dim_qk2 > 0)) return -1;
+    if (P->q_starts) {
+        if (P->q_starts[0] < 0) return -1;
+        for (int64_t b = 0; b < P->batch; b++)
+            if (q_tokens(P, b) < 0 || q_tokens(P, b) > P->q_len) return -1;
+    }
     return 0;
 }
 
@@ -201,15 +246,18 @@ int oracle_get_threads(void)
 }
 
 /*
- * Attention for the listed rows (row = (b*q_len + t)*num_q_heads + hq), or for every row in that
- * order when rows == NULL. out is [nrows][dim_v], lse is [nrows]. Returns 0, or -1 on a
+ * Attention for the listed rows (row = n*num_q_heads + hq for packed token row n, i.e.
+ * (b*q_len + t)*num_q_heads + hq without q_starts), or for every row in that order when
+ * rows == NULL. out is [nrows][dim_v], lse is [nrows]. With q_starts, a token row below
+ * q_starts[0] belongs to no sequence and gets out = 0, lse = -inf. Returns 0, or -1 on a
  * malformed problem.
  */
 int oracle_attend(const oracle_problem *P, const int64_t *rows, int64_t nrows, double *out, double *lse)
 {
     if (check_problem(P) || !out || !lse) return -1;
     const int64_t G = P->num_q_heads / P->num_kv_heads;
-    const int64_t total = (int64_t)P->batch * P->q_len * P->num_q_heads;
+    const int64_t tokens = P->q_starts ? (int64_t)P->q_starts[P->batch] : (int64_t)P->batch * P->q_len;
+    const int64_t total = tokens * P->num_q_heads;
     if (!rows) nrows = total;
     for (int64_t i = 0; rows && i < nrows; i++)
         if (rows[i] < 0 || rows[i] >= total) return -1;
@@ -218,12 +266,22 @@ int oracle_attend(const oracle_problem *P, const int64_t *rows, int64_t nrows, d
 #pragma omp parallel for schedule(dynamic, 1) num_threads(oracle_get_threads())
     for (int64_t i = 0; i < nrows; i++) {
         const int64_t r = rows ? rows[i] : i;
-        const int64_t hq = r % P->num_q_heads;
-        const int64_t t = (r / P->num_q_heads) % P->q_len;
-        const int64_t b = r / ((int64_t)P->num_q_heads * P->q_len);
+        const int64_t hq = r % P->num_q_heads, n = r / P->num_q_heads;
+        int64_t b = n / P->q_len, t = n % P->q_len;
+        double *o = out + i * P->dim_v;
+        if (P->q_starts) {  /* the sequence whose packed rows hold n */
+            b = -1;
+            for (int64_t c = 0; c < P->batch; c++)
+                if (P->q_starts[c] <= n && n < P->q_starts[c + 1]) b = c;
+            if (b < 0) {
+                for (int64_t d = 0; d < P->dim_v; d++) o[d] = 0.0;
+                lse[i] = -INFINITY;
+                continue;
+            }
+            t = n - P->q_starts[b];
+        }
         const int64_t hkv = hq / G;
         const int64_t L = P->seq_lens ? P->seq_lens[b] : P->kv_len;
-        double *o = out + i * P->dim_v;
 
         double *s = (double *)malloc((size_t)(L > 0 ? L : 1) * sizeof(double));
         char *vis = (char *)malloc((size_t)(L > 0 ? L : 1));

@@ -478,12 +478,134 @@ def pin_fp8_paged_and_broadcast(orc):
     assert np.array_equal(c[0], d[0]) and np.array_equal(c[1], d[1]), "broadcast scale != full array"
 
 
+# ------------------------------------------------------------------ speculative decoding
+def _random_tree(g, n):
+    """Parent of draft token i (i >= 1) uniform in [0, i); token 0 is the root."""
+    return [-1] + [int(torch.randint(0, i, (1,), generator=g)) for i in range(1, n)]
+
+
+def _tree_dense(parents):
+    """[n, n] bool: token t sees draft key i iff i is t or one of its ancestors (walks the parent
+    pointers; no bit packing involved)."""
+    n = len(parents)
+    m = torch.zeros(n, n, dtype=torch.bool)
+    for t in range(n):
+        i = t
+        while i >= 0:
+            m[t, i] = True
+            i = parents[i]
+    return m
+
+
+def _pack_rows(dense, words):
+    """bool [rows, <= 32*words] -> int32 [rows, words], bit i of the row at word i // 32, bit i % 32
+    (numpy's little-endian bit packing, read back as little-endian 32-bit words)."""
+    rows = dense.shape[0]
+    full = np.zeros((rows, 32 * words), dtype=np.uint8)
+    full[:, :dense.shape[1]] = dense.numpy()
+    by = np.packbits(full, axis=1, bitorder="little")
+    return torch.from_numpy(by.view("<u4").astype(np.int64).astype(np.int32).reshape(rows, words))
+
+
+def _spec_problem(g, Qs, lens, Qmax, Hq=4, Hkv=2, D=6):
+    B = len(Qs)
+    L = max(lens)
+    starts = torch.tensor([0] + list(np.cumsum(Qs)), dtype=torch.int32)
+    T = int(starts[-1])
+    q = _randn(g, T, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    return q, k, v, starts, torch.tensor(lens, dtype=torch.int32)
+
+
+def pin_tree_mask_library(orc):
+    """Packed tree masks over ragged draft counts (some above 32, so rows span two words) equal
+    SDPA per sequence with a dense mask from the trees' ancestor sets, alone and with causal +
+    window."""
+    g = _gen(31)
+    Qmax = 40
+    Qs, lens = [5, 40, 0, 1, 33], [23, 61, 9, 4, 40]
+    q, k, v, starts, sl = _spec_problem(g, Qs, lens, Qmax)
+    W = (Qmax + 31) // 32
+    dense_rows, trees = [], []
+    for b, n in enumerate(Qs):
+        tr = _tree_dense(_random_tree(g, n)) if n else torch.zeros(0, 0, dtype=torch.bool)
+        trees.append(tr)
+        dense_rows.append(tr)
+    tm = _pack_rows(torch.cat([torch.nn.functional.pad(t, (0, Qmax - t.shape[1])) for t in dense_rows]), W)
+    # and an arbitrary bit pattern (rows need not contain the first draft, or themselves)
+    bits = [torch.rand(n, n, generator=g) < 0.5 for n in Qs]
+    tb = _pack_rows(torch.cat([torch.nn.functional.pad(t, (0, Qmax - t.shape[1])) for t in bits]), W)
+    for causal, window, mask, dense in ((False, 0, tm, trees), (True, 17, tm, trees), (False, 0, tb, bits)):
+        out, lse = orc.attend(q, k, v, scale=0.45, seq_lens=sl, q_starts=starts, q_len=Qmax, tree_mask=mask,
+                              causal=causal, window=window)
+        for b, n in enumerate(Qs):
+            if n == 0:
+                continue
+            Lb, s0 = lens[b], int(starts[b])
+            m = _library_mask(1, n, Lb, [Lb], causal, window)[0]
+            m[:, Lb - n:] &= dense[b]
+            ro, rl = _sdpa(q[None, s0:s0 + n], k[b:b + 1, :Lb], v[b:b + 1, :Lb], 0.45, m[None])
+            _close(out[s0:s0 + n], ro[0], what=f"out b={b} causal={causal}")
+            _close(lse[s0:s0 + n], rl[0], what=f"lse b={b} causal={causal}")
+
+
+def pin_tree_chain_is_causal(orc):
+    """A chain-shaped tree (token t sees drafts 0..t) is the bottom-right causal mask, and a mask
+    with every bit set changes nothing."""
+    g = _gen(32)
+    B, Q, Hq, Hkv, D, L = 3, 6, 4, 2, 5, 17
+    q = _randn(g, B, Q, Hq, D)
+    k = _randn(g, B, L, Hkv, D)
+    v = _randn(g, B, L, Hkv, D)
+    lens = torch.tensor([17, 6, 11], dtype=torch.int32)
+    chain = torch.ones(Q, Q, dtype=torch.bool).tril()
+    tm = _pack_rows(chain.repeat(B, 1), 1)
+    a = orc.attend(q, k, v, scale=0.6, seq_lens=lens, tree_mask=tm)
+    c = orc.attend(q, k, v, scale=0.6, seq_lens=lens, causal=True)
+    _close(a[0], c[0], what="chain out")
+    _close(a[1], c[1], what="chain lse")
+    every = torch.full((B * Q, 1), -1, dtype=torch.int32)
+    a = orc.attend(q, k, v, scale=0.6, seq_lens=lens, tree_mask=every, window=4)
+    c = orc.attend(q, k, v, scale=0.6, seq_lens=lens, window=4)
+    _close(a[0], c[0], what="all-ones out")
+    _close(a[1], c[1], what="all-ones lse")
+
+
+def pin_varlen_equals_separate(orc):
+    """Packed queries with per-sequence token counts (including 0) equal each sequence computed
+    alone with its own q_len, causal and windowed."""
+    g = _gen(33)
+    Qs, lens = [3, 0, 1, 4], [12, 5, 9, 4]
+    q, k, v, starts, sl = _spec_problem(g, Qs, lens, 4)
+    for causal, window in ((True, 0), (True, 3), (False, 0)):
+        out, lse = orc.attend(q, k, v, scale=0.8, seq_lens=sl, q_starts=starts, q_len=4,
+                              causal=causal, window=window)
+        assert out.shape == (sum(Qs), 4, 6)
+        for b, n in enumerate(Qs):
+            if n == 0:
+                continue
+            s0 = int(starts[b])
+            ro, rl = orc.attend(q[None, s0:s0 + n], k[b:b + 1], v[b:b + 1], scale=0.8,
+                                seq_lens=sl[b:b + 1], causal=causal, window=window)
+            _close(out[s0:s0 + n], ro[0], what=f"out b={b}")
+            _close(lse[s0:s0 + n], rl[0], what=f"lse b={b}")
+    # a packed row below q_starts[0] belongs to no sequence
+    shifted = starts + 2
+    qq = torch.cat([_randn(g, 2, 4, 6), q])
+    out, lse = orc.attend(qq, k, v, scale=0.8, seq_lens=sl, q_starts=shifted, q_len=4)
+    assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:2]))
+    ref = orc.attend(q, k, v, scale=0.8, seq_lens=sl, q_starts=starts, q_len=4)
+    _close(out[2:], ref[0], what="offset start out")
+
+
 ALL_PINS = [
     pin_library_attention, pin_library_causal_window, pin_library_block_list, pin_golden_visibility,
     pin_one_visible_key, pin_identical_keys, pin_constant_values, pin_large_logits, pin_empty_rows,
     pin_paged_equals_contiguous, pin_layout_and_rows, pin_widening, pin_mla_two_part_score,
     pin_merge_closed_form, pin_merge_identities, pin_split_then_merge, pin_key_order_invariance,
     pin_e4m3_decode_library, pin_e4m3_closed_forms, pin_fp8_equals_dequantised, pin_fp8_paged_and_broadcast,
+    pin_tree_mask_library, pin_tree_chain_is_causal, pin_varlen_equals_separate,
 ]
 
 

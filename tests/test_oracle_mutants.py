@@ -23,7 +23,16 @@ MUTANTS = [
     ("gqa head map", "const int64_t hkv = hq / G;", "const int64_t hkv = hq % P->num_kv_heads;"),
     ("causal off by one", "if (P->causal && j > pos) return 0;", "if (P->causal && j >= pos) return 0;"),
     ("window off by one", "pos - j >= P->window", "pos - j > P->window"),
-    ("query position", "int64_t pos = L - P->q_len + t;", "int64_t pos = L - 1 - t;"),
+    ("query position", "int64_t pos = L - q_tokens(P, b) + t;", "int64_t pos = L - 1 - t;"),
+    ("varlen query position", "int64_t pos = L - q_tokens(P, b) + t;", "int64_t pos = L - P->q_len + t;"),
+    ("varlen query rows", "if (P->q_starts) return q_row(P, b, t) * st[1] + hq * st[2];",
+     "if (P->q_starts) return (b * P->q_len + t) * st[1] + hq * st[2];"),
+    ("varlen sequence lookup", "if (P->q_starts[c] <= n && n < P->q_starts[c + 1]) b = c;",
+     "if (P->q_starts[c] < n && n <= P->q_starts[c + 1]) b = c;"),
+    ("tree bit order", ">> (i % 32)) & 1u);", ">> (31 - i % 32)) & 1u);"),
+    ("tree first draft", "const int64_t first_draft = L - q_tokens(P, b);", "const int64_t first_draft = L - P->q_len;"),
+    ("tree row pitch", "q_row(P, b, t) * words + i / 32", "q_row(P, b, t) + i / 32"),
+    ("tree prefix bound", "if (j < first_draft) return 1;", "if (j <= first_draft) return 1;"),
     ("second score part dropped",
      "acc += widen(P->q2, P->q_type, qo2 + d) * widen(P->k2, P->kv_type, ko2 + d);", "acc += 0.0;"),
     ("scale dropped", "return P->scale * acc;", "return acc;"),
@@ -41,12 +50,12 @@ MUTANTS = [
     ("merge weight sign", "double w = exp(ls[s] - M);", "double w = exp(M - ls[s]);"),
     ("merge lse without max", "lse[r] = M + log(W);", "lse[r] = log(W);"),
     ("merge empty guard", "if (M == -INFINITY) {", "if (0) {"),
-    ("empty row lse", "lse[i] = -INFINITY;", "lse[i] = 0.0;"),
+    ("empty row lse", "lse[i] = -INFINITY;\n            free(s);", "lse[i] = 0.0;\n            free(s);"),
     ("key range end", "j >= P->key_hi", "j > P->key_hi"),
     ("sequence length of row", "P->seq_lens[b] : P->kv_len", "P->seq_lens[0] : P->kv_len"),
-    ("query token of row", "const int64_t t = (r / P->num_q_heads) % P->q_len;",
-     "const int64_t t = r % P->q_len;"),
-    ("q token stride", "t * P->q_stride[1]", "t * P->q_stride[2]"),
+    ("query token of row", "int64_t b = n / P->q_len, t = n % P->q_len;",
+     "int64_t b = n / P->q_len, t = r % P->q_len;"),
+    ("q token stride", "return b * st[0] + t * st[1] + hq * st[2];", "return b * st[0] + t * st[2] + hq * st[2];"),
     ("running max", "if (s[j] > m) m = s[j];", "if (s[j] < m) m = s[j];"),
     ("merge normalisation", "for (int32_t d = 0; d < dim_v; d++) o[d] /= W;", ""),
     ("e4m3 exponent bias", "mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
