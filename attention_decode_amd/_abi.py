@@ -42,6 +42,7 @@ class DecodeArgs(ctypes.Structure):
         ("kv_format", ctypes.c_int32),
         ("k_scale", ctypes.c_void_p), ("k_scale_stride", I64x3),
         ("v_scale", ctypes.c_void_p), ("v_scale_stride", I64x3),
+        ("q_starts", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
     ]
 
 
@@ -127,14 +128,25 @@ def _stream(stream):
 
 
 def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, window=0, out=None, lse=None,
-              head_dim_qk=None, k_scale=None, v_scale=None):
+              head_dim_qk=None, k_scale=None, v_scale=None, q_starts=None, q_len=None, tree_mask=None):
     """Fill an ad_decode_args from tensors (q [B,Q,Hq,D]; k/v token-major 4-D views). uint8 k / v
-    are an E4M3 cache, with k_scale / v_scale fp32 3-D views indexed like the cache rows."""
+    are an E4M3 cache, with k_scale / v_scale fp32 3-D views indexed like the cache rows.
+    Variable query lengths: q_starts int32 [B + 1] with q (and out) packed [tokens, Hq, D] and
+    q_len the largest per-sequence count. tree_mask: int32 [token rows, ceil(q_len / 32)]."""
     a = DecodeArgs()
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
     a.dtype = _DTYPE[q.dtype]
+    if q_starts is not None:  # packed rows: view as [1, tokens, Hq, D]; q_stride[0] is unused
+        if q.dim() != 3 or q_len is None:
+            raise ValueError("with q_starts, q is packed [tokens, heads, dim] and q_len is given")
+        q = q.unsqueeze(0)
+        out = None if out is None else out.unsqueeze(0)
+        a.q_starts = _ptr(q_starts)
+    a.tree_mask = _ptr(tree_mask)
     a.batch, a.q_len, a.num_q_heads = q.shape[0], q.shape[1], q.shape[2]
+    if q_starts is not None:
+        a.batch, a.q_len = q_starts.numel() - 1, int(q_len)
     a.num_kv_heads = k.shape[2]
     a.head_dim_qk = q.shape[3] if head_dim_qk is None else head_dim_qk
     a.head_dim_v = (v if v is not None else k).shape[3]

@@ -57,6 +57,11 @@ struct PartialParams {
     int64_t ks_s[3];
     const float *v_scale;
     int64_t vs_s[3];
+    // Speculative decoding: packed query rows of variable count per sequence (q_starts, nullable)
+    // and a tree mask over each sequence's last Q_b keys, mask_words 32-bit words per token row.
+    const int32_t *q_starts;
+    const uint32_t *tree_mask;
+    int32_t mask_words;
     // MLA second score part (rope): q_pe rows and kpe rows, 64 columns
     const void *q2;
     int64_t q2_s[3];
@@ -84,6 +89,36 @@ __device__ __forceinline__ UnitId decode_unit(const PartialParams &p) {
     return u;
 }
 
+// Query tokens of sequence b and the packed row of its token 0: q_len tokens at row b * q_len, or
+// with q_starts the count q_starts[b+1] - q_starts[b] clamped to [0, q_len] (so that the padded
+// partial rows stay in bounds) at row q_starts[b].
+struct QRows {
+    int n;
+    int first;
+};
+__device__ __forceinline__ QRows q_rows(const int32_t *q_starts, int q_len, int b) {
+    if (!q_starts) return QRows{q_len, b * q_len};
+    const int s0 = q_starts[b];
+    return QRows{min(max(q_starts[b + 1] - s0, 0), q_len), s0};
+}
+
+// Output element offset and LSE index of padded row `row` = (b * q_len + t) * num_q_heads + hq
+// (the host keeps the row count below 2^31); t must be < the sequence's token count.
+struct OutIdx {
+    int64_t off;
+    int lse;
+};
+__device__ __forceinline__ OutIdx out_index(const int32_t *q_starts, int q_len, int num_q_heads,
+                                            const int64_t out_s[3], int row) {
+    const int hq = row % num_q_heads, tq = row / num_q_heads;
+    const int t = tq % q_len, b = tq / q_len;
+    if (q_starts) {
+        const int n = q_starts[b] + t;
+        return OutIdx{(int64_t)n * out_s[1] + hq * out_s[2], n * num_q_heads + hq};
+    }
+    return OutIdx{b * out_s[0] + t * out_s[1] + hq * out_s[2], row};
+}
+
 struct MergeParams {
     const float *part_o;
     const float *part_lse;
@@ -101,6 +136,7 @@ struct MergeParams {
     void *out;
     int64_t out_s[3];
     float *lse;
+    const int32_t *q_starts;  // nullable: rows of tokens t >= Q_b are skipped, out / lse packed
 };
 
 // Launchers (hipSuccess or the launch error). They assume the host checks already passed.

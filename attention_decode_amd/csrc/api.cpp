@@ -78,8 +78,14 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
     if (!(std::isfinite(a->scale))) return fail(AD_E_RANGE, "scale must be finite");
     if (a->kv_format != AD_KV_SAME && a->kv_format != AD_KV_FP8_E4M3)
         return fail(AD_E_DTYPE, "kv_format %d is not AD_KV_SAME or AD_KV_FP8_E4M3", a->kv_format);
+    if (a->tree_mask && a->q_len > 64)
+        return fail(AD_E_UNSUPPORTED, "a tree mask covers at most 64 query tokens (q_len %d)", a->q_len);
+    if ((reinterpret_cast<uintptr_t>(a->q_starts) & 3u) || (reinterpret_cast<uintptr_t>(a->tree_mask) & 3u))
+        return fail(AD_E_ALIGN, "q_starts and tree_mask must be 4-byte aligned");
     if (a->batch == 0) return AD_OK;  // nothing is read or written: no pointer is needed
     if (path == Path::Mla) {
+        if (a->q_starts || a->tree_mask)
+            return fail(AD_E_UNSUPPORTED, "MLA takes neither variable query lengths nor a tree mask");
         if (a->dtype != AD_BF16) return fail(AD_E_UNSUPPORTED, "MLA supports bf16 only");
         if (a->head_dim_qk != 576 || a->head_dim_v != 512 || a->num_kv_heads != 1)
             return fail(AD_E_UNSUPPORTED, "MLA needs head_dim_qk 576, head_dim_v 512 and one KV head");
@@ -260,6 +266,9 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
     p.window = a->window;
     p.num_splits = pl.splits;
     p.chunk = pl.chunk;
+    p.q_starts = a->q_starts;
+    p.tree_mask = a->tree_mask;
+    p.mask_words = (a->q_len + 31) / 32;
     if (a->kv_format == AD_KV_FP8_E4M3) {
         p.kv_fp8 = 1;
         p.k_scale = a->k_scale;
@@ -372,6 +381,7 @@ int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, 
     m.out = a->out;
     for (int i = 0; i < 3; ++i) m.out_s[i] = a->out_stride[i];
     m.lse = a->lse;
+    m.q_starts = a->q_starts;
     hipError_t e = ad::launch_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return AD_OK;

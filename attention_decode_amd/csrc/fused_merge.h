@@ -43,12 +43,9 @@ __device__ __forceinline__ float load_partial(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Output element offset of flat row `row` = (b * q_len + t) * num_q_heads + hq (the host keeps
-// the row count below 2^31), column 0.
-__device__ __forceinline__ int64_t out_offset(const PartialParams &p, int row) {
-    const int hq = row % p.num_q_heads, tq = row / p.num_q_heads;
-    const int t = tq % p.q_len, b = tq / p.q_len;
-    return b * p.out_s[0] + t * p.out_s[1] + hq * p.out_s[2];
+// Output element offset (column 0) and LSE index of padded row `row` (packed rows with q_starts).
+__device__ __forceinline__ OutIdx out_index(const PartialParams &p, int row) {
+    return out_index(p.q_starts, p.q_len, p.num_q_heads, p.out_s, row);
 }
 
 __device__ __forceinline__ void store_out(const PartialParams &p, int64_t off, float v) {
@@ -62,10 +59,9 @@ __device__ __forceinline__ void store_out(const PartialParams &p, int64_t off, f
 template <int NTHREADS, int DV, typename RowFn>
 __device__ void fused_write_empty(const PartialParams &p, int nr, RowFn out_row) {
     for (int r = 0; r < nr; ++r) {
-        const int row = (int)out_row(r);
-        const int64_t off = out_offset(p, row);
-        for (int d = threadIdx.x; d < DV; d += NTHREADS) store_out(p, off + d, 0.f);
-        if (p.lse && threadIdx.x == 0) p.lse[row] = -INFINITY;
+        const OutIdx oi = out_index(p, (int)out_row(r));
+        for (int d = threadIdx.x; d < DV; d += NTHREADS) store_out(p, oi.off + d, 0.f);
+        if (p.lse && threadIdx.x == 0) p.lse[oi.lse] = -INFINITY;
     }
 }
 
@@ -78,7 +74,7 @@ template <int NTHREADS, int DV, int EPT, typename RowFn>
 __device__ void fused_arrive_merge(const PartialParams &p, int unit, int nsplit, int nr, RowFn out_row,
                                    float *weights) {
     __shared__ int s_last;
-    __shared__ int s_row[64];                // per row: flat output row
+    __shared__ int s_row[64];                // per row: LSE index
     __shared__ float s_inv[64], s_lse[64];   // per row: 1 / sum_s w_s and the merged LSE
     __shared__ int64_t s_off[64];            // per row: output element offset of column 0
     __builtin_amdgcn_s_waitcnt(kWaitStores);  // this wave's partial stores are acknowledged
@@ -110,9 +106,9 @@ __device__ void fused_arrive_merge(const PartialParams &p, int unit, int nsplit,
         weights[i] = load_partial(p.part_lse + (int64_t)(int)out_row(r) * S + s);
     }
     for (int r = threadIdx.x; r < nr; r += NTHREADS) {
-        const int row = (int)out_row(r);
-        s_row[r] = row;
-        s_off[r] = out_offset(p, row);
+        const OutIdx oi = out_index(p, (int)out_row(r));
+        s_row[r] = oi.lse;
+        s_off[r] = oi.off;
     }
     __syncthreads();
     for (int r = threadIdx.x; r < nr; r += NTHREADS) {

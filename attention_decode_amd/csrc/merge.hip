@@ -7,7 +7,9 @@
 // partial row is read with one coalesced wave-wide load. The split weights are wave-uniform:
 // the row index is made uniform with readfirstlane, so the LSE reads become scalar loads and the
 // exponentials are computed once per split per lane without any cross-lane traffic beyond the
-// max. Ragged batches (paged path) merge only the ceil(L_b / chunk) splits that hold keys.
+// max. Ragged batches (paged path) merge only the ceil(L_b / chunk) splits that hold keys. With
+// variable query lengths the rows of tokens past a sequence's count are skipped, and the others
+// are written to their packed output rows.
 #include "ad_internal.h"
 
 #include <math.h>
@@ -24,10 +26,11 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
     const int lane = threadIdx.x & 63;
     const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6));
     if (row >= p.rows) return;
-    const int hq = row % p.num_q_heads;
     const int t = (row / p.num_q_heads) % p.q_len;
     const int b = row / (p.num_q_heads * p.q_len);
     const int Dv = p.head_dim_v;
+    if (p.q_starts && t >= q_rows(p.q_starts, p.q_len, b).n) return;  // uniform: no such token
+    const OutIdx oi = out_index(p.q_starts, p.q_len, p.num_q_heads, p.out_s, row);
 
     int S = p.num_splits;
     if (p.count_by_len) {
@@ -67,8 +70,7 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
-    char *dst = static_cast<char *>(p.out) +
-                (b * p.out_s[0] + t * p.out_s[1] + hq * p.out_s[2] + lane * VEC) * (OUT_BF16 ? 2 : 4);
+    char *dst = static_cast<char *>(p.out) + (oi.off + lane * VEC) * (OUT_BF16 ? 2 : 4);
     if constexpr (OUT_BF16) {
         __bf16 *d = reinterpret_cast<__bf16 *>(dst);
 #pragma unroll
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
 #pragma unroll
         for (int j = 0; j < VEC; ++j) d[j] = o[j] * inv;
     }
-    if (p.lse && lane == 0) p.lse[row] = W > 0.f ? M + __builtin_amdgcn_logf(W) * kLn2 : -INFINITY;
+    if (p.lse && lane == 0) p.lse[oi.lse] = W > 0.f ? M + __builtin_amdgcn_logf(W) * kLn2 : -INFINITY;
 }
 
 template <int VEC>

@@ -124,8 +124,12 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
-    const int G = p.group, Q = p.q_len, R = G * Q, S = p.num_splits, Dv = p.head_dim_v;
+    const int G = p.group, Q = p.q_len, S = p.num_splits, Dv = p.head_dim_v;
+    // this sequence's query tokens (fewer than q_len with variable query lengths)
+    const QRows qrows = q_rows(p.q_starts, Q, b);
+    const int Qb = qrows.n, R = G * Qb;
     const int r0 = rb * kRows, nr = min(kRows, R - r0);
+    if (nr <= 0) return;  // uniform: a row block past the sequence's last token
     const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
 
     int vlen = L;
@@ -176,9 +180,15 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     const int map_mask = (1 << map_shift) - 1;
 
     // ---- this lane's query row (row col of the unit) as the B operand, and its visible range
-    const uint16_t *qbase = static_cast<const uint16_t *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
+    const uint16_t *qbase = static_cast<const uint16_t *>(p.q) +
+                            (p.q_starts ? (int64_t)qrows.first * p.q_s[1] : b * p.q_s[0]) +
+                            (int64_t)(h * G) * p.q_s[2];
     u32x4 qb[kKs];
     int lo_r = INT_MIN, hi_r = INT_MAX;
+    // Tree mask: the last Qb keys are the drafts; this lane's row sees draft i only with bit i of
+    // its token's mask row (tm0: drafts 0-31, tm1: 32-63).
+    const int first_draft = L - Qb;
+    uint32_t tm0 = ~0u, tm1 = ~0u;
     {
         const int ra = r0 + col;
         const int t = ra / G, g = ra - t * G;
@@ -187,9 +197,14 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks)  // fp8: the head-dim order of the fp8 K operand
                 qb[ks] = ld16(qr + (FP8 ? 32 * (ks / 2) + 16 * half + 8 * (ks % 2) : 16 * ks + 8 * half));
-            const int qpos = L - Q + t;
+            const int qpos = L - Qb + t;
             if (p.causal) hi_r = qpos + 1;
             if (p.window) lo_r = qpos - p.window + 1;
+            if (p.tree_mask) {
+                const uint32_t *mr = p.tree_mask + (int64_t)(qrows.first + t) * p.mask_words;
+                tm0 = mr[0];
+                tm1 = p.mask_words > 1 ? mr[1] : 0u;
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
@@ -199,10 +214,11 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     // [lo_max, hi_min) by every row.
     const int t_first = __builtin_amdgcn_readfirstlane(r0 / G);
     const int t_last = __builtin_amdgcn_readfirstlane((r0 + nr - 1) / G);
-    const int hi_min = p.causal ? L - Q + t_first + 1 : INT_MAX;
-    const int hi_max = p.causal ? L - Q + t_last + 1 : INT_MAX;
-    const int lo_min = p.window ? L - Q + t_first - p.window + 1 : INT_MIN;
-    const int lo_max = p.window ? L - Q + t_last - p.window + 1 : INT_MIN;
+    // (tree mask: keys from the first draft on are never seen by every row for certain)
+    const int hi_min = min(p.causal ? L - Qb + t_first + 1 : INT_MAX, p.tree_mask ? first_draft : INT_MAX);
+    const int hi_max = p.causal ? L - Qb + t_last + 1 : INT_MAX;
+    const int lo_min = p.window ? L - Qb + t_first - p.window + 1 : INT_MIN;
+    const int lo_max = p.window ? L - Qb + t_last - p.window + 1 : INT_MIN;
 
     // ---- key addressing: virtual key index v (position in the split's key range) -> logical
     // position and row offsets. Only called with v < t1.
@@ -354,7 +370,11 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int pos = pos4 + e;
-                    const bool vis = v4 + e < t1 && pos < L && pos >= lo_r && pos < hi_r;
+                    bool vis = v4 + e < t1 && pos < L && pos >= lo_r && pos < hi_r;
+                    if (p.tree_mask && vis && pos >= first_draft) {
+                        const int i = pos - first_draft;  // < Qb <= 64: a visible key lies below L
+                        vis = ((i < 32 ? tm0 : tm1) >> (i & 31)) & 1u;
+                    }
                     sv[4 * q4 + e] = vis ? sv[4 * q4 + e] : -INFINITY;
                 }
             }

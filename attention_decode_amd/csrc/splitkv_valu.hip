@@ -127,8 +127,12 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps step bases scalar
     const int slot = lane / LPT, c = lane % LPT;
-    const int G = p.group, Q = p.q_len, R = G * Q, S = p.num_splits, Dv = p.head_dim_v;
+    const int G = p.group, Q = p.q_len, S = p.num_splits, Dv = p.head_dim_v;
+    // this sequence's query tokens (fewer than q_len with variable query lengths)
+    const QRows qr = q_rows(p.q_starts, Q, b);
+    const int Qb = qr.n, R = G * Qb;
     const int r0 = rb * RP, nr = min(RP, R - r0);  // this unit's rows: r0 .. r0 + nr - 1
+    if (nr <= 0) return;  // uniform: a row block past the sequence's last token
     const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
 
     int vlen = L;  // length of the key range the splits partition
@@ -164,6 +168,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     __shared__ float s_m[kWaves][RP];
     __shared__ float s_l[kWaves][RP];
     __shared__ float s_lf[kWaves][RP];
+    __shared__ uint32_t s_tree[RP][2];  // tree mask words of each row's token
 
     const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
     const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
@@ -179,14 +184,26 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     if constexpr (MODE != KV_CONTIG) __syncthreads();
 
     // ---- query rows of this unit: row r0 + r = t*G + g (hq = h*G + g)
-    const T *qbase = static_cast<const T *>(p.q) + b * p.q_s[0] + (int64_t)(h * G) * p.q_s[2];
+    const T *qbase = static_cast<const T *>(p.q) + (p.q_starts ? (int64_t)qr.first * p.q_s[1] : b * p.q_s[0]) +
+                     (int64_t)(h * G) * p.q_s[2];
+    // Tree mask: the last Qb keys are the drafts; a row sees draft i only with bit i of its token's
+    // mask row. Steps that reach the drafts take the masked path.
+    const int first_draft = L - Qb;
+    if (p.tree_mask) {
+        if (tid < RP * 2) {
+            const int r = tid >> 1, w = tid & 1;
+            const int t = (r0 + min(r, nr - 1)) / G;
+            s_tree[r][w] = w < p.mask_words ? p.tree_mask[(int64_t)(qr.first + t) * p.mask_words + w] : 0u;
+        }
+        __syncthreads();
+    }
     u32x4 qv[RP][kQv];
     int lo[RP], hi[RP];  // visible key positions of row r: [lo, hi)
-    int lo_max = INT_MIN, hi_min = INT_MAX;
+    int lo_max = INT_MIN, hi_min = p.tree_mask ? first_draft : INT_MAX;
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         const int ra = r0 + r, t = ra / G, g = ra - t * G;
-        const int qpos = L - Q + t;
+        const int qpos = L - Qb + t;
         hi[r] = p.causal ? qpos + 1 : INT_MAX;
         lo[r] = p.window ? qpos - p.window + 1 : INT_MIN;
         if (r < nr) {
@@ -356,7 +373,11 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                     d *= p.scale_log2;
                 if constexpr (kMasked) {
                     const int pos = cur.pos0 + u * kSlots + slot;
-                    const bool vis = cur.val[u] && pos >= lo[r] && pos < hi[r];
+                    bool vis = cur.val[u] && pos >= lo[r] && pos < hi[r];
+                    if (p.tree_mask && vis && pos >= first_draft) {
+                        const int i = pos - first_draft;  // < Qb <= 64: a visible key lies below L
+                        vis = (s_tree[r][i >> 5] >> (i & 31)) & 1u;
+                    }
                     d = vis ? d : -INFINITY;
                 }
                 sc[u][r] = d;

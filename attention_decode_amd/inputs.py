@@ -19,6 +19,10 @@ The workloads (sizes of the decode benchmarks this library is measured on; 6 is 
    (the latent), KV len 8192, bf16, paged with page 64, scale 1/sqrt(192).
 6. workload 3 with its cache quantised to OCP E4M3 (fp8) bytes with one fp32 scale per (token, KV
    head) row for K and for V (the same lengths and values before quantisation).
+7. speculative decoding over workload 3's shape: B=64 paged sequences (lengths uniform in
+   [128, 8192], page 16, 32 q / 8 KV heads, D=128, bf16), each with 1 to 8 draft tokens (uniform)
+   as packed variable-length queries, and a random token tree per sequence as the tree mask
+   (token t sees itself and its ancestors among the drafts).
 
 Cache layouts: a contiguous cache is stored head-major ``[B, Hkv, L, D]``; a paged pool is stored
 ``[pages, Hkv, page_size, D]``. Both are handed out as token-major *views* ``[B, L, Hkv, D]`` /
@@ -32,7 +36,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-NUM_CONFIGS = 6
+NUM_CONFIGS = 7
 
 
 @dataclass
@@ -72,13 +76,18 @@ class Workload:
     kv_format: str = "same"
     k_scale: torch.Tensor | None = None
     v_scale: torch.Tensor | None = None
+    # speculative decoding: packed variable-length queries (q is then [tokens, Hq, D] and q_len
+    # the largest count) and a tree mask over each sequence's last Q_b keys (int32 words,
+    # [token rows, ceil(q_len / 32)])
+    q_starts: torch.Tensor | None = None
+    tree_mask: torch.Tensor | None = None
     storage: dict = field(default_factory=dict)
 
     def to(self, device) -> "Workload":
         """Copy every tensor to `device`, keeping the storage layout the views point into."""
         out = copy.copy(self)
         out.storage = {name: t.to(device) for name, t in self.storage.items()}
-        for f in ("seq_lens", "block_table", "num_blocks", "block_idx"):
+        for f in ("seq_lens", "block_table", "num_blocks", "block_idx", "q_starts", "tree_mask"):
             t = getattr(self, f)
             if t is not None:
                 setattr(out, f, t.to(device))
@@ -90,12 +99,14 @@ class Workload:
         inside a listed block (block-sparse cache), and visible to at least one query row under
         the causal / sliding-window bounds."""
         lens = [int(x) for x in self.seq_lens.to("cpu")]
+        counts = self.q_counts()
         per_tok = self.bytes_per_key()
         heads = 1 if self.kind == "mla" else self.num_kv_heads
         out = []
         for b, L in enumerate(lens):
-            hi = L                                                                 # newest query sits at L - 1
-            lo = max(0, L - self.q_len - self.window + 1) if self.window else 0   # oldest key of the first query
+            Qb = counts[b]
+            hi = L if Qb else 0                                               # newest query sits at L - 1
+            lo = max(0, L - Qb - self.window + 1) if self.window else 0      # oldest key of the first query
             row = []
             for h in range(heads):
                 if self.num_blocks is None:
@@ -107,6 +118,13 @@ class Workload:
                 row.append(n * per_tok)
             out.append(row)
         return out
+
+    def q_counts(self) -> list:
+        """Query tokens of each sequence: q_len, or the differences of q_starts."""
+        if self.q_starts is None:
+            return [self.q_len] * self.batch
+        qs = [int(x) for x in self.q_starts.to("cpu")]
+        return [qs[b + 1] - qs[b] for b in range(self.batch)]
 
     def bytes_per_key(self) -> int:
         """Bytes one key costs per KV head: its K and V rows (MLA: ckv + kpe once), plus its two
@@ -126,9 +144,11 @@ class Workload:
     def flops(self) -> int:
         """Multiply-adds x 2 of one step over the visible keys: q.k (head_dim_qk) and p.v (head_dim_v)
         for every query row of each KV head."""
-        keys = self.kv_bytes() // self.bytes_per_key()
-        rows_per_head = self.q_len * (self.num_q_heads if self.kind == "mla" else self.num_q_heads // self.num_kv_heads)
-        return keys * rows_per_head * (self.head_dim_qk + self.head_dim_v) * 2
+        per_key = self.bytes_per_key()
+        heads_per_kv = self.num_q_heads if self.kind == "mla" else self.num_q_heads // self.num_kv_heads
+        counts = self.q_counts()
+        keys_rows = sum(sum(x) // per_key * counts[b] * heads_per_kv for b, x in enumerate(self.kv_bytes_by_group()))
+        return keys_rows * (self.head_dim_qk + self.head_dim_v) * 2
 
 
 # token-major view of each storage tensor: (storage name, permutation) per field
@@ -346,6 +366,49 @@ def mla(*, config=0, name="custom", batch, num_heads, kv_len, page_size, dim_lat
     return _finish(w)
 
 
+def random_tree_masks(g, counts, q_len):
+    """Tree masks of random draft-token trees, one tree per sequence with counts[b] tokens: the
+    parent of token i >= 1 is uniform in [0, i) and token 0 is the root; token t sees itself and
+    its ancestors. Returns int32 [sum(counts), ceil(q_len / 32)] words, bit i of a row = draft i."""
+    words = (q_len + 31) // 32
+    rows = []
+    for n in counts:
+        parent = [-1] + [int(torch.randint(0, i, (1,), generator=g)) for i in range(1, n)]
+        for t in range(n):
+            bits, i = 0, t
+            while i >= 0:
+                bits |= 1 << i
+                i = parent[i]
+            rows.append([(bits >> (32 * w)) & 0xFFFFFFFF for w in range(words)])
+    m = torch.tensor(rows, dtype=torch.int64).reshape(len(rows), words)
+    return torch.where(m >= 2 ** 31, m - 2 ** 32, m).to(torch.int32)
+
+
+def with_spec(w: Workload, counts=None, tree: bool = False, seed: int = 0) -> Workload:
+    """Speculative-decoding form of a workload whose q is [B, q_len, Hq, D]: with `counts`, the
+    first counts[b] query tokens of each sequence become packed variable-length queries
+    (q [tokens, Hq, D], q_starts [B + 1]); with `tree`, a random token tree per sequence becomes
+    the tree mask (drawn from torch.Generator seeded with `seed`)."""
+    if w.kind == "mla":
+        raise ValueError("MLA takes no variable query lengths or tree masks")
+    out = copy.copy(w)
+    out.storage = dict(w.storage)
+    if counts is not None:
+        counts = [int(c) for c in counts]
+        if len(counts) != w.batch or min(counts) < 0 or max(counts) > w.q_len:
+            raise ValueError("counts must give 0..q_len tokens per sequence")
+        q = w.storage["q"]
+        out.storage["q"] = torch.cat([q[b, :counts[b]] for b in range(w.batch)]).contiguous()
+        starts = [0]
+        for c in counts:
+            starts.append(starts[-1] + c)
+        out.q_starts = torch.tensor(starts, dtype=torch.int32)
+    if tree:
+        g = torch.Generator().manual_seed(seed)
+        out.tree_mask = random_tree_masks(g, out.q_counts(), w.q_len)
+    return _finish(out)
+
+
 def make(config: int, *, seed: int | None = None, poison: bool = False) -> Workload:
     """One of the five benchmark workloads, generated on the CPU."""
     s = 1000 + config if seed is None else seed
@@ -377,4 +440,13 @@ def make(config: int, *, seed: int | None = None, poison: bool = False) -> Workl
         return paged(config=6, name="paged_gqa_fp8_ragged", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
                      head_dim=128, page_size=16, dtype=torch.bfloat16, seed=s3 + 1, poison=poison,
                      max_pages=512, kv_format="fp8", kv_scales="token")
+    if config == 7:  # workload 3's shape with 1-8 draft tokens per sequence and a token tree each
+        s7 = 1007 if seed is None else seed
+        g = torch.Generator().manual_seed(s7)
+        lens = torch.randint(128, 8193, (64,), generator=g, dtype=torch.int64).tolist()
+        counts = torch.randint(1, 9, (64,), generator=g, dtype=torch.int64).tolist()
+        base = paged(config=7, name="paged_gqa_bf16_spec_tree", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, page_size=16, q_len=8, dtype=torch.bfloat16, seed=s7 + 1, poison=poison,
+                     max_pages=512)
+        return with_spec(base, counts=counts, tree=True, seed=s7 + 2)
     raise ValueError(f"unknown workload {config}")

@@ -6,6 +6,9 @@ workspace, and each call enqueues the whole step on the current stream:
       split per work unit merges); with fused=False, attn_decode_splitkv + attn_decode_merge and
       the partials are kept in part_o / part_lse
   MLA: attn_decode_mla (partial pass + merge)
+With packed variable-length queries (w.q_starts) out / lse are packed [tokens, Hq, ...] too; the
+separate public merge takes whole [B, q_len] rows, so that form needs fused=True (attn_decode
+still picks one or two launches itself).
 """
 from __future__ import annotations
 
@@ -22,11 +25,15 @@ class DecodeStep:
         self.w = w
         dev = w.q.device
         B, Q, Hq, Dv = w.batch, w.q_len, w.num_q_heads, w.head_dim_v
-        self.out = torch.empty(B, Q, Hq, Dv, dtype=w.dtype, device=dev) if out is None else out
-        self.lse = torch.empty(B, Q, Hq, dtype=torch.float32, device=dev) if lse is None else lse
+        rows = (w.q.shape[0],) if w.q_starts is not None else (B, Q)
+        if w.q_starts is not None and not fused:
+            raise ValueError("packed variable-length queries need fused=True")
+        self.out = torch.empty(*rows, Hq, Dv, dtype=w.dtype, device=dev) if out is None else out
+        self.lse = torch.empty(*rows, Hq, dtype=torch.float32, device=dev) if lse is None else lse
         forced = num_splits if num_splits is not None else (w.num_splits or 0)
         common = dict(scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max, causal=w.causal,
-                      window=w.window, out=self.out, lse=self.lse)
+                      window=w.window, out=self.out, lse=self.lse, q_starts=w.q_starts,
+                      q_len=w.q_len if w.q_starts is not None else None, tree_mask=w.tree_mask)
         self.sparse = self.paged = None
         self.fused = fused and w.kind != "mla"
         if w.kind == "mla":

@@ -45,6 +45,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     4: ("partial_mfma_sparse", "partial_mfma_kernel + merge_kernel (two launches per step)"),
     5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
     6: ("partial_mfma_paged_fp8", "partial_mfma_kernel, fp8 cache + merge_kernel (two launches per step)"),
+    7: ("partial_mfma_paged_spec", "partial_mfma_kernel, draft trees + merge_kernel (two launches per step)"),
 }
 
 
@@ -64,10 +65,13 @@ class Step:
         self.abi = _abi
         dev = w.q.device
         B, Q, Hq, Dv = w.batch, w.q_len, w.num_q_heads, w.head_dim_v
-        self.out = torch.empty(B, Q, Hq, Dv, dtype=w.dtype, device=dev)
-        self.lse = torch.empty(B, Q, Hq, dtype=torch.float32, device=dev)
+        rows = (w.q.shape[0],) if w.q_starts is not None else (B, Q)  # packed variable-length queries
+        self.out = torch.empty(*rows, Hq, Dv, dtype=w.dtype, device=dev)
+        self.lse = torch.empty(*rows, Hq, dtype=torch.float32, device=dev)
         common = dict(scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max, causal=w.causal,
                       window=w.window, out=self.out, lse=self.lse)
+        if w.q_starts is not None or w.tree_mask is not None:
+            common.update(q_starts=w.q_starts, q_len=Q if w.q_starts is not None else None, tree_mask=w.tree_mask)
         self.sets = []
         for c in range(copies):
             # .clone() of a strided view keeps its strides
@@ -144,6 +148,10 @@ def oracle_kwargs(w):
         kw.update(q2=w.q_pe, k2=w.kpe)
     if w.kv_format == "fp8":
         kw.update(k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.q_starts is not None:
+        kw.update(q_starts=w.q_starts, q_len=w.q_len)
+    if w.tree_mask is not None:
+        kw.update(tree_mask=w.tree_mask)
     return kw
 
 
@@ -154,7 +162,9 @@ def cpu_baseline(w_cpu, budget_s=12.0):
     import oracle
 
     orc = oracle.load()
-    Hq, Q = w_cpu.num_q_heads, w_cpu.q_len
+    Hq = w_cpu.num_q_heads
+    counts = w_cpu.q_counts()
+    first = [int(x) for x in w_cpu.q_starts] if w_cpu.q_starts is not None else [b * w_cpu.q_len for b in range(w_cpu.batch)]
     Hkv = 1 if w_cpu.kind == "mla" else w_cpu.num_kv_heads
     G = Hq // Hkv
     by_group = w_cpu.kv_bytes_by_group()
@@ -168,7 +178,7 @@ def cpu_baseline(w_cpu, budget_s=12.0):
         # next chunk of groups: grow geometrically so the timing overhead stays negligible
         n = max(1, min(len(order) - i, 2 ** min(groups.bit_length(), 6)))
         sel = order[i:i + n]
-        rows = [(b * Q + t) * Hq + h * G + g for (b, h) in sel for t in range(Q) for g in range(G)]
+        rows = [(first[b] + t) * Hq + h * G + g for (b, h) in sel for t in range(counts[b]) for g in range(G)]
         t0 = time.perf_counter()
         orc.attend(w_cpu.q, w_cpu.k, v, rows=rows, **kw)
         elapsed += time.perf_counter() - t0
@@ -178,7 +188,8 @@ def cpu_baseline(w_cpu, budget_s=12.0):
     return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": orc.threads(),
             "kind": "oracle",
             "sample": f"{groups} (sequence, KV head) groups of the {len(order)} in the workload (in order, "
-                      f"wrapping), all {G * Q} query rows each: {done_bytes / 1e6:.1f} MB of KV in {elapsed:.1f} s"}
+                      f"wrapping), all {G} x (query tokens) rows each: {done_bytes / 1e6:.1f} MB of KV in "
+                      f"{elapsed:.1f} s"}
 
 
 def load_traffic(kernel_tag):
@@ -302,6 +313,10 @@ def main():
               "head_dim_qk": w.head_dim_qk, "head_dim_v": w.head_dim_v, "q_len": w.q_len,
               "kv_tokens": int(w_cpu.seq_lens.sum()), "kv_bytes_per_step": kv_bytes, "flops_per_step": flops,
               "splits": step.splits, "split_keys": step.chunk, "cache_copies_rotated": copies}
+    if w.q_starts is not None:
+        config["query_tokens"] = int(w.q.shape[0])  # packed variable-length queries, q_len at most
+    if w.tree_mask is not None:
+        config["tree_mask"] = True
     if w.page_size:
         config["page_size"] = w.page_size
     if w.num_blocks is not None:

@@ -110,6 +110,26 @@ typedef struct ad_decode_args {
     int64_t k_scale_stride[3];
     const float *v_scale;
     int64_t v_scale_stride[3];
+    /* Speculative decoding (TensorRT-LLM xqa mha.cu SPEC_DEC: qCuSeqLens and the packed input
+     * mask; mslk splitk_kernels.py Seq_starts_q). Both NULL in a zero-filled struct: off.
+     *
+     * q_starts [batch + 1] (device): variable query lengths. Sequence b has
+     * Q_b = q_starts[b+1] - q_starts[b] query tokens, 0 <= Q_b <= q_len (q_len is then the
+     * largest count), and its token t is packed row n = q_starts[b] + t: q row at
+     * q + n*q_stride[1] + hq*q_stride[2] (q_stride[0] is not used), out row likewise with
+     * out_stride, lse[n*num_q_heads + hq]. The token sits at position L_b - Q_b + t. Rows of
+     * tokens t >= Q_b do not exist: nothing is read or written for them (the partial layout of
+     * attn_decode_splitkv keeps its [batch, q_len, ...] rows; those stay unwritten). The counts
+     * are the caller's contract, like a block table: they are clamped to [0, q_len] for the
+     * library's own buffers, but q / out / lse rows are addressed through q_starts as given.
+     *
+     * tree_mask (device): the last Q_b keys of sequence b are its draft tokens, draft key i at
+     * position L_b - Q_b + i. Token row n (q_starts[b] + t, or b*q_len + t without q_starts)
+     * sees draft key i only if bit i % 32 of tree_mask[n * ceil(q_len / 32) + i / 32] is set;
+     * keys before the drafts are not affected, and the mask combines (AND) with causal, window
+     * and block lists. q_len <= 64 with a tree mask. Neither field is supported with MLA. */
+    const int32_t *q_starts;
+    const uint32_t *tree_mask;
 } ad_decode_args;
 
 /* Paged cache: logical page p of sequence b is pool page block_table[b * bt_stride + p]

@@ -27,6 +27,10 @@ def oracle_of(orc, w, rows=None, key_range=None):
               key_range=key_range)
     if w.kv_format == "fp8":
         kw.update(k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.q_starts is not None:
+        kw.update(q_starts=w.q_starts, q_len=w.q_len)
+    if w.tree_mask is not None:
+        kw.update(tree_mask=w.tree_mask)
     if w.kind == "contiguous":
         if w.num_blocks is not None:
             kw.update(num_blocks=w.num_blocks, block_idx=w.block_idx, block_size=w.block_size)

@@ -384,3 +384,28 @@ def test_kernel_query(monkeypatch):
     a.head_dim_qk = 96
     with pytest.raises(_abi.ADError):
         ad.attn_decode_kernel(a)
+
+
+def test_spec_decoding_rejections():
+    """Tree masks cover at most 64 query tokens; q_starts and tree_mask must be 4-byte aligned;
+    MLA takes neither. Checked before any device work."""
+    q, k, v, out = _tensors(Q=1)
+    qp = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    outp = torch.zeros(5, 8, 128, dtype=torch.bfloat16)
+    starts = torch.tensor([0, 3, 5], dtype=torch.int32)
+    mask = torch.zeros(5, 3, dtype=torch.int32)
+    a = _abi.make_args(qp, k, v, scale=0.1, out=outp, q_starts=starts, q_len=65, tree_mask=mask)
+    assert a.batch == 2 and a.q_len == 65 and a.q_stride[1] == 8 * 128 and a.q_stride[2] == 128
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(a), ctypes.byref(ctypes.c_int32())) == -5
+    a.q_len = 64
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX  # 4 heads x 64 rows per KV head
+    a.tree_mask = a.tree_mask + 2
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(a), ctypes.byref(ctypes.c_int32())) == -4
+    a.tree_mask, a.q_starts = None, a.q_starts + 1
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(a), ctypes.byref(ctypes.c_int32())) == -4
+    qm = torch.zeros(2, 16, 512, dtype=torch.bfloat16)
+    ckv = torch.zeros(4, 64, 1, 512, dtype=torch.bfloat16)
+    m = _abi.make_args(qm, ckv, None, head_dim_qk=576, scale=0.1, q_starts=starts, q_len=1)
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(m), ctypes.byref(ctypes.c_int32())) == -5
+    m = _abi.make_args(qm[None], ckv, None, head_dim_qk=576, scale=0.1, tree_mask=mask)
+    assert _abi.lib().attn_decode_kernel(ctypes.byref(m), ctypes.byref(ctypes.c_int32())) == -5

@@ -105,3 +105,23 @@ def test_one_launch_equals_two_launches(monkeypatch, kernel):
         o1, l1, _ = run(w, num_splits=S)
         o2, l2, _ = run(w, num_splits=S, fused=False)
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2), f"S={S}"
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_every_value_code_decodes_exactly(monkeypatch, kernel):
+    """With one key per sequence the output is that key's value row times its scale (1 here), and
+    every E4M3 value is a bf16 value: each of the 252 nonzero finite codes (and +0) must come out bit-exact as
+    PyTorch's float8_e4m3fn decodes it (sequence 0 carries codes 0x00-0x7E, sequence 1 0x80-0xFE;
+    the two NaN codes are replaced by 0, and so is -0, 0x80: a weighted sum that starts from +0
+    returns +0 for it, which attention cannot tell apart)."""
+    force(monkeypatch, kernel)
+    say(f"[gpu] fp8 value codes, {kernel}")
+    w = inputs.contiguous(batch=2, num_q_heads=1, num_kv_heads=1, head_dim=128, kv_len=1, seed=11,
+                          kv_format="fp8")
+    codes = torch.arange(256, dtype=torch.int32).reshape(2, 128)
+    codes[(codes % 128 == 127) | (codes == 128)] = 0
+    w.storage["v"].copy_(codes.to(torch.uint8).reshape(2, 1, 1, 128))
+    w.storage["v_scale"].fill_(1.0)
+    out, lse, _ = run(w)
+    want = codes.to(torch.uint8).view(torch.float8_e4m3fn).to(torch.bfloat16).reshape(2, 1, 1, 128)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
