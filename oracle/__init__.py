@@ -17,6 +17,8 @@ Variable query lengths: with q_starts ([batch + 1] packed token offsets) q (and 
 [tokens, num_q_heads, dim], q_len (the largest per-sequence count, the tree-mask row pitch) is
 passed explicitly, and out / lse come back packed as [tokens, num_q_heads, ...]. A tree mask is
 int32/uint32 [token rows, ceil(q_len / 32)] (bit i of a row: draft key i visible).
+An int4 cache passes k and v as int32 views [..., n_groups + dim / 8] (coefficient words, then
+the packed values; see oracle.c) with int4_groups = n_groups; dim_v is then dim_qk.
 """
 from __future__ import annotations
 
@@ -31,8 +33,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "oracle.c")
 LIBRARY = os.path.join(_HERE, "liboracle.so")
 
-F64, F32, BF16, E4M3 = 0, 1, 2, 3
-_TYPE = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16, torch.uint8: E4M3}
+F64, F32, BF16, E4M3, INT4 = 0, 1, 2, 3, 4
+_TYPE = {torch.float64: F64, torch.float32: F32, torch.bfloat16: BF16, torch.uint8: E4M3, torch.int32: INT4}
 
 
 class Problem(ctypes.Structure):
@@ -56,6 +58,7 @@ class Problem(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("ks_stride", ctypes.c_int64 * 3),
         ("v_scale", ctypes.c_void_p), ("vs_stride", ctypes.c_int64 * 3),
         ("q_starts", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
+        ("n_groups", ctypes.c_int32),
     ]
 
 
@@ -111,7 +114,7 @@ class Oracle:
                q2=None, k2=None, block_table=None, page_size: int = 0,
                num_blocks=None, block_idx=None, block_size: int = 0,
                causal: bool = False, window: int = 0, key_range=None, rows=None, k_scale=None, v_scale=None,
-               q_starts=None, q_len: int | None = None, tree_mask=None):
+               q_starts=None, q_len: int | None = None, tree_mask=None, int4_groups: int = 0):
         """Returns (out, lse) as float64 numpy arrays.
 
         out is [batch, q_len, num_q_heads, dim_v] (packed [tokens, num_q_heads, dim_v] with
@@ -134,13 +137,18 @@ class Oracle:
         if qs is not None:
             B, Q = qs.numel() - 1, int(q_len)
         Hkv = k.shape[2]
-        if q.dtype not in _TYPE or k.dtype not in _TYPE or v.dtype != k.dtype or q.dtype == torch.uint8:
+        if q.dtype not in _TYPE or k.dtype not in _TYPE or v.dtype != k.dtype or q.dtype in (torch.uint8, torch.int32):
             raise ValueError("unsupported element types")
+        if (k.dtype == torch.int32) != (int4_groups > 0):
+            raise ValueError("an int4 (int32) cache needs int4_groups, and only it takes them")
+        if int4_groups and k.shape[3] != int4_groups + Dqk // 8:
+            raise ValueError("int4 rows hold n_groups coefficient words and dim / 8 packed words")
         if (k.dtype == torch.uint8) != (k_scale is not None and v_scale is not None):
             raise ValueError("an fp8 (uint8) cache needs k_scale and v_scale, and only it takes them")
         P = Problem()
         P.batch, P.q_len, P.num_q_heads, P.num_kv_heads = B, Q, Hq, Hkv
-        P.dim_qk, P.dim_v = Dqk, v.shape[3]
+        P.dim_qk, P.dim_v = Dqk, (Dqk if int4_groups else v.shape[3])
+        P.n_groups = int(int4_groups)
         P.scale = float(scale)
         P.q_type, P.kv_type = _TYPE[q.dtype], _TYPE[k.dtype]
         P.q, P.q_stride = q.data_ptr(), self._strides3(q)
@@ -194,7 +202,7 @@ class Oracle:
         else:
             P.key_lo, P.key_hi = int(key_range[0]), int(key_range[1])
 
-        Dv = v.shape[3]
+        Dv = P.dim_v
         tokens = int(qs[-1]) if qs is not None else B * Q
         if rows is None:
             n = tokens * Hq

@@ -68,6 +68,13 @@
  * (1 + m/8) 2^(e-7), e = 0 gives the subnormal m 2^-9, and S.1111.111 is NaN (no infinities), so
  * the largest finite magnitude is 1.75 * 2^8 = 448.
  *
+ * Int4 cache (mslk splitk_kernels.py, the int4 branch of dequantize / _process_int4_quantization):
+ * every K (V) row of dim_qk (dim_v) values is stored as 32-bit words, n_groups coefficient words
+ * followed by the packed values, 8 per word. Dimension d belongs to group g = d / (dim / n_groups)
+ * and is the unsigned 4-bit field (d % 8) of packed word d / 8 (bits 4(d % 8) .. 4(d % 8) + 3);
+ * coefficient word g holds two IEEE half floats, the scale in its low 16 bits and the shift in its
+ * high 16 bits, and the value is field * scale + shift. Row strides then count 32-bit words.
+ *
  * oracle_merge() is the LSE-weighted combine of per-split (o_s, lse_s) pairs written out in fp64
  * (mslk splitk_kernels.py, _splitK_reduce): M = max_s lse_s, w_s = exp(lse_s - M),
  * out = sum_s w_s o_s / sum_s w_s, lse = M + ln sum_s w_s; M = -inf gives out 0, lse -inf.
@@ -83,7 +90,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_E4M3 = 3 };
+enum { ORC_F64 = 0, ORC_F32 = 1, ORC_BF16 = 2, ORC_E4M3 = 3, ORC_INT4 = 4 };
 
 typedef struct {
     int32_t batch, q_len, num_q_heads, num_kv_heads;
@@ -111,6 +118,7 @@ typedef struct {
      * n * q_stride[1] + hq * q_stride[2]); NULL: q_len tokens per sequence */
     const int32_t *q_starts;
     const uint32_t *tree_mask; /* [token rows][ceil(q_len / 32)] words; NULL: none */
+    int32_t n_groups;          /* kv_type ORC_INT4: coefficient words per row (1, 2, 4 or 8) */
 } oracle_problem;
 
 /* Value of one OCP E4M3 byte, from the format's definition. */
@@ -125,6 +133,29 @@ static double e4m3(uint8_t x)
     else
         mag = ldexp(1.0 + m / 8.0, e - 7);
     return sign ? -mag : mag;
+}
+
+/* IEEE binary16 value of a 16-bit pattern, from the format's definition. */
+static double half_value(uint32_t h)
+{
+    const int sign = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    double mag;
+    if (e == 31)
+        mag = m ? NAN : INFINITY;
+    else if (e == 0)
+        mag = ldexp((double)m, -24);
+    else
+        mag = ldexp(1.0 + m / 1024.0, e - 15);
+    return sign ? -mag : mag;
+}
+
+/* Value of dimension d of the int4 row that starts at word `row` (dim values per row). */
+static double int4_value(const void *base, int64_t row, int64_t d, int64_t dim, int32_t n_groups)
+{
+    const uint32_t *w = (const uint32_t *)base + row;
+    const uint32_t coef = w[d / (dim / n_groups)];
+    const uint32_t field = (w[n_groups + d / 8] >> (4 * (d % 8))) & 15u;
+    return (double)field * half_value(coef & 0xFFFFu) + half_value(coef >> 16);
 }
 
 static double widen(const void *base, int32_t type, int64_t i)
@@ -201,8 +232,11 @@ static double score(const oracle_problem *P, int64_t b, int64_t t, int64_t hq, i
     int64_t qo = q_offset(P, P->q_stride, b, t, hq);
     int64_t ko = kv_row(P, P->k_stride, b, hkv, j);
     const double ks = P->kv_type == ORC_E4M3 ? (double)P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)] : 1.0;
-    for (int64_t d = 0; d < P->dim_qk; d++)
-        acc += widen(P->q, P->q_type, qo + d) * (widen(P->k, P->kv_type, ko + d) * ks);
+    for (int64_t d = 0; d < P->dim_qk; d++) {
+        const double kd = P->kv_type == ORC_INT4 ? int4_value(P->k, ko, d, P->dim_qk, P->n_groups)
+                                                 : widen(P->k, P->kv_type, ko + d) * ks;
+        acc += widen(P->q, P->q_type, qo + d) * kd;
+    }
     if (P->dim_qk2 > 0) {
         int64_t qo2 = q_offset(P, P->q2_stride, b, t, hq);
         int64_t ko2 = kv_row(P, P->k2_stride, b, hkv, j);
@@ -224,6 +258,12 @@ static int check_problem(const oracle_problem *P)
     if (P->window < 0) return -1;
     if (P->q_type == ORC_E4M3) return -1;
     if (P->kv_type == ORC_E4M3 && (!P->k_scale || !P->v_scale || P->dim_qk2 > 0)) return -1;
+    if (P->kv_type == ORC_INT4) {
+        const int32_t g = P->n_groups;
+        if (P->dim_qk2 > 0 || (g != 1 && g != 2 && g != 4 && g != 8)) return -1;
+        if (P->dim_qk % (8 * g) || P->dim_v % (8 * g)) return -1;
+    }
+    if (P->q_type == ORC_INT4) return -1;
     if (P->q_starts) {
         if (P->q_starts[0] < 0) return -1;
         for (int64_t b = 0; b < P->batch; b++)
@@ -316,7 +356,11 @@ int oracle_attend(const oracle_problem *P, const int64_t *rows, int64_t nrows, d
             const double vs =
                 P->kv_type == ORC_E4M3 ? (double)P->v_scale[kv_row(P, P->vs_stride, b, hkv, j)] : 1.0;
             l += w;
-            for (int64_t d = 0; d < P->dim_v; d++) o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);
+            for (int64_t d = 0; d < P->dim_v; d++) {
+                const double vd = P->kv_type == ORC_INT4 ? int4_value(P->v, vo, d, P->dim_v, P->n_groups)
+                                                         : widen(P->v, P->kv_type, vo + d) * vs;
+                o[d] += w * vd;
+            }
         }
         for (int64_t d = 0; d < P->dim_v; d++) o[d] /= l;
         lse[i] = m + log(l);

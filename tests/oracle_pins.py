@@ -599,6 +599,73 @@ def pin_varlen_equals_separate(orc):
     _close(out[2:], ref[0], what="offset start out")
 
 
+# ------------------------------------------------------------------ int4 cache
+def _int4_rows(g, rows_shape, D, n_groups):
+    """Random 4-bit fields, fp16 scales and shifts per (row, group), the packed int32 rows built
+    from them with numpy bit operations, and the dequantised values computed from the fields
+    directly (field * scale + shift in fp64)."""
+    n = torch.randint(0, 16, (*rows_shape, D), generator=g)
+    sc = (torch.rand(*rows_shape, n_groups, generator=g) * 0.2 + 1e-3).to(torch.float16)
+    sh = (torch.randn(*rows_shape, n_groups, generator=g)).to(torch.float16)
+    sc.view(-1)[0] = torch.tensor(3e-6, dtype=torch.float16)  # a subnormal half scale
+    gs = D // n_groups
+    deq = n.double() * sc.double().repeat_interleave(gs, -1) + sh.double().repeat_interleave(gs, -1)
+    nn = n.numpy().astype(np.uint32).reshape(-1, D // 8, 8)
+    packed = np.zeros(nn.shape[:2], dtype=np.uint32)
+    for j in range(8):
+        packed |= nn[:, :, j] << np.uint32(4 * j)
+    coef = (sc.view(torch.int16).numpy().astype(np.uint32) & 0xFFFF) | \
+           ((sh.view(torch.int16).numpy().astype(np.uint32) & 0xFFFF) << 16)
+    words = np.concatenate([coef.reshape(-1, n_groups), packed], axis=1)
+    t = torch.from_numpy(words.view(np.int32).copy()).reshape(*rows_shape, n_groups + D // 8)
+    return t, deq
+
+
+def pin_int4_library(orc):
+    """Attention over packed int4 rows (1, 2, 4 and 8 groups; a subnormal half scale) equals fp64
+    SDPA over the values computed from the fields; the paged layout gives the same bits."""
+    g = _gen(41)
+    B, Q, Hq, Hkv, D, L, P = 2, 2, 4, 2, 64, 21, 8
+    lens = torch.tensor([21, 13], dtype=torch.int32)
+    q = _randn(g, B, Q, Hq, D)
+    for ng in (1, 2, 4, 8):
+        kw, kd = _int4_rows(g, (B, Hkv, L), D, ng)
+        vw, vd = _int4_rows(g, (B, Hkv, L), D, ng)
+        k, v = kw.permute(0, 2, 1, 3), vw.permute(0, 2, 1, 3)
+        out, lse = orc.attend(q, k, v, scale=0.3, seq_lens=lens, causal=True, int4_groups=ng)
+        ref_o, ref_l = _sdpa(q, kd.permute(0, 2, 1, 3), vd.permute(0, 2, 1, 3), 0.3,
+                             _library_mask(B, Q, L, lens, True, 0))
+        _close(out, ref_o, what=f"int4 out groups={ng}")
+        _close(lse, ref_l, what=f"int4 lse groups={ng}")
+        # paged: page p of sequence b is pool page perm[b*npg + p]
+        npg = (L + P - 1) // P
+        perm = torch.randperm(B * npg, generator=g)
+        pool_k = torch.zeros(B * npg, Hkv, P, ng + D // 8, dtype=torch.int32)
+        pool_v = torch.zeros_like(pool_k)
+        kp = torch.nn.functional.pad(kw, (0, 0, 0, npg * P - L))
+        vp = torch.nn.functional.pad(vw, (0, 0, 0, npg * P - L))
+        for b in range(B):
+            for pg in range(npg):
+                pool_k[perm[b * npg + pg]] = kp[b, :, pg * P:(pg + 1) * P]
+                pool_v[perm[b * npg + pg]] = vp[b, :, pg * P:(pg + 1) * P]
+        bt = perm.reshape(B, npg).to(torch.int32)
+        o2, l2 = orc.attend(q, pool_k.permute(0, 2, 1, 3), pool_v.permute(0, 2, 1, 3), scale=0.3, seq_lens=lens,
+                            causal=True, block_table=bt, page_size=P, int4_groups=ng)
+        assert np.array_equal(out, o2) and np.array_equal(lse, l2), f"paged int4 != contiguous, groups={ng}"
+
+
+def pin_int4_one_key(orc):
+    """One visible key: the output is that key's value row, field * scale + shift, exactly."""
+    g = _gen(42)
+    D = 64
+    for ng in (1, 8):
+        kw, _ = _int4_rows(g, (1, 1, 1), D, ng)
+        vw, vd = _int4_rows(g, (1, 1, 1), D, ng)
+        q = _randn(g, 1, 1, 1, D)
+        out, lse = orc.attend(q, kw.permute(0, 2, 1, 3), vw.permute(0, 2, 1, 3), scale=1.0, int4_groups=ng)
+        assert np.array_equal(out.reshape(-1), vd.reshape(-1).numpy()), f"one key, groups={ng}"
+
+
 ALL_PINS = [
     pin_library_attention, pin_library_causal_window, pin_library_block_list, pin_golden_visibility,
     pin_one_visible_key, pin_identical_keys, pin_constant_values, pin_large_logits, pin_empty_rows,
@@ -606,6 +673,7 @@ ALL_PINS = [
     pin_merge_closed_form, pin_merge_identities, pin_split_then_merge, pin_key_order_invariance,
     pin_e4m3_decode_library, pin_e4m3_closed_forms, pin_fp8_equals_dequantised, pin_fp8_paged_and_broadcast,
     pin_tree_mask_library, pin_tree_chain_is_causal, pin_varlen_equals_separate,
+    pin_int4_library, pin_int4_one_key,
 ]
 
 

@@ -33,6 +33,14 @@ MUTANTS = [
     ("tree first draft", "const int64_t first_draft = L - q_tokens(P, b);", "const int64_t first_draft = L - P->q_len;"),
     ("tree row pitch", "q_row(P, b, t) * words + i / 32", "q_row(P, b, t) + i / 32"),
     ("tree prefix bound", "if (j < first_draft) return 1;", "if (j <= first_draft) return 1;"),
+    ("int4 field order", ">> (4 * (d % 8))) & 15u;", ">> (4 * (7 - d % 8))) & 15u;"),
+    ("int4 scale and shift swapped", "(double)field * half_value(coef & 0xFFFFu) + half_value(coef >> 16)",
+     "(double)field * half_value(coef >> 16) + half_value(coef & 0xFFFFu)"),
+    ("int4 group of a dimension", "const uint32_t coef = w[d / (dim / n_groups)];",
+     "const uint32_t coef = w[d % n_groups];"),
+    ("int4 values after the coefficients", "(w[n_groups + d / 8] >>", "(w[d / 8] >>"),
+    ("half exponent bias", "mag = ldexp(1.0 + m / 1024.0, e - 15);", "mag = ldexp(1.0 + m / 1024.0, e - 14);"),
+    ("half subnormal scale", "mag = ldexp((double)m, -24);", "mag = ldexp((double)m, -25);"),
     ("second score part dropped",
      "acc += widen(P->q2, P->q_type, qo2 + d) * widen(P->k2, P->kv_type, ko2 + d);", "acc += 0.0;"),
     ("scale dropped", "return P->scale * acc;", "return acc;"),
@@ -42,8 +50,8 @@ MUTANTS = [
     ("page slot index", "(j % P->page_size) * st[1]", "(j / P->page_size) * st[1]"),
     ("page table index", "P->block_table[b * P->bt_stride + j / P->page_size]",
      "P->block_table[b * P->bt_stride + j % P->page_size]"),
-    ("values read from keys", "o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);",
-     "o[d] += w * (widen(P->k, P->kv_type, vo + d) * vs);"),
+    ("values read from keys", ": widen(P->v, P->kv_type, vo + d) * vs;",
+     ": widen(P->k, P->kv_type, vo + d) * vs;"),
     ("bf16 widening", "<< 16;", "<< 15;"),
     ("block id off by one", "+ i * P->idx_stride[2]] == blk)", "+ i * P->idx_stride[2]] == blk + 1)"),
     ("block of key", "int64_t blk = j / P->block_size;", "int64_t blk = j % P->block_size;"),
@@ -61,11 +69,13 @@ MUTANTS = [
     ("e4m3 exponent bias", "mag = ldexp(1.0 + m / 8.0, e - 7);", "mag = ldexp(1.0 + m / 8.0, e - 8);"),
     ("e4m3 subnormal scale", "mag = ldexp((double)m, -9);", "mag = ldexp((double)m, -10);"),
     ("e4m3 mantissa step", "1.0 + m / 8.0", "1.0 + m / 16.0"),
-    ("e4m3 sign dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e4m3 sign dropped", "        mag = ldexp(1.0 + m / 8.0, e - 7);\n    return sign ? -mag : mag;",
+     "        mag = ldexp(1.0 + m / 8.0, e - 7);\n    return mag;"),
+    ("half sign dropped", "        mag = ldexp(1.0 + m / 1024.0, e - 15);\n    return sign ? -mag : mag;",
+     "        mag = ldexp(1.0 + m / 1024.0, e - 15);\n    return mag;"),
     ("e4m3 nan code", "if (e == 15 && m == 7)", "if (e == 15)"),
-    ("key scale dropped", "* (widen(P->k, P->kv_type, ko + d) * ks);", "* widen(P->k, P->kv_type, ko + d);"),
-    ("value scale dropped", "o[d] += w * (widen(P->v, P->kv_type, vo + d) * vs);",
-     "o[d] += w * widen(P->v, P->kv_type, vo + d);"),
+    ("key scale dropped", ": widen(P->k, P->kv_type, ko + d) * ks;", ": widen(P->k, P->kv_type, ko + d);"),
+    ("value scale dropped", ": widen(P->v, P->kv_type, vo + d) * vs;", ": widen(P->v, P->kv_type, vo + d);"),
     ("key scale from value scales", "(double)P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)]",
      "(double)P->v_scale[kv_row(P, P->ks_stride, b, hkv, j)]"),
     ("key scale strides", "P->k_scale[kv_row(P, P->ks_stride, b, hkv, j)]",
