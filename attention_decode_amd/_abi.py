@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(HERE, "libattn_decode.so")
 
 AD_F32, AD_BF16 = 0, 1
-AD_KV_SAME, AD_KV_FP8_E4M3 = 0, 1
+AD_KV_SAME, AD_KV_FP8_E4M3, AD_KV_INT4 = 0, 1, 2
 AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA = 0, 1, 2
 AD_MAX_SPLITS = 256
 STATUS = {0: "AD_OK", -1: "AD_E_NULL", -2: "AD_E_DTYPE", -3: "AD_E_SHAPE", -4: "AD_E_ALIGN",
@@ -43,6 +43,7 @@ class DecodeArgs(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("k_scale_stride", I64x3),
         ("v_scale", ctypes.c_void_p), ("v_scale_stride", I64x3),
         ("q_starts", ctypes.c_void_p), ("tree_mask", ctypes.c_void_p),
+        ("kv_groups", ctypes.c_int32),
     ]
 
 
@@ -132,7 +133,9 @@ def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, w
     """Fill an ad_decode_args from tensors (q [B,Q,Hq,D]; k/v token-major 4-D views). uint8 k / v
     are an E4M3 cache, with k_scale / v_scale fp32 3-D views indexed like the cache rows.
     Variable query lengths: q_starts int32 [B + 1] with q (and out) packed [tokens, Hq, D] and
-    q_len the largest per-sequence count. tree_mask: int32 [token rows, ceil(q_len / 32)]."""
+    q_len the largest per-sequence count. tree_mask: int32 [token rows, ceil(q_len / 32)].
+    int32 k / v are an int4 cache: rows of n_groups coefficient words then D / 8 packed words
+    (n_groups is read off the row length)."""
     a = DecodeArgs()
     if q.dtype not in _DTYPE:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -150,6 +153,10 @@ def make_args(q, k, v, *, scale, seq_lens=None, kv_len_max=None, causal=False, w
     a.num_kv_heads = k.shape[2]
     a.head_dim_qk = q.shape[3] if head_dim_qk is None else head_dim_qk
     a.head_dim_v = (v if v is not None else k).shape[3]
+    if k.dtype == torch.int32:
+        a.kv_format = AD_KV_INT4
+        a.kv_groups = k.shape[3] - q.shape[3] // 8
+        a.head_dim_v = q.shape[3]
     a.scale = float(scale)
     a.q, a.q_stride = _ptr(q), _s3(q)
     a.k, a.k_stride = _ptr(k), _s3(k)

@@ -57,6 +57,9 @@ struct PartialParams {
     int64_t ks_s[3];
     const float *v_scale;
     int64_t vs_s[3];
+    // Int4 cache: k / v rows of 32-bit words (k_s / v_s count words), kv_groups coefficient words
+    // (fp16 scale low, fp16 shift high) then D / 8 words of 4-bit fields.
+    int32_t kv_int4, kv_groups;
     // Speculative decoding: packed query rows of variable count per sequence (q_starts, nullable)
     // and a tree mask over each sequence's last Q_b keys, mask_words 32-bit words per token row.
     const int32_t *q_starts;

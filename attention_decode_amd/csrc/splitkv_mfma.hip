@@ -531,6 +531,7 @@ hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream) {
+    if (p.kv_int4) return hipErrorInvalidValue;  // int4 caches run on the vector kernel only
     if (p.kv_fp8) {  // the host admits an fp8 cache with head dim 128 only
         if (head_dim != 128) return hipErrorInvalidValue;
         return by_mode<128, true>(p, mode, stream);

@@ -106,16 +106,22 @@ __device__ __forceinline__ bf16x2 e4m3_pair(uint32_t w) {
 
 // FP8: k and v hold OCP E4M3 bytes with fp32 row scales (bf16 queries); K / V elements are then
 // bytes, each lane still owns 16 of a row, and its query values for them are two 16-B words.
-template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8>
+// INT4: k and v hold rows of 32-bit words, kv_groups coefficient words (fp16 scale low, fp16 shift
+// high) and then D / 8 words of 4-bit fields (field d % 8 of word d / 8); each lane owns 16
+// consecutive dimensions (two value words and its group's coefficient word), dequantises them
+// exactly in fp32 and runs the fp32 arithmetic (bf16 queries widened once).
+template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8, bool INT4>
 __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
     constexpr bool kBf16 = sizeof(T) == 2;
-    static_assert(!FP8 || kBf16, "an fp8 cache is read with bf16 queries");
-    using KV = std::conditional_t<FP8, uint8_t, T>;           // one K / V element
-    constexpr int kPer16 = 16 / (int)sizeof(KV);              // K / V elements per 16-B piece
-    constexpr int kSlots = 64 / LPT;                          // rows per wave-wide load
-    constexpr int kPieces = D * (int)sizeof(KV) / (16 * LPT);  // 16-B pieces per lane per row
-    constexpr int kEPL = kPieces * kPer16;                    // elements per lane per row
-    constexpr int kQv = FP8 ? 2 * kPieces : kPieces;          // 16-B query words per lane per row
+    static_assert(!(FP8 || INT4) || kBf16, "a quantised cache is read with bf16 queries");
+    static_assert(!INT4 || (D == 128 && LPT == 8), "the int4 lane map: 8 lanes x 16 dimensions per row");
+    using KV = std::conditional_t<FP8, uint8_t, std::conditional_t<INT4, uint32_t, T>>;  // one K / V element
+    constexpr bool kF32Math = !kBf16 || INT4;                  // fp32 products and unrounded P
+    constexpr int kPer16 = INT4 ? 16 : 16 / (int)sizeof(KV);   // K / V elements per 16-B piece (int4: per lane)
+    constexpr int kSlots = 64 / LPT;                           // rows per wave-wide load
+    constexpr int kPieces = INT4 ? 1 : D * (int)sizeof(KV) / (16 * LPT);  // 16-B pieces per lane per row
+    constexpr int kEPL = kPieces * kPer16;                     // elements per lane per row
+    constexpr int kQv = (FP8 || INT4) ? 2 * kPieces : kPieces;  // 16-B query words per lane per row
     constexpr int kStep = kSlots * U;                         // keys per wave per step
     static_assert(kPieces >= 1, "row too short for the lanes sharing it");
     static_assert(MODE == KV_CONTIG || (kStep <= 16 && 16 % kStep == 0),
@@ -217,7 +223,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
             for (int i = 0; i < kPieces; ++i) {
                 const T *src = qr + (i * LPT + c) * kPer16;  // the lane's elements of piece i
-                if constexpr (FP8) {
+                if constexpr (FP8 || INT4) {
                     qv[r][2 * i] = ld16(src);
                     qv[r][2 * i + 1] = ld16(src + 8);
                 } else {
@@ -226,8 +232,16 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
             }
         }
     }
-    float qf[kBf16 ? 1 : RP][kBf16 ? 1 : kEPL];  // fp32 queries, prescaled by scale*log2(e)
-    if constexpr (!kBf16) {
+    float qf[kF32Math ? RP : 1][kF32Math ? kEPL : 1];  // fp32 queries, prescaled by scale*log2(e)
+    if constexpr (INT4) {  // bf16 queries widened: element e of the lane's 16 is word e/2 of the pair
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int e = 0; e < kEPL; ++e) {
+                const uint32_t w = qv[r][e / 8][(e % 8) / 2];
+                qf[r][e] = __uint_as_float(e % 2 ? (w & 0xFFFF0000u) : (w << 16)) * p.scale_log2;
+            }
+    } else if constexpr (!kBf16) {
 #pragma unroll
         for (int r = 0; r < RP; ++r)
 #pragma unroll
@@ -255,6 +269,10 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     const KV *safe = reinterpret_cast<const KV *>(qbase);
     const int map_mask = (1 << map_shift) - 1;
     const int lane_piece = c * kPer16;
+    // int4: this lane's two value words and its group's coefficient word inside a row (a query
+    // row read instead is 64 words long, more than the largest offset, 8 + 15)
+    const int i4_vals = INT4 ? p.kv_groups + 2 * c : 0;
+    const int i4_coef = INT4 ? (16 * c) * p.kv_groups / D : 0;
 
     // l: row sum of the probabilities as multiplied into acc (the rounded P for bf16), the output
     // normaliser; lf: the same sum in full fp32, which gives the LSE.
@@ -322,11 +340,26 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 f.vs[u] = *(valid ? vsrow + off * p.vs_s[1] : p.v_scale);
             }
             f.val[u] = valid;
+            if constexpr (INT4) {  // dword loads: int4 rows are only 4-byte aligned
+                f.k[u][0] = u32x4{kp[i4_vals], kp[i4_vals + 1], kp[i4_coef], 0u};
+                f.v[u][0] = u32x4{vp[i4_vals], vp[i4_vals + 1], vp[i4_coef], 0u};
+            } else {
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) f.k[u][i] = ld16(kp + i * LPT * kPer16 + lane_piece);
+                for (int i = 0; i < kPieces; ++i) f.k[u][i] = ld16(kp + i * LPT * kPer16 + lane_piece);
 #pragma unroll
-            for (int i = 0; i < kPieces; ++i) f.v[u][i] = ld16(vp + i * LPT * kPer16 + lane_piece);
+                for (int i = 0; i < kPieces; ++i) f.v[u][i] = ld16(vp + i * LPT * kPer16 + lane_piece);
+            }
         }
+    };
+
+    // int4: the 16 values of a lane's two value words w.x, w.y with coefficient word w.z, exactly
+    // (a 4-bit field times an fp16 scale is exact in fp32; the shift is added with one rounding)
+    auto int4_values = [&](const u32x4 &w, float (&x)[16]) {
+        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[2] & 0xFFFFu));
+        const float sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[2] >> 16));
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            x[e] = fmaf((float)((w[e / 8] >> (4 * (e % 8))) & 15u), sc, sh);
     };
 
     // Arithmetic of one step on its loaded K and V.
@@ -335,6 +368,8 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         float sc[U][RP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
+            float kq[INT4 ? 16 : 1];  // int4 cache: the key's 16 values of this lane, once per key
+            if constexpr (INT4) int4_values(cur.k[u][0], kq);
             bf16x2 kp8[FP8 ? kPieces : 1][8];  // fp8 cache: the keys' bytes as bf16 pairs, once per key
             if constexpr (FP8) {
 #pragma unroll
@@ -355,6 +390,9 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             d = dot2(as_bf16x2(qv[r][2 * i + e / 4][e % 4]), kp8[i][e], d);
+                } else if constexpr (INT4) {
+#pragma unroll
+                    for (int e = 0; e < kEPL; ++e) d = fmaf(qf[r][e], kq[e], d);
                 } else if constexpr (kBf16) {
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
@@ -369,7 +407,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 d = slot_sum<LPT>(d);
                 if constexpr (FP8)
                     d *= p.scale_log2 * (cur.val[u] ? cur.ks[u] : 0.f);
-                else if constexpr (kBf16)
+                else if constexpr (kBf16 && !INT4)
                     d *= p.scale_log2;
                 if constexpr (kMasked) {
                     const int pos = cur.pos0 + u * kSlots + slot;
@@ -455,6 +493,23 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                             o[3] = dot2(pk[r], v3, o[3]);
                         }
                     }
+                }
+            }
+        } else if constexpr (INT4) {
+            // fp32 P.V with the unrounded P; a key that was not read has all its words zeroed
+            // (scale and shift 0) so that the query row it read cannot reach the sums
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                u32x4 w = cur.v[u][0];
+                if constexpr (kMasked) w = cur.val[u] ? w : u32x4{0u, 0u, 0u, 0u};
+                float vq[16];
+                int4_values(w, vq);
+#pragma unroll
+                for (int r = 0; r < RP; ++r) {
+                    l[r] += sc[u][r];
+                    lf[r] += sc[u][r];
+#pragma unroll
+                    for (int e = 0; e < kEPL; ++e) acc[r][e] = fmaf(sc[u][r], vq[e], acc[r][e]);
                 }
             }
         } else if constexpr (kBf16) {
@@ -587,36 +642,37 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     }
 }
 
-template <typename T, int D, int RP, int MODE, bool FP8>
+template <typename T, int D, int RP, int MODE, bool FP8, bool INT4>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int kRowLanes = D * (FP8 ? 1 : (int)sizeof(T)) / 16;
     constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
     constexpr int U = AD_VALU_KEYS_PER_SLOT;
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
-    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8>), grid, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8, INT4>), grid, dim3(kThreads), 0, stream,
+                       p);
     return hipGetLastError();
 }
 
-template <typename T, int D, int RP, bool FP8>
+template <typename T, int D, int RP, bool FP8, bool INT4>
 hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
     switch (mode) {
-        case KV_CONTIG: return launch_t<T, D, RP, KV_CONTIG, FP8>(p, s);
-        case KV_PAGED: return launch_t<T, D, RP, KV_PAGED, FP8>(p, s);
-        default: return launch_t<T, D, RP, KV_SPARSE, FP8>(p, s);
+        case KV_CONTIG: return launch_t<T, D, RP, KV_CONTIG, FP8, INT4>(p, s);
+        case KV_PAGED: return launch_t<T, D, RP, KV_PAGED, FP8, INT4>(p, s);
+        default: return launch_t<T, D, RP, KV_SPARSE, FP8, INT4>(p, s);
     }
 }
 
-// An fp8 unit holds at most 4 rows (the host plans so): 8 rows would need more registers than a
-// lane has, and those instantiations are not built.
-template <typename T, int D, bool FP8 = false>
+// An fp8 or int4 unit holds at most 4 rows (the host plans so): 8 rows would need more registers
+// than a lane has, and those instantiations are not built.
+template <typename T, int D, bool FP8 = false, bool INT4 = false>
 hipError_t by_rows(const PartialParams &p, int rows_padded, int mode, hipStream_t s) {
-    constexpr int kMaxRows = FP8 ? 4 : 8;
+    constexpr int kMaxRows = (FP8 || INT4) ? 4 : 8;
     if (rows_padded > kMaxRows) return hipErrorInvalidValue;
     switch (rows_padded) {
-        case 1: return by_mode<T, D, 1, FP8>(p, mode, s);
-        case 2: return by_mode<T, D, 2, FP8>(p, mode, s);
-        case 4: return by_mode<T, D, 4, FP8>(p, mode, s);
-        default: return by_mode<T, D, kMaxRows, FP8>(p, mode, s);
+        case 1: return by_mode<T, D, 1, FP8, INT4>(p, mode, s);
+        case 2: return by_mode<T, D, 2, FP8, INT4>(p, mode, s);
+        case 4: return by_mode<T, D, 4, FP8, INT4>(p, mode, s);
+        default: return by_mode<T, D, kMaxRows, FP8, INT4>(p, mode, s);
     }
 }
 
@@ -627,6 +683,10 @@ hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, 
     if (p.kv_fp8) {  // the host admits an fp8 cache with bf16 queries and head dim 128 only
         if (dtype != DT_BF16 || head_dim != 128) return hipErrorInvalidValue;
         return by_rows<uint16_t, 128, true>(p, rows_padded, mode, stream);
+    }
+    if (p.kv_int4) {  // likewise for an int4 cache
+        if (dtype != DT_BF16 || head_dim != 128) return hipErrorInvalidValue;
+        return by_rows<uint16_t, 128, false, true>(p, rows_padded, mode, stream);
     }
     if (dtype == DT_F32) {
         return head_dim == 64 ? by_rows<float, 64>(p, rows_padded, mode, stream)

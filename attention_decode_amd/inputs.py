@@ -23,6 +23,8 @@ The workloads (sizes of the decode benchmarks this library is measured on; 6 is 
    [128, 8192], page 16, 32 q / 8 KV heads, D=128, bf16), each with 1 to 8 draft tokens (uniform)
    as packed variable-length queries, and a random token tree per sequence as the tree mask
    (token t sees itself and its ancestors among the drafts).
+8. workload 3 with its cache quantised to int4: every K and V row one group of 128 4-bit fields
+   with an fp16 scale and shift (mslk's row-wise int4 layout), from the same values.
 
 Cache layouts: a contiguous cache is stored head-major ``[B, Hkv, L, D]``; a paged pool is stored
 ``[pages, Hkv, page_size, D]``. Both are handed out as token-major *views* ``[B, L, Hkv, D]`` /
@@ -36,7 +38,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-NUM_CONFIGS = 7
+NUM_CONFIGS = 8
 
 
 @dataclass
@@ -73,7 +75,8 @@ class Workload:
     # quantised cache: "fp8" = k / v hold OCP E4M3 bytes, with fp32 row scales (views indexed like
     # the cache rows: [B, L, Hkv] contiguous, [pages, page, Hkv] paged; zero strides for one scale
     # per tensor)
-    kv_format: str = "same"
+    kv_format: str = "same"   # "same" | "fp8" | "int4"
+    kv_groups: int = 0        # int4: coefficient groups per row
     k_scale: torch.Tensor | None = None
     v_scale: torch.Tensor | None = None
     # speculative decoding: packed variable-length queries (q is then [tokens, Hq, D] and q_len
@@ -129,6 +132,8 @@ class Workload:
     def bytes_per_key(self) -> int:
         """Bytes one key costs per KV head: its K and V rows (MLA: ckv + kpe once), plus its two
         fp32 row scales when an fp8 cache has one scale per row."""
+        if self.kv_format == "int4":  # K and V rows of kv_groups + D / 8 words
+            return 4 * (2 * self.kv_groups + (self.head_dim_qk + self.head_dim_v) // 8)
         es = 1 if self.kv_format == "fp8" else torch.finfo(self.dtype).bits // 8
         if self.kind == "mla":
             return self.head_dim_qk * es
@@ -196,11 +201,39 @@ def quantize_e4m3(x: torch.Tensor, per: str):
     return q.to(torch.float8_e4m3fn).view(torch.uint8), scale.float().contiguous()
 
 
+INT4_POISON = 0x7E007E00  # a word whose halves are both fp16 NaN (a coefficient word of NaN)
+
+
+def quantize_int4(x: torch.Tensor, groups: int) -> torch.Tensor:
+    """Input preparation for an int4 cache: every row of the last dimension D is split into
+    `groups` groups; per group the shift is the minimum and the scale (max - min) / 15, both
+    rounded to fp16, and each value becomes the nearest field in 0..15 of
+    (x - shift) / scale. Returns int32 words [..., groups + D / 8]: the coefficient words (fp16
+    scale in the low half, shift in the high half), then the fields, field d % 8 of word d / 8."""
+    x = x.float()
+    D = x.shape[-1]
+    xg = x.reshape(*x.shape[:-1], groups, D // groups)
+    lo, hi = xg.amin(dim=-1), xg.amax(dim=-1)
+    shift = lo.to(torch.float16)
+    scale = ((hi - lo) / 15.0).to(torch.float16)
+    safe = torch.where(scale.float() > 0, scale.float(), torch.ones_like(scale.float()))
+    f = torch.round((xg - shift.float()[..., None]) / safe[..., None]).clamp(0, 15).to(torch.int64)
+    f = torch.where((scale.float() > 0)[..., None], f, torch.zeros_like(f)).reshape(*x.shape[:-1], D // 8, 8)
+    packed = torch.zeros(f.shape[:-1], dtype=torch.int64)
+    for j in range(8):
+        packed |= f[..., j] << (4 * j)
+    coef = (scale.view(torch.int16).to(torch.int64) & 0xFFFF) | ((shift.view(torch.int16).to(torch.int64) & 0xFFFF) << 16)
+    words = torch.cat([coef, packed], dim=-1)
+    return torch.where(words >= 2 ** 31, words - 2 ** 32, words).to(torch.int32)
+
+
 def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len,
                q_len=1, dtype=torch.bfloat16, scale=None, seq_lens=None, seed=0,
-               causal=False, window=0, num_splits=None, kv_format="same", kv_scales="token") -> Workload:
+               causal=False, window=0, num_splits=None, kv_format="same", kv_scales="token",
+               kv_groups=1) -> Workload:
     """Head-major contiguous cache [B, Hkv, L, D]; `seq_lens` (list) may be ragged (<= kv_len).
-    kv_format="fp8": K and V are quantised to E4M3 with row (kv_scales="token") or tensor scales."""
+    kv_format="fp8": K and V are quantised to E4M3 with row (kv_scales="token") or tensor scales;
+    kv_format="int4": to 4-bit fields with kv_groups fp16 scale / shift pairs per row."""
     g = torch.Generator().manual_seed(seed)
     q = _randn(g, (batch, q_len, num_q_heads, head_dim), dtype)
     k = _randn(g, (batch, num_kv_heads, kv_len, head_dim), dtype)
@@ -213,6 +246,9 @@ def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, hea
                  kv_len_max=kv_len, seq_lens=sl, q=None, k=None, v=None, causal=causal, window=window,
                  num_splits=num_splits, kv_format=kv_format)
     w.storage = {"q": q, "k": k, "v": v}
+    if kv_format == "int4":
+        w.kv_groups = kv_groups
+        w.storage["k"], w.storage["v"] = quantize_int4(k, kv_groups), quantize_int4(v, kv_groups)
     if kv_format == "fp8":
         w.storage["k"], w.storage["k_scale"] = quantize_e4m3(k, kv_scales)
         w.storage["v"], w.storage["v_scale"] = quantize_e4m3(v, kv_scales)
@@ -221,7 +257,8 @@ def contiguous(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, hea
 
 def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_dim, page_size,
           q_len=1, dtype=torch.bfloat16, scale=None, seed=0, poison=False, max_pages=None,
-          causal=False, window=0, shuffle_pages=True, kv_format="same", kv_scales="token") -> Workload:
+          causal=False, window=0, shuffle_pages=True, kv_format="same", kv_scales="token",
+          kv_groups=1) -> Workload:
     """Paged cache: pool [pages, Hkv, page_size, D] (head-major pages), block table [B, max_pages].
 
     The logical content of sequence b depends only on the seed and seq_lens; the physical page
@@ -264,6 +301,13 @@ def paged(*, config=0, name="custom", seq_lens, num_q_heads, num_kv_heads, head_
                  kv_len_max=mp * page_size, seq_lens=sl, q=None, k=None, v=None,
                  block_table=bt, page_size=page_size, causal=causal, window=window, kv_format=kv_format)
     w.storage = {"q": q, "k": k_pool, "v": v_pool}
+    if kv_format == "int4":
+        w.kv_groups = kv_groups
+        for name_, pool in (("k", k_pool), ("v", v_pool)):
+            live = ~torch.isnan(pool).any(dim=-1)                    # rows that hold a key
+            words = quantize_int4(torch.nan_to_num(pool), kv_groups)
+            words[~live] = INT4_POISON                                  # NaN coefficients where nothing belongs
+            w.storage[name_] = words
     if kv_format == "fp8":
         for name_, pool in (("k", k_pool), ("v", v_pool)):
             live = ~torch.isnan(pool).any(dim=-1)                    # rows that hold a key
@@ -286,7 +330,7 @@ def window_block_list(kv_len: int, q_len: int, window: int, block_size: int):
 
 def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_dim, kv_len, q_len,
            block_size, blocks, dtype=torch.bfloat16, scale=None, seed=0, causal=True, window=0,
-           poison=False, seq_lens=None, kv_format="same", kv_scales="token") -> Workload:
+           poison=False, seq_lens=None, kv_format="same", kv_scales="token", kv_groups=1) -> Workload:
     """Contiguous head-major cache with a per-(b, KV head) list of KV blocks: ``blocks`` is one list
     shared by every (b, KV head), or a nested list blocks[b][h] of lists of any lengths (the index
     array is padded with -1, which is never read). With ``poison`` every key outside the listed
@@ -294,7 +338,7 @@ def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_di
     w = contiguous(config=config, name=name, batch=batch, num_q_heads=num_q_heads,
                    num_kv_heads=num_kv_heads, head_dim=head_dim, kv_len=kv_len, q_len=q_len,
                    dtype=dtype, scale=scale, seed=seed, causal=causal, window=window, seq_lens=seq_lens,
-                   kv_format=kv_format, kv_scales=kv_scales)
+                   kv_format=kv_format, kv_scales=kv_scales, kv_groups=kv_groups)
     if blocks and isinstance(blocks[0], (list, tuple)):
         lists = [[list(blocks[b][h]) for h in range(num_kv_heads)] for b in range(batch)]
     else:
@@ -315,7 +359,9 @@ def sparse(*, config=0, name="custom", batch, num_q_heads, num_kv_heads, head_di
                     keep[blk * block_size:(blk + 1) * block_size] = True
                 keep[int(w.seq_lens[b]):] = False
                 for name_ in ("k", "v"):
-                    if w.kv_format == "fp8":  # the E4M3 NaN code, and NaN row scales
+                    if w.kv_format == "int4":  # NaN coefficients
+                        w.storage[name_][b, h, ~keep, :] = INT4_POISON
+                    elif w.kv_format == "fp8":  # the E4M3 NaN code, and NaN row scales
                         w.storage[name_][b, h, ~keep, :] = 0x7F
                         if w.storage[name_ + "_scale"].numel() > 1:
                             w.storage[name_ + "_scale"][b, h, ~keep] = float("nan")
@@ -440,6 +486,13 @@ def make(config: int, *, seed: int | None = None, poison: bool = False) -> Workl
         return paged(config=6, name="paged_gqa_fp8_ragged", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
                      head_dim=128, page_size=16, dtype=torch.bfloat16, seed=s3 + 1, poison=poison,
                      max_pages=512, kv_format="fp8", kv_scales="token")
+    if config == 8:  # workload 3's lengths and values, the cache quantised to int4, one group per row
+        s8 = 1003 if seed is None else seed
+        g = torch.Generator().manual_seed(s8)
+        lens = torch.randint(128, 8193, (64,), generator=g, dtype=torch.int64).tolist()
+        return paged(config=8, name="paged_gqa_int4_ragged", seq_lens=lens, num_q_heads=32, num_kv_heads=8,
+                     head_dim=128, page_size=16, dtype=torch.bfloat16, seed=s8 + 1, poison=poison,
+                     max_pages=512, kv_format="int4", kv_groups=1)
     if config == 7:  # workload 3's shape with 1-8 draft tokens per sequence and a token tree each
         s7 = 1007 if seed is None else seed
         g = torch.Generator().manual_seed(s7)

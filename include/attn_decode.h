@@ -58,6 +58,7 @@ extern "C" {
 /* Cache element formats (ad_decode_args.kv_format). */
 #define AD_KV_SAME 0     /* k and v hold `dtype` elements */
 #define AD_KV_FP8_E4M3 1 /* k and v hold OCP E4M3 bytes with fp32 row scales */
+#define AD_KV_INT4 2     /* k and v hold rows of 4-bit fields with fp16 scale / shift per group */
 
 #define AD_MAX_SPLITS 256
 
@@ -102,9 +103,9 @@ typedef struct ad_decode_args {
      * is dequantised as its decoded value times the fp32 scale of its row,
      * k_scale[b * k_scale_stride[0] + j * k_scale_stride[1] + h * k_scale_stride[2]] (paged:
      * page, slot, head), likewise for v. Zero strides broadcast; all zero is one scale per tensor,
-     * xqa's form. Supported on the vector path with bf16 q / out and head dim 128, any number of
-     * query rows per KV head (in blocks of at most 4); not with MLA. AD_KV_SAME (a zero-filled
-     * struct) ignores the rest. */
+     * xqa's form. Supported with bf16 q / out and head dim 128 on both partial kernels (the
+     * matrix-core kernel by default, the vector kernel in blocks of at most 4 rows); not with MLA.
+     * AD_KV_SAME (a zero-filled struct) ignores the rest. */
     int32_t kv_format;
     const float *k_scale;
     int64_t k_scale_stride[3];
@@ -130,6 +131,17 @@ typedef struct ad_decode_args {
      * and block lists. q_len <= 64 with a tree mask. Neither field is supported with MLA. */
     const int32_t *q_starts;
     const uint32_t *tree_mask;
+    /* Int4 cache (mslk splitk_kernels.py, the int4 path of dequantize /
+     * _process_int4_quantization). With AD_KV_INT4, every K (V) row is kv_groups + D/8 32-bit
+     * words: kv_groups coefficient words, each an fp16 scale in its low half and an fp16 shift in
+     * its high half, then the packed values, dimension d being the unsigned 4-bit field d % 8
+     * (bits 4*(d % 8) upwards) of packed word d / 8. Dimension d belongs to group
+     * d / (D / kv_groups) and its value is field * scale + shift. k / v point at those words
+     * (4-byte aligned) and their strides count words. kv_groups is 1, 2, 4 or 8; head dim 128
+     * (qk == v), bf16 q / out; not with MLA. Runs on the vector path in units of at most 4 rows,
+     * in fp32 arithmetic. Ignored unless kv_format == AD_KV_INT4. This path is switched off in
+     * this build: arguments are validated as described, then every call returns AD_E_UNSUPPORTED. */
+    int32_t kv_groups;
 } ad_decode_args;
 
 /* Paged cache: logical page p of sequence b is pool page block_table[b * bt_stride + p]

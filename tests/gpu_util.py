@@ -27,6 +27,8 @@ def oracle_of(orc, w, rows=None, key_range=None):
               key_range=key_range)
     if w.kv_format == "fp8":
         kw.update(k_scale=w.k_scale, v_scale=w.v_scale)
+    if w.kv_format == "int4":
+        kw.update(int4_groups=w.kv_groups)
     if w.q_starts is not None:
         kw.update(q_starts=w.q_starts, q_len=w.q_len)
     if w.tree_mask is not None:

@@ -409,3 +409,28 @@ def test_spec_decoding_rejections():
     assert _abi.lib().attn_decode_kernel(ctypes.byref(m), ctypes.byref(ctypes.c_int32())) == -5
     m = _abi.make_args(qm[None], ckv, None, head_dim_qk=576, scale=0.1, tree_mask=mask)
     assert _abi.lib().attn_decode_kernel(ctypes.byref(m), ctypes.byref(ctypes.c_int32())) == -5
+
+
+def test_int4_cache_rejections():
+    """An int4 cache: bf16 queries, head dim 128, kv_groups 1/2/4/8, 4-byte aligned rows, not with
+    MLA. The path is switched off: arguments that pass every check get AD_E_UNSUPPORTED."""
+    q, _, _, out = _tensors()
+    kw = torch.zeros(2, 2, 64, 17, dtype=torch.int32).permute(0, 2, 1, 3)
+    a = _abi.make_args(q, kw, kw, scale=0.1, out=out)
+    assert a.kv_format == _abi.AD_KV_INT4 and a.kv_groups == 1 and a.head_dim_v == 128
+
+    def kind(args):
+        return _abi.lib().attn_decode_kernel(ctypes.byref(args), ctypes.byref(ctypes.c_int32()))
+
+    assert kind(a) == -5 and "switched off" in _abi.attn_decode_last_error()
+    b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
+    b.kv_groups = 3
+    assert kind(b) == -7
+    b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
+    b.k = b.k + 2
+    assert kind(b) == -4
+    q32, _, _, out32 = _tensors(dtype=torch.float32)
+    assert kind(_abi.make_args(q32, kw, kw, scale=0.1, out=out32)) == -5
+    b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
+    b.head_dim_qk = b.head_dim_v = 64
+    assert kind(b) == -5
