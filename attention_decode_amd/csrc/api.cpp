@@ -290,6 +290,7 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
         p.kv_groups = a->kv_groups;
     }
     if (a->kv_format == AD_KV_FP8_E4M3) {
+        p.kv_fp8 = 1;
         p.k_scale = a->k_scale;
         p.v_scale = a->v_scale;
         for (int i = 0; i < 3; ++i) {
@@ -301,6 +302,10 @@ ad::PartialParams base_params(const ad_decode_args *a, const Plan &pl) {
 }
 
 hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mode, hipStream_t stream) {
+    // The kernels pick their element format from these flags: a block that disagrees with the
+    // arguments would read a byte-strided cache as 16-bit elements, past the end of its allocation.
+    if ((a->kv_format == AD_KV_FP8_E4M3) != (p.kv_fp8 != 0) || (a->kv_format == AD_KV_INT4) != (p.kv_int4 != 0))
+        return hipErrorInvalidValue;
     const Rows rows = row_plan(a);
     p.row_blocks = rows.blocks;
     // one work group per (split, b, KV head, row block) on a 1-D grid
