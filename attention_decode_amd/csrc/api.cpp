@@ -64,8 +64,6 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ------------------------------------------------------------------ validation
 enum class Path { Contig, Paged, Mla };
 
-constexpr bool kInt4Enabled = false;
-
 int check_args(const ad_decode_args *a, Path path, bool need_out) {
     if (!a) return fail(AD_E_NULL, "args is NULL");
     if (a->dtype != AD_F32 && a->dtype != AD_BF16) return fail(AD_E_DTYPE, "dtype %d is not AD_F32 or AD_BF16", a->dtype);
@@ -124,11 +122,6 @@ int check_args(const ad_decode_args *a, Path path, bool need_out) {
     if (!strides_aligned(a->q_stride, es) ||
         (!int4 && (!strides_aligned(a->k_stride, kv_es) || (a->v && !strides_aligned(a->v_stride, kv_es)))))
         return fail(AD_E_ALIGN, "q/k/v strides must keep every row 16-byte aligned");
-    // The int4 cache path is switched off: a run that included its GPU tests ended with a GPU
-    // fault whose cause was not found in the code (its loads were checked in bounds on the host
-    // for every test workload). The arguments are still validated as above.
-    if (int4 && !kInt4Enabled)
-        return fail(AD_E_UNSUPPORTED, "the int4 cache path is switched off in this build");
     if (need_out) {
         if (!a->out) return fail(AD_E_NULL, "out is NULL");
         if (!aligned16(a->out) || !strides_aligned(a->out_stride, es))

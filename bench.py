@@ -46,6 +46,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
     6: ("partial_mfma_paged_fp8", "partial_mfma_kernel, fp8 cache + merge_kernel (two launches per step)"),
     7: ("partial_mfma_paged_spec", "partial_mfma_kernel, draft trees + merge_kernel (two launches per step)"),
+    8: ("partial_valu_paged_int4", "partial_valu_kernel, int4 cache + merge_kernel (two launches per step)"),
 }
 
 

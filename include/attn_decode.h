@@ -139,8 +139,7 @@ typedef struct ad_decode_args {
      * d / (D / kv_groups) and its value is field * scale + shift. k / v point at those words
      * (4-byte aligned) and their strides count words. kv_groups is 1, 2, 4 or 8; head dim 128
      * (qk == v), bf16 q / out; not with MLA. Runs on the vector path in units of at most 4 rows,
-     * in fp32 arithmetic. Ignored unless kv_format == AD_KV_INT4. This path is switched off in
-     * this build: arguments are validated as described, then every call returns AD_E_UNSUPPORTED. */
+     * in fp32 arithmetic. Ignored unless kv_format == AD_KV_INT4. */
     int32_t kv_groups;
 } ad_decode_args;
 

@@ -411,9 +411,9 @@ def test_spec_decoding_rejections():
     assert _abi.lib().attn_decode_kernel(ctypes.byref(m), ctypes.byref(ctypes.c_int32())) == -5
 
 
-def test_int4_cache_rejections():
+def test_int4_cache_rejections(monkeypatch):
     """An int4 cache: bf16 queries, head dim 128, kv_groups 1/2/4/8, 4-byte aligned rows, not with
-    MLA. The path is switched off: arguments that pass every check get AD_E_UNSUPPORTED."""
+    MLA, always the vector kernel."""
     q, _, _, out = _tensors()
     kw = torch.zeros(2, 2, 64, 17, dtype=torch.int32).permute(0, 2, 1, 3)
     a = _abi.make_args(q, kw, kw, scale=0.1, out=out)
@@ -422,13 +422,19 @@ def test_int4_cache_rejections():
     def kind(args):
         return _abi.lib().attn_decode_kernel(ctypes.byref(args), ctypes.byref(ctypes.c_int32()))
 
-    assert kind(a) == -5 and "switched off" in _abi.attn_decode_last_error()
+    assert kind(a) == 0 and ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    monkeypatch.delenv("AD_PARTIAL_KERNEL")
     b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
     b.kv_groups = 3
     assert kind(b) == -7
     b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
     b.k = b.k + 2
     assert kind(b) == -4
+    b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
+    b.k_stride[1] = 17  # any word stride is fine for int4 rows
+    assert kind(b) == 0
     q32, _, _, out32 = _tensors(dtype=torch.float32)
     assert kind(_abi.make_args(q32, kw, kw, scale=0.1, out=out32)) == -5
     b = _abi.make_args(q, kw, kw, scale=0.1, out=out)

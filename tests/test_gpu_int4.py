@@ -10,8 +10,6 @@ from attention_decode_amd.step import DecodeStep
 from gpu_util import assert_matches, gpu_available, oracle_of, say
 
 pytestmark = [pytest.mark.gpu,
-              pytest.mark.skip(reason="the int4 path is switched off: a run that included these tests ended "
-                                      "with a GPU fault whose cause was not found in the code"),
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
 
