@@ -106,17 +106,20 @@ __device__ __forceinline__ bf16x2 e4m3_pair(uint32_t w) {
 
 // FP8: k and v hold OCP E4M3 bytes with fp32 row scales (bf16 queries); K / V elements are then
 // bytes, each lane still owns 16 of a row, and its query values for them are two 16-B words.
-// INT4: k and v hold rows of 32-bit words, kv_groups coefficient words (fp16 scale low, fp16 shift
-// high) and then D / 8 words of 4-bit fields (field d % 8 of word d / 8); each lane owns 16
-// consecutive dimensions (two value words and its group's coefficient word), dequantises them
-// exactly in fp32 and runs the fp32 arithmetic (bf16 queries widened once).
+// INT4: k and v hold rows of 32-bit words, kv_groups coefficient words (fp16 scale s low, fp16
+// shift m high) and then D / 8 words of 4-bit fields f (field d % 8 of word d / 8); each lane owns
+// 16 consecutive dimensions, all in one group (two value words and the group's coefficient word).
+// q.k over them is s * sum q (128 + f) + (m - 128 s) * sum q: the fields become bf16 pairs
+// 128 + f by masking in an exponent (exact), multiplied with v_dot2 against the queries paired
+// the same way, and the per-row query sums fix the offset in fp32. P.V keeps P unrounded:
+// acc += (p s) f in fp32 with f converted from bytes, and p m is summed once per row and added
+// at the end.
 template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8, bool INT4>
-__global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
+__device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
     constexpr bool kBf16 = sizeof(T) == 2;
     static_assert(!(FP8 || INT4) || kBf16, "a quantised cache is read with bf16 queries");
     static_assert(!INT4 || (D == 128 && LPT == 8), "the int4 lane map: 8 lanes x 16 dimensions per row");
     using KV = std::conditional_t<FP8, uint8_t, std::conditional_t<INT4, uint32_t, T>>;  // one K / V element
-    constexpr bool kF32Math = !kBf16 || INT4;                  // fp32 products and unrounded P
     constexpr int kPer16 = INT4 ? 16 : 16 / (int)sizeof(KV);   // K / V elements per 16-B piece (int4: per lane)
     constexpr int kSlots = 64 / LPT;                           // rows per wave-wide load
     constexpr int kPieces = INT4 ? 1 : D * (int)sizeof(KV) / (16 * LPT);  // 16-B pieces per lane per row
@@ -126,7 +129,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     static_assert(kPieces >= 1, "row too short for the lanes sharing it");
     static_assert(MODE == KV_CONTIG || (kStep <= 16 && 16 % kStep == 0),
                   "a step must stay inside one page / listed block (both are >= 16 keys)");
-    static_assert(!kBf16 || U % 2 == 0, "bf16 P.V pairs keys");
+    static_assert(!kBf16 || INT4 || U % 2 == 0, "bf16 P.V pairs keys");
 
     const UnitId wu = decode_unit(p);
     const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
@@ -232,16 +235,27 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
             }
         }
     }
-    float qf[kF32Math ? RP : 1][kF32Math ? kEPL : 1];  // fp32 queries, prescaled by scale*log2(e)
-    if constexpr (INT4) {  // bf16 queries widened: element e of the lane's 16 is word e/2 of the pair
+    // int4: the lane's 16 query values as pairs (dim 8w + j, dim 8w + j + 4), the order in which
+    // the fields of packed word w come out two at a time, and their fp32 sum
+    bf16x2 qp[INT4 ? RP : 1][INT4 ? 8 : 1];
+    float qsum[INT4 ? RP : 1];
+    if constexpr (INT4) {
 #pragma unroll
-        for (int r = 0; r < RP; ++r)
+        for (int r = 0; r < RP; ++r) {
+            qsum[r] = 0.f;
 #pragma unroll
-            for (int e = 0; e < kEPL; ++e) {
-                const uint32_t w = qv[r][e / 8][(e % 8) / 2];
-                qf[r][e] = __uint_as_float(e % 2 ? (w & 0xFFFF0000u) : (w << 16)) * p.scale_log2;
-            }
-    } else if constexpr (!kBf16) {
+            for (int w = 0; w < 2; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t a = qv[r][w][j / 2], b = qv[r][w][2 + j / 2];  // dims j and j + 4
+                    const uint32_t pr = j % 2 ? ((a >> 16) | (b & 0xFFFF0000u)) : ((a & 0xFFFFu) | (b << 16));
+                    qp[r][4 * w + j] = as_bf16x2(pr);
+                    qsum[r] += __uint_as_float(pr << 16) + __uint_as_float(pr & 0xFFFF0000u);
+                }
+        }
+    }
+    float qf[kBf16 ? 1 : RP][kBf16 ? 1 : kEPL];  // fp32 queries, prescaled by scale*log2(e)
+    if constexpr (!kBf16) {
 #pragma unroll
         for (int r = 0; r < RP; ++r)
 #pragma unroll
@@ -276,12 +290,14 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 
     // l: row sum of the probabilities as multiplied into acc (the rounded P for bf16), the output
     // normaliser; lf: the same sum in full fp32, which gives the LSE.
-    float m[RP], l[RP], lf[RP], acc[RP][kEPL];
+    // int4: pm = sum of p * shift of the lane's group, added to every accumulator at the end
+    float m[RP], l[RP], lf[RP], acc[RP][kEPL], pm[INT4 ? RP : 1];
 #pragma unroll
     for (int r = 0; r < RP; ++r) {
         m[r] = -INFINITY;
         l[r] = 0.f;
         lf[r] = 0.f;
+        if constexpr (INT4) pm[r] = 0.f;
 #pragma unroll
         for (int e = 0; e < kEPL; ++e) acc[r][e] = 0.f;
     }
@@ -352,14 +368,10 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         }
     };
 
-    // int4: the 16 values of a lane's two value words w.x, w.y with coefficient word w.z, exactly
-    // (a 4-bit field times an fp16 scale is exact in fp32; the shift is added with one rounding)
-    auto int4_values = [&](const u32x4 &w, float (&x)[16]) {
-        const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[2] & 0xFFFFu));
-        const float sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[2] >> 16));
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            x[e] = fmaf((float)((w[e / 8] >> (4 * (e % 8))) & 15u), sc, sh);
+    // int4: scale and shift of a coefficient word (w.z of a lane's loaded words)
+    auto int4_coef = [](uint32_t cw, float &sc, float &sh) {
+        sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(cw & 0xFFFFu));
+        sh = (float)__builtin_bit_cast(_Float16, (uint16_t)(cw >> 16));
     };
 
     // Arithmetic of one step on its loaded K and V.
@@ -368,8 +380,19 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
         float sc[U][RP];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            float kq[INT4 ? 16 : 1];  // int4 cache: the key's 16 values of this lane, once per key
-            if constexpr (INT4) int4_values(cur.k[u][0], kq);
+            // int4 cache: the key's fields as bf16 pairs 128 + f (dims 8w + j, 8w + j + 4), once per key
+            bf16x2 kf[INT4 ? 8 : 1];
+            float ksc = 0.f, koff = 0.f;  // s and m - 128 s of the lane's group
+            if constexpr (INT4) {
+#pragma unroll
+                for (int w = 0; w < 2; ++w)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        kf[4 * w + j] = as_bf16x2(((cur.k[u][0][w] >> (4 * j)) & 0x000F000Fu) | 0x43004300u);
+                float sh;
+                int4_coef(cur.k[u][0][2], ksc, sh);
+                koff = fmaf(-128.f, ksc, sh);
+            }
             bf16x2 kp8[FP8 ? kPieces : 1][8];  // fp8 cache: the keys' bytes as bf16 pairs, once per key
             if constexpr (FP8) {
 #pragma unroll
@@ -392,7 +415,8 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                             d = dot2(as_bf16x2(qv[r][2 * i + e / 4][e % 4]), kp8[i][e], d);
                 } else if constexpr (INT4) {
 #pragma unroll
-                    for (int e = 0; e < kEPL; ++e) d = fmaf(qf[r][e], kq[e], d);
+                    for (int i = 0; i < 8; ++i) d = dot2(qp[r][i], kf[i], d);
+                    d = fmaf(ksc, d, koff * qsum[r]);
                 } else if constexpr (kBf16) {
 #pragma unroll
                     for (int i = 0; i < kPieces; ++i)
@@ -407,7 +431,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 d = slot_sum<LPT>(d);
                 if constexpr (FP8)
                     d *= p.scale_log2 * (cur.val[u] ? cur.ks[u] : 0.f);
-                else if constexpr (kBf16 && !INT4)
+                else if constexpr (kBf16)
                     d *= p.scale_log2;
                 if constexpr (kMasked) {
                     const int pos = cur.pos0 + u * kSlots + slot;
@@ -441,6 +465,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 m[r] = raise ? mx[r] : m[r];
                 l[r] *= alpha;
                 lf[r] *= alpha;
+                if constexpr (INT4) pm[r] *= alpha;
 #pragma unroll
                 for (int e = 0; e < kEPL; ++e) acc[r][e] *= alpha;
             }
@@ -496,20 +521,32 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
                 }
             }
         } else if constexpr (INT4) {
-            // fp32 P.V with the unrounded P; a key that was not read has all its words zeroed
-            // (scale and shift 0) so that the query row it read cannot reach the sums
+            // fp32 P.V with the unrounded P: acc += (p s) f and pm += p m; a key that was not read
+            // has all its words zeroed (scale and shift 0) so that the row it read stays out
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 u32x4 w = cur.v[u][0];
                 if constexpr (kMasked) w = cur.val[u] ? w : u32x4{0u, 0u, 0u, 0u};
-                float vq[16];
-                int4_values(w, vq);
+                float f[16];  // fields of dims 8w + 2k (low nibble of byte k) and 8w + 2k + 1 (high)
+#pragma unroll
+                for (int ww = 0; ww < 2; ++ww) {
+                    const uint32_t lo = w[ww] & 0x0F0F0F0Fu, hi = (w[ww] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        f[8 * ww + 2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
+                        f[8 * ww + 2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
+                    }
+                }
+                float vsc, vsh;
+                int4_coef(w[2], vsc, vsh);
 #pragma unroll
                 for (int r = 0; r < RP; ++r) {
-                    l[r] += sc[u][r];
-                    lf[r] += sc[u][r];
+                    const float pr = sc[u][r], ps = pr * vsc;
+                    l[r] += pr;
+                    lf[r] += pr;
+                    pm[r] = fmaf(pr, vsh, pm[r]);
 #pragma unroll
-                    for (int e = 0; e < kEPL; ++e) acc[r][e] = fmaf(sc[u][r], vq[e], acc[r][e]);
+                    for (int e = 0; e < kEPL; ++e) acc[r][e] = fmaf(ps, f[e], acc[r][e]);
                 }
             }
         } else if constexpr (kBf16) {
@@ -578,6 +615,12 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     while (iterate(A, B) && iterate(B, A)) {
     }
 
+    if constexpr (INT4) {  // the shifts' share of the lane's accumulators
+#pragma unroll
+        for (int r = 0; r < RP; ++r)
+#pragma unroll
+            for (int e = 0; e < kEPL; ++e) acc[r][e] += pm[r];
+    }
     // ---- combine the row-slots of the wave (lanes c, c+LPT, ...)
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
@@ -642,14 +685,30 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
     }
 }
 
+template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8, bool INT4>
+__global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialParams p) {
+    partial_valu_body<T, D, RP, MODE, U, LPT, FP8, INT4>(p);
+}
+
+// The int4 form is bound by memory latency at one wave per SIMD; held to two (256 registers), a
+// second wave's loads and arithmetic overlap the first's wait.
+template <typename T, int D, int RP, int MODE, int U, int LPT>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+partial_valu_int4_kernel(const PartialParams p) {
+    partial_valu_body<T, D, RP, MODE, U, LPT, false, true>(p);
+}
+
 template <typename T, int D, int RP, int MODE, bool FP8, bool INT4>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int kRowLanes = D * (FP8 ? 1 : (int)sizeof(T)) / 16;
     constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
-    constexpr int U = AD_VALU_KEYS_PER_SLOT;
+    constexpr int U = INT4 ? 1 : AD_VALU_KEYS_PER_SLOT;  // int4: one key per slot and step (registers)
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
-    hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8, INT4>), grid, dim3(kThreads), 0, stream,
-                       p);
+    if constexpr (INT4)
+        hipLaunchKernelGGL((partial_valu_int4_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8, INT4>), grid, dim3(kThreads), 0, stream,
+                           p);
     return hipGetLastError();
 }
 
