@@ -107,8 +107,9 @@ __device__ __forceinline__ bf16x2 e4m3_pair(uint32_t w) {
 // FP8: k and v hold OCP E4M3 bytes with fp32 row scales (bf16 queries); K / V elements are then
 // bytes, each lane still owns 16 of a row, and its query values for them are two 16-B words.
 // INT4: k and v hold rows of 32-bit words, kv_groups coefficient words (fp16 scale s low, fp16
-// shift m high) and then D / 8 words of 4-bit fields f (field d % 8 of word d / 8); each lane owns
-// 16 consecutive dimensions, all in one group (two value words and the group's coefficient word).
+// shift m high) and then D / 8 words of 4-bit fields f (field d % 8 of word d / 8); 16 lanes share
+// a row and each owns 8 consecutive dimensions, all in one group (one value word and the group's
+// coefficient word), so that a wave-wide load covers 4 keys and a step 16.
 // q.k over them is s * sum q (128 + f) + (m - 128 s) * sum q: the fields become bf16 pairs
 // 128 + f by masking in an exponent (exact), multiplied with v_dot2 against the queries paired
 // the same way, and the per-row query sums fix the offset in fp32. P.V keeps P unrounded:
@@ -118,13 +119,14 @@ template <typename T, int D, int RP, int MODE, int U, int LPT, bool FP8, bool IN
 __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
     constexpr bool kBf16 = sizeof(T) == 2;
     static_assert(!(FP8 || INT4) || kBf16, "a quantised cache is read with bf16 queries");
-    static_assert(!INT4 || (D == 128 && LPT == 8), "the int4 lane map: 8 lanes x 16 dimensions per row");
+    static_assert(!INT4 || (D == 128 && (LPT == 8 || LPT == 16)), "the int4 lane map: 8 or 16 lanes per row");
     using KV = std::conditional_t<FP8, uint8_t, std::conditional_t<INT4, uint32_t, T>>;  // one K / V element
-    constexpr int kPer16 = INT4 ? 16 : 16 / (int)sizeof(KV);   // K / V elements per 16-B piece (int4: per lane)
+    constexpr int kPer16 = INT4 ? D / LPT : 16 / (int)sizeof(KV);  // K / V elements per 16-B piece (int4: per lane)
+    constexpr int kIW = INT4 ? D / (8 * LPT) : 1;                 // int4: packed value words per lane
     constexpr int kSlots = 64 / LPT;                           // rows per wave-wide load
     constexpr int kPieces = INT4 ? 1 : D * (int)sizeof(KV) / (16 * LPT);  // 16-B pieces per lane per row
     constexpr int kEPL = kPieces * kPer16;                     // elements per lane per row
-    constexpr int kQv = (FP8 || INT4) ? 2 * kPieces : kPieces;  // 16-B query words per lane per row
+    constexpr int kQv = FP8 ? 2 * kPieces : INT4 ? kPer16 / 8 : kPieces;  // 16-B query words per lane per row
     constexpr int kStep = kSlots * U;                         // keys per wave per step
     static_assert(kPieces >= 1, "row too short for the lanes sharing it");
     static_assert(MODE == KV_CONTIG || (kStep <= 16 && 16 % kStep == 0),
@@ -226,25 +228,28 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
 #pragma unroll
             for (int i = 0; i < kPieces; ++i) {
                 const T *src = qr + (i * LPT + c) * kPer16;  // the lane's elements of piece i
-                if constexpr (FP8 || INT4) {
+                if constexpr (FP8) {
                     qv[r][2 * i] = ld16(src);
                     qv[r][2 * i + 1] = ld16(src + 8);
+                } else if constexpr (INT4) {
+#pragma unroll
+                    for (int qi = 0; qi < kQv; ++qi) qv[r][qi] = ld16(src + 8 * qi);
                 } else {
                     qv[r][i] = ld16(src);
                 }
             }
         }
     }
-    // int4: the lane's 16 query values as pairs (dim 8w + j, dim 8w + j + 4), the order in which
-    // the fields of packed word w come out two at a time, and their fp32 sum
-    bf16x2 qp[INT4 ? RP : 1][INT4 ? 8 : 1];
+    // int4: the lane's query values as pairs (dim 8w + j, dim 8w + j + 4), the order in which the
+    // fields of its packed word w come out two at a time, and their fp32 sum
+    bf16x2 qp[INT4 ? RP : 1][INT4 ? 4 * kIW : 1];
     float qsum[INT4 ? RP : 1];
     if constexpr (INT4) {
 #pragma unroll
         for (int r = 0; r < RP; ++r) {
             qsum[r] = 0.f;
 #pragma unroll
-            for (int w = 0; w < 2; ++w)
+            for (int w = 0; w < kIW; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint32_t a = qv[r][w][j / 2], b = qv[r][w][2 + j / 2];  // dims j and j + 4
@@ -283,10 +288,10 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
     const KV *safe = reinterpret_cast<const KV *>(qbase);
     const int map_mask = (1 << map_shift) - 1;
     const int lane_piece = c * kPer16;
-    // int4: this lane's two value words and its group's coefficient word inside a row (a query
-    // row read instead is 64 words long, more than the largest offset, 8 + 15)
-    const int i4_vals = INT4 ? p.kv_groups + 2 * c : 0;
-    const int i4_coef = INT4 ? (16 * c) * p.kv_groups / D : 0;
+    // int4: this lane's value words and its group's coefficient word inside a row (a query row
+    // read instead is 64 words long, more than the largest offset, 8 + 15)
+    const int i4_vals = INT4 ? p.kv_groups + kIW * c : 0;
+    const int i4_coef = INT4 ? (kPer16 * c) * p.kv_groups / D : 0;
 
     // l: row sum of the probabilities as multiplied into acc (the rounded P for bf16), the output
     // normaliser; lf: the same sum in full fp32, which gives the LSE.
@@ -356,9 +361,9 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
                 f.vs[u] = *(valid ? vsrow + off * p.vs_s[1] : p.v_scale);
             }
             f.val[u] = valid;
-            if constexpr (INT4) {  // dword loads: int4 rows are only 4-byte aligned
-                f.k[u][0] = u32x4{kp[i4_vals], kp[i4_vals + 1], kp[i4_coef], 0u};
-                f.v[u][0] = u32x4{vp[i4_vals], vp[i4_vals + 1], vp[i4_coef], 0u};
+            if constexpr (INT4) {  // dword loads: int4 rows are only 4-byte aligned; coefficient in .z
+                f.k[u][0] = u32x4{kp[i4_vals], kIW > 1 ? kp[i4_vals + 1] : 0u, kp[i4_coef], 0u};
+                f.v[u][0] = u32x4{vp[i4_vals], kIW > 1 ? vp[i4_vals + 1] : 0u, vp[i4_coef], 0u};
             } else {
 #pragma unroll
                 for (int i = 0; i < kPieces; ++i) f.k[u][i] = ld16(kp + i * LPT * kPer16 + lane_piece);
@@ -381,11 +386,11 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             // int4 cache: the key's fields as bf16 pairs 128 + f (dims 8w + j, 8w + j + 4), once per key
-            bf16x2 kf[INT4 ? 8 : 1];
+            bf16x2 kf[INT4 ? 4 * kIW : 1];
             float ksc = 0.f, koff = 0.f;  // s and m - 128 s of the lane's group
             if constexpr (INT4) {
 #pragma unroll
-                for (int w = 0; w < 2; ++w)
+                for (int w = 0; w < kIW; ++w)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         kf[4 * w + j] = as_bf16x2(((cur.k[u][0][w] >> (4 * j)) & 0x000F000Fu) | 0x43004300u);
@@ -415,7 +420,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
                             d = dot2(as_bf16x2(qv[r][2 * i + e / 4][e % 4]), kp8[i][e], d);
                 } else if constexpr (INT4) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) d = dot2(qp[r][i], kf[i], d);
+                    for (int i = 0; i < 4 * kIW; ++i) d = dot2(qp[r][i], kf[i], d);
                     d = fmaf(ksc, d, koff * qsum[r]);
                 } else if constexpr (kBf16) {
 #pragma unroll
@@ -527,9 +532,9 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
             for (int u = 0; u < U; ++u) {
                 u32x4 w = cur.v[u][0];
                 if constexpr (kMasked) w = cur.val[u] ? w : u32x4{0u, 0u, 0u, 0u};
-                float f[16];  // fields of dims 8w + 2k (low nibble of byte k) and 8w + 2k + 1 (high)
+                float f[kEPL];  // fields of dims 8w + 2k (low nibble of byte k) and 8w + 2k + 1 (high)
 #pragma unroll
-                for (int ww = 0; ww < 2; ++ww) {
+                for (int ww = 0; ww < kIW; ++ww) {
                     const uint32_t lo = w[ww] & 0x0F0F0F0Fu, hi = (w[ww] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
                     for (int k = 0; k < 4; ++k) {
@@ -701,8 +706,9 @@ partial_valu_int4_kernel(const PartialParams p) {
 template <typename T, int D, int RP, int MODE, bool FP8, bool INT4>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int kRowLanes = D * (FP8 ? 1 : (int)sizeof(T)) / 16;
-    constexpr int LPT = AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
-    constexpr int U = INT4 ? 1 : AD_VALU_KEYS_PER_SLOT;  // int4: one key per slot and step (registers)
+    // int4: 16 lanes per row (8 dimensions each) and 4 keys per slot, a 16-key step in few registers
+    constexpr int LPT = INT4 ? 16 : AD_VALU_LANES_PER_ROW < kRowLanes ? AD_VALU_LANES_PER_ROW : kRowLanes;
+    constexpr int U = INT4 ? 4 : AD_VALU_KEYS_PER_SLOT;
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
     if constexpr (INT4)
         hipLaunchKernelGGL((partial_valu_int4_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
