@@ -238,7 +238,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1"}))
+        print(json.dumps({"error": "bench.py measures one GPU; run it with --gpus 1"}))
         log("bench.py: only --gpus 1 is supported (the decode step runs on a single GPU)")
         sys.exit(2)
 

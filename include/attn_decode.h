@@ -47,7 +47,7 @@ extern "C" {
 #define AD_E_DTYPE (-2)       /* unknown or unsupported element type */
 #define AD_E_SHAPE (-3)       /* inconsistent sizes (e.g. Hq % Hkv != 0, non-positive sizes) */
 #define AD_E_ALIGN (-4)       /* a row start or the last dimension is not 16-byte aligned/contiguous */
-#define AD_E_UNSUPPORTED (-5) /* a valid request this build has no kernel for (e.g. head dim 96) */
+#define AD_E_UNSUPPORTED (-5) /* a valid request the library has no kernel for (e.g. head dim 96) */
 #define AD_E_WORKSPACE (-6)   /* workspace missing or smaller than attn_decode_workspace_size() */
 #define AD_E_RANGE (-7)       /* a count out of range (num_splits, page size, window, ...) */
 
