@@ -699,7 +699,7 @@ __global__ void __launch_bounds__(kThreads) partial_valu_kernel(const PartialPar
 // second wave's loads and arithmetic overlap the first's wait.
 template <typename T, int D, int RP, int MODE, int U, int LPT>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-partial_valu_int4_kernel(const PartialParams p) {
+partial_valu_kernel_int4(const PartialParams p) {
     partial_valu_body<T, D, RP, MODE, U, LPT, false, true>(p);
 }
 
@@ -711,7 +711,7 @@ hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     constexpr int U = INT4 ? 4 : AD_VALU_KEYS_PER_SLOT;
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
     if constexpr (INT4)
-        hipLaunchKernelGGL((partial_valu_int4_kernel<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((partial_valu_kernel_int4<T, D, RP, MODE, U, LPT>), grid, dim3(kThreads), 0, stream, p);
     else
         hipLaunchKernelGGL((partial_valu_kernel<T, D, RP, MODE, U, LPT, FP8, INT4>), grid, dim3(kThreads), 0, stream,
                            p);

@@ -46,7 +46,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
     6: ("partial_mfma_paged_fp8", "partial_mfma_kernel, fp8 cache + merge_kernel (two launches per step)"),
     7: ("partial_mfma_paged_spec", "partial_mfma_kernel, draft trees + merge_kernel (two launches per step)"),
-    8: ("partial_valu_paged_int4", "partial_valu_kernel, int4 cache + merge_kernel (two launches per step)"),
+    8: ("partial_valu_paged_int4", "partial_valu_kernel_int4 + merge_kernel (two launches per step)"),
 }
 
 
@@ -101,6 +101,8 @@ class Step:
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
             self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
             kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
+            if w.kv_format == "int4":  # the vector kernel's int4 form has a symbol of its own
+                kind += "_int4"
             if self.launches == 1:
                 self.kernel_name = f"{kind} (merge inside; the whole step)"
             else:  # the partial pass alone, into buffers of its own

@@ -128,3 +128,24 @@ def test_rows_outside_the_sequences_untouched(monkeypatch):
     assert torch.all(out[T:] == 7.0) and torch.all(lse[T:] == 7.0)
     assert torch.isfinite(out[:T]).all() and torch.isfinite(lse[:T]).all()
 
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("kind", ["paged", "sparse"])
+def test_fp8_cache_with_drafts(orc, monkeypatch, kernel, kind):
+    """Packed draft tokens with tree masks over an E4M3 cache with row scales."""
+    force(monkeypatch, kernel)
+    lens = [300, 45, 0, 129]
+    say(f"[gpu] spec + fp8 {kind} {kernel}")
+    common = dict(num_q_heads=8, num_kv_heads=2, head_dim=128, q_len=5, seed=1500, causal=False, window=0,
+                  kv_format="fp8", poison=True)
+    if kind == "paged":
+        w = inputs.paged(seq_lens=lens, page_size=16, **common)
+    else:
+        w = inputs.sparse(batch=4, kv_len=384, block_size=64, seq_lens=lens,
+                          blocks=[[[0, 2, 4], [1, 4]], [[0], [0]], [[], [0]], [[0, 1], [2]]], **common)
+    w = inputs.with_spec(w, counts=[5, 2, 0, 4], tree=True, seed=4)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 3):
+        out, lse, _ = run(w, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, torch.bfloat16, f"S={S}")
