@@ -213,6 +213,9 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     // (the scores of those keys are masked). Latent rows past the split read the unit's query
     // row instead. The buffer form of the LDS copy matters: the compiler treats the global form
     // as a possible LDS access of unknown order and would make every LDS read wait for all.
+    // The copies are nontemporal (cache-policy bit 1 of the buffer instruction): each reads whole
+    // lines once: 128 -> 113 us for 32 sequences of 8192 keys under 128 heads.
+    constexpr int kStreamPolicy = 2;
     const int64_t rope_stride = p.k2_s[1] * 2;  // bytes between the rotary rows of two slots of a page
     auto issue = [&](lds_u8 *lat_slot, lds_u8 *rope_slot, int base) {
         // Row addresses of key base + i in lane i (i < 32), computed once per tile on the vector
@@ -233,7 +236,7 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
                 __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, kLatent * 2, kBufferFlags);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 rsrc, (__attribute__((address_space(3))) void *)(lat_slot + kk * 1024), 16, (lane ^ swz_lat(kk)) << 4,
-                0, 0, 0);
+                0, 0, kStreamPolicy);
         }
         const int v0 = base + 8 * wave;  // uniform: first key of this wave's rotary group
         const int nv = min(max(t1 - v0, 0), 8);
@@ -243,7 +246,7 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
             (void *)row, (short)0, nv > 0 ? (int)((nv - 1) * rope_stride) + kRope * 2 : 0, kBufferFlags);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void *)(rope_slot + wave * 1024), 16,
-            (int)((lane >> 3) * rope_stride) + (((lane & 7) ^ swz_rope(k)) << 4), 0, 0, 0);
+            (int)((lane >> 3) * rope_stride) + (((lane & 7) ^ swz_rope(k)) << 4), 0, 0, kStreamPolicy);
     };
 
     // Per-lane LDS offsets inside a slot; every read adds a compile-time offset that fits the DS

@@ -81,7 +81,13 @@ __device__ __forceinline__ float slot_sum(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// Every 16-B load of this kernel is nontemporal: the 8 lanes sharing a row read whole 128-B lines
+// in one instruction and nothing is read twice, so the lines need not stay in the caches
+// (measured: 224 -> 205 us on the ragged paged cache of 64 sequences, 56.7 -> 52.7 us on the
+// contiguous 16 x 4096 cache).
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 
 // Reinterpretations take the 32-bit word BY VALUE: hipcc miscompiles __builtin_bit_cast applied
 // directly to an element of an ext_vector_type lvalue (it reads the wrong element), so vector
