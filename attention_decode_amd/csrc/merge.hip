@@ -39,6 +39,38 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
         S = min(S, Sb);
     }
     const float *ls = p.part_lse + (int64_t)row * p.num_splits;
+    const float *po = p.part_o + (int64_t)row * p.num_splits * Dv + lane * VEC;
+    // The partial rows of the first 4 splits are loaded before the LSEs are read, so that both
+    // round trips overlap; later splits follow 4 at a time. Splits are summed in ascending order.
+    float x[4][VEC];
+    auto load4 = [&](int s0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float *src = po + (int64_t)(s0 + j) * Dv;
+            if (s0 + j < S) {
+                if constexpr (VEC % 4 == 0) {
+#pragma unroll
+                    for (int k = 0; k < VEC; k += 4) {
+                        const float4 v = *reinterpret_cast<const float4 *>(src + k);
+                        x[j][k] = v.x;
+                        x[j][k + 1] = v.y;
+                        x[j][k + 2] = v.z;
+                        x[j][k + 3] = v.w;
+                    }
+                } else if constexpr (VEC == 2) {
+                    const float2 v = *reinterpret_cast<const float2 *>(src);
+                    x[j][0] = v.x;
+                    x[j][1] = v.y;
+                } else {
+                    x[j][0] = src[0];
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) x[j][k] = 0.f;
+            }
+        }
+    };
+    load4(0);
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, ls[s]);
     const float ms = (M == -INFINITY) ? 0.f : M;
@@ -47,26 +79,16 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
 #pragma unroll
     for (int j = 0; j < VEC; ++j) o[j] = 0.f;
     float W = 0.f;
-    const float *po = p.part_o + (int64_t)row * p.num_splits * Dv + lane * VEC;
-    for (int s = 0; s < S; ++s) {
-        const float w = __builtin_amdgcn_exp2f((ls[s] - ms) * kLog2e);
-        W += w;
-        const float *src = po + (int64_t)s * Dv;
-        if constexpr (VEC % 4 == 0) {
+    for (int s0 = 0; s0 < S; s0 += 4) {
+        if (s0 > 0) load4(s0);
 #pragma unroll
-            for (int j = 0; j < VEC; j += 4) {
-                const float4 x = *reinterpret_cast<const float4 *>(src + j);
-                o[j] += w * x.x;
-                o[j + 1] += w * x.y;
-                o[j + 2] += w * x.z;
-                o[j + 3] += w * x.w;
+        for (int j = 0; j < 4; ++j) {
+            if (s0 + j < S) {
+                const float w = __builtin_amdgcn_exp2f((ls[s0 + j] - ms) * kLog2e);
+                W += w;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) o[k] += w * x[j][k];
             }
-        } else if constexpr (VEC == 2) {
-            const float2 x = *reinterpret_cast<const float2 *>(src);
-            o[0] += w * x.x;
-            o[1] += w * x.y;
-        } else {
-            o[0] += w * src[0];
         }
     }
     const float inv = W > 0.f ? 1.f / W : 0.f;
