@@ -19,13 +19,15 @@
  *     the stride arrays) are HOST memory, read during the call only. The library allocates no
  *     device memory, never synchronises and never throws. Work is enqueued on `stream` (a
  *     hipStream_t; NULL = the default stream) and runs asynchronously.
- *   - Strides are in ELEMENTS. The last (feature) dimension of every tensor is contiguous, and
- *     every row start must be 16-byte aligned.
+ *   - Strides are in ELEMENTS (bytes for an fp8 cache, 32-bit words for an int4 cache). The
+ *     last (feature) dimension of every tensor is contiguous, and every row start must be
+ *     16-byte aligned (int4 cache rows: 4-byte aligned).
  *   - Return value: AD_OK (0), a negative AD_E_* code when the arguments were rejected on the
  *     host before anything was enqueued, or a positive hipError_t when a launch failed.
  *     attn_decode_last_error() gives a message for the calling thread's last non-OK return.
  *   - Data contracts that are NOT checked (they live in device memory): seq_lens[b] <=
- *     kv_len_max and >= q_len; block-table entries for the pages a sequence covers lie in
+ *     kv_len_max and >= the sequence's query tokens; q_starts nondecreasing with counts of at
+ *     most q_len; block-table entries for the pages a sequence covers lie in
  *     [0, pages of the pool) (entries past the sequence are never read and may hold -1);
  *     listed sparse blocks are < ceil(kv_len_max / block_size). Keys outside a sequence, past
  *     its last page slot, in unlisted blocks or in unreferenced pages are never read into the
@@ -51,7 +53,7 @@ extern "C" {
 #define AD_E_WORKSPACE (-6)   /* workspace missing or smaller than attn_decode_workspace_size() */
 #define AD_E_RANGE (-7)       /* a count out of range (num_splits, page size, window, ...) */
 
-/* ---- element types (Q, K, V and the output share one) ------------------------------------ */
+/* ---- element types (Q, K, V and the output share one, unless kv_format quantises K / V) ---- */
 #define AD_F32 0
 #define AD_BF16 1
 
