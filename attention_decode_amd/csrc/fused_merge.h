@@ -56,8 +56,10 @@ __device__ __forceinline__ void store_out(const PartialParams &p, int64_t off, f
 }
 
 // Writes out = 0 and lse = -inf for rows r < nr (a unit without any key: no split arrives).
+// Both helpers are always inlined: a call would pass the kernel's parameter block by address,
+// which moves it to scratch and turns every load of the calling kernel into a flat load.
 template <int NTHREADS, int DV, typename RowFn>
-__device__ void fused_write_empty(const PartialParams &p, int nr, RowFn out_row) {
+__device__ __forceinline__ void fused_write_empty(const PartialParams &p, int nr, RowFn out_row) {
     for (int r = 0; r < nr; ++r) {
         const OutIdx oi = out_index(p, (int)out_row(r));
         for (int d = threadIdx.x; d < DV; d += NTHREADS) store_out(p, oi.off + d, 0.f);
@@ -71,8 +73,8 @@ __device__ void fused_write_empty(const PartialParams &p, int nr, RowFn out_row)
 // weights: LDS scratch of at least nr * nsplit floats that the caller no longer needs. Every
 // thread of the group must call it.
 template <int NTHREADS, int DV, int EPT, typename RowFn>
-__device__ void fused_arrive_merge(const PartialParams &p, int unit, int nsplit, int nr, RowFn out_row,
-                                   float *weights) {
+__device__ __forceinline__ void fused_arrive_merge(const PartialParams &p, int unit, int nsplit, int nr, RowFn out_row,
+                                                   float *weights) {
     __shared__ int s_last;
     __shared__ int s_row[64];                // per row: LSE index
     __shared__ float s_inv[64], s_lse[64];   // per row: 1 / sum_s w_s and the merged LSE
