@@ -36,6 +36,7 @@ struct PartialParams {
     // shape
     int32_t batch, q_len, num_q_heads, num_kv_heads, group, head_dim_v;
     int32_t row_blocks;   // work units per KV head along its G * q_len query rows (grid y = Hkv * row_blocks)
+    int32_t mfma_rows;    // matrix-core kernel, bf16: whole-row loads staged through LDS (grids of several rounds)
     float scale_log2;     // softmax scale * log2(e): scores are kept in base-2 units
     int32_t causal, window;
     int32_t num_splits, chunk;  // split s covers [s*chunk, (s+1)*chunk) of the (virtual) key range

@@ -302,7 +302,22 @@ hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mod
     const Rows rows = row_plan(a);
     p.row_blocks = rows.blocks;
     // one work group per (split, b, KV head, row block) on a 1-D grid
-    if ((int64_t)p.num_splits * a->batch * a->num_kv_heads * rows.blocks > INT_MAX) return hipErrorInvalidConfiguration;
+    const int64_t groups = (int64_t)p.num_splits * a->batch * a->num_kv_heads * rows.blocks;
+    if (groups > INT_MAX) return hipErrorInvalidConfiguration;
+    if (rows.mfma && a->kv_format == AD_KV_SAME) {
+        // Whole-row loads staged through LDS (bf16 caches): every load reads whole lines once, at
+        // the price of a round trip through LDS per tile. That pays when a compute unit runs
+        // several work groups in turn (2048 groups: 258 -> 238 us) and costs when each runs one
+        // (256 groups: 33.9 -> 35.5 us). AD_MFMA_ROWS=0/1 forces the choice (testing aid).
+        const char *set = getenv("AD_MFMA_ROWS");
+        if (set && *set) {
+            p.mfma_rows = env_int("AD_MFMA_ROWS") != 0;
+        } else {
+            int cus = 0;
+            if (device_cus(&cus) != AD_OK) return hipErrorInvalidDevice;
+            p.mfma_rows = groups > cus;
+        }
+    }
     if (rows.mfma) return ad::launch_partial_mfma(p, a->head_dim_qk, mode, stream);
     return ad::launch_partial_valu(p, a->dtype, a->head_dim_qk, rows.per_unit, mode, stream);  // fp8: p.kv_fp8
 }

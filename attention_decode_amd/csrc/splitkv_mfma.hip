@@ -71,6 +71,11 @@ constexpr int kRows = 32;   // query rows per work unit
 constexpr float kLazyRescale = 8.f;
 
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+// Whole-row loads (ROWS form): the lanes that share a row read all of it in one instruction, so
+// whole lines are read once and the loads are nontemporal.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 // A lane reads 16 B of a line per instruction and four instructions cover it, so the lines must
 // stay cached between them; with an fp8 cache the fourth read of each line is nontemporal (the
 // line is done then): 164 -> 150 us on the ragged paged fp8 cache. On bf16 caches the same hint
@@ -119,8 +124,9 @@ __device__ __forceinline__ int swz(int k) {
     return ((2 * (k & 7)) | ((k >> 3) & 1)) & (D / 8 - 1);
 }
 
-template <int D, int MODE, bool FP8>
+template <int D, int MODE, bool FP8, bool ROWS>
 __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialParams p) {
+    static_assert(!(ROWS && FP8), "whole-row loads are built for bf16 caches");
     constexpr int kKs = D / 16;    // k-steps of the score product
     constexpr int kSlabs = D / 32; // 32-column slabs of the output
     constexpr int kRowBytes = D * 2;  // one bf16 row of the LDS V tile
@@ -165,7 +171,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     }
 
     __shared__ int s_map[kMapCapacity];
-    // Per-wave V tiles during the loop; per-wave fp32 accumulators for the final combine.
+    // Per-wave V tiles (and K tiles, ROWS form) during the loop; per-wave fp32 accumulators for
+    // the final combine.
     __shared__ __attribute__((aligned(16))) unsigned char s_buf[kWaves * kRows * D * 4];
     __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
     __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
@@ -297,15 +304,57 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
             f.ks = *ksp;
             f.vs = *vsp;
             f.live = kp != safe;
-        } else {
+        } else if constexpr (!ROWS) {
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) f.k[ks] = ld16(kp + 16 * ks + 8 * half);
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) f.v[ks] = ld16(vp + 16 * ks + 8 * half);
         }
     };
+    // ROWS form: kRowLanes lanes share a row (16 B each), a wave-wide load covers kRowsPerLoad
+    // rows and kKs loads the tile's 32 keys, for K and again for V; the rows go to the wave's LDS
+    // tiles, from which the matrix cores read K as the A operand and V transposed.
+    constexpr int kRowLanes = D * 2 / 16;
+    constexpr int kRowsPerLoad = 64 / kRowLanes;
+    static_assert(kRowsPerLoad * kKs == kTile, "the loads of a tile cover its keys");
+    const int lrow = lane / kRowLanes, lpiece = lane % kRowLanes;  // row within a load, 16-B piece
+    // element offsets of the K and V rows of key v from kbase / vbase; ok false: not read
+    struct RowOff {
+        int64_t k, v;
+        bool ok;
+    };
+    auto rows_of = [&](int v) -> RowOff {
+        RowOff r{0, 0, false};
+        if (v >= t1) return r;
+        if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
+            if (v < lo_min || v >= hi_max) return r;
+            const int64_t page = s_map[(v >> map_shift) - map_first];
+            const int slot = v & map_mask;
+            r.k = page * p.k_s[0] + slot * p.k_s[1];
+            r.v = page * p.v_s[0] + slot * p.v_s[1];
+        } else {
+            const int pos = logical(v);
+            if (pos >= L || pos < lo_min || pos >= hi_max) return r;
+            r.k = (int64_t)pos * p.k_s[1];
+            r.v = (int64_t)pos * p.v_s[1];
+        }
+        r.ok = true;
+        return r;
+    };
+    auto fetch_rows = [&](Buf &f, int base) {
+        f.base = base;
+#pragma unroll
+        for (int i = 0; i < kKs; ++i) {
+            const RowOff r = rows_of(base + kRowsPerLoad * i + lrow);
+            const KV *kp = r.ok ? kbase + r.k : safe;
+            const KV *vp = r.ok ? vbase + r.v : safe;
+            f.k[i] = ld16_stream(kp + 8 * lpiece);
+            f.v[i] = ld16_stream(vp + 8 * lpiece);
+        }
+    };
 
-    lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;  // this wave's V tile
+    lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;             // this wave's V tile
+    lds_u8 *kw = (lds_u8 *)s_buf + (kWaves + wave) * kTile * kRowBytes;  // and its K tile (ROWS form)
     // Transposing-read addresses (bytes in vw) of this lane, for k-step t, read rd and slab s:
     // row 16t + 8rd + 4*half + (lane&15)/4, chunk 4s + 2*((lane>>4)&1) + (lane&3)/2, half-chunk lane&1.
     const int tr_row = 4 * half + ((lane & 15) >> 2);
@@ -336,6 +385,14 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
                 s_ks[wave][col] = cur.live ? cur.ks : 0.f;
                 s_vs[wave][col] = cur.live ? cur.vs : 0.f;
             }
+        } else if constexpr (ROWS) {  // load i: chunk lpiece of row kRowsPerLoad * i + lrow, K and V
+#pragma unroll
+            for (int i = 0; i < kKs; ++i) {
+                const int kk = kRowsPerLoad * i + lrow;
+                const int at = kk * kRowBytes + ((lpiece ^ swz<D>(kk)) << 4);
+                *(__attribute__((address_space(3))) u32x4 *)(kw + at) = cur.k[i];
+                *(__attribute__((address_space(3))) u32x4 *)(vw + at) = cur.v[i];
+            }
         } else {
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks)
@@ -352,6 +409,13 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
                 const u32x4 w = cur.k[j];
                 sc = mfma(e4m3_x8(w[0], w[1]), qb[2 * j], sc);
                 sc = mfma(e4m3_x8(w[2], w[3]), qb[2 * j + 1], sc);
+            }
+        } else if constexpr (ROWS) {  // the A operand of k-step ks: row col, chunk 2 ks + half of the K tile
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) {
+                const u32x4 a = *(__attribute__((address_space(3))) u32x4 *)(kw + col * kRowBytes +
+                                                                                (((2 * ks + half) ^ swz<D>(col)) << 4));
+                sc = mfma(a, qb[ks], sc);
             }
         } else {
 #pragma unroll
@@ -449,8 +513,14 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     };
 
     constexpr int kStride = kWaves * kTile;
+    auto prefetch = [&](Buf &f, int base) {
+        if constexpr (ROWS)
+            fetch_rows(f, base);
+        else
+            fetch(f, base);
+    };
     auto iterate = [&](Buf &cur, Buf &nxt) {
-        fetch(nxt, cur.base + kStride);
+        prefetch(nxt, cur.base + kStride);
         __builtin_amdgcn_sched_barrier(0);
         bool full = cur.base + kTile <= t1;
         if (full) {
@@ -467,7 +537,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     const int first = t0 + wave * kTile;
     const int ntiles = first < t1 ? (t1 - first + kStride - 1) / kStride : 0;
     Buf A, B;
-    fetch(A, first);
+    prefetch(A, first);
     int i = 0;
     for (; i + 2 <= ntiles; i += 2) {
         iterate(A, B);
@@ -478,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     // ---- combine the waves: o_s = acc / l, lse_s = (m + log2 lf) * ln 2
     l = pair_sum(l);
     lf = pair_sum(lf);
-    __syncthreads();  // every wave is done with its V tile: s_buf now holds the accumulators
+    __syncthreads();  // every wave is done with its tiles: s_buf now holds the accumulators
     float *s_o = reinterpret_cast<float *>(s_buf) + wave * kRows * D;
     if (half == 0) {
         s_m[wave][col] = m;
@@ -524,7 +594,12 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
 template <int D, int MODE, bool FP8>
 hipError_t launch_t(const PartialParams &p, hipStream_t stream) {
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
-    hipLaunchKernelGGL((partial_mfma_kernel<D, MODE, FP8>), grid, dim3(kThreads), 0, stream, p);
+    if constexpr (!FP8)
+        if (p.mfma_rows) {
+            hipLaunchKernelGGL((partial_mfma_kernel<D, MODE, false, true>), grid, dim3(kThreads), 0, stream, p);
+            return hipGetLastError();
+        }
+    hipLaunchKernelGGL((partial_mfma_kernel<D, MODE, FP8, false>), grid, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
 

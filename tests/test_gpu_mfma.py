@@ -30,6 +30,14 @@ def kernel(name):
             os.environ["AD_PARTIAL_KERNEL"] = old
 
 
+@pytest.fixture(autouse=True, params=["cols", "rows"])
+def load_form(request, monkeypatch):
+    """Every test runs with both load forms of the bf16 matrix-core kernel: lane pairs that read
+    K as the matrix operand straight from HBM (cols), and whole rows staged through LDS (rows)."""
+    monkeypatch.setenv("AD_MFMA_ROWS", "1" if request.param == "rows" else "0")
+    return request.param
+
+
 def run(w_cpu, num_splits=None):
     wg = w_cpu.to("cuda")
     step = DecodeStep(wg, num_splits=num_splits)
@@ -182,3 +190,29 @@ def test_mfma_matches_valu_closely():
     assert float((ov.double() - om.double()).abs().max()) <= 2e-3
     assert float((lv.double() - lm.double()).abs().max()) <= 2e-4
     assert not np.isnan(om.float().numpy()).any()
+
+
+@pytest.mark.parametrize("kind", ["contiguous", "paged", "sparse", "spec"])
+def test_load_forms_bit_identical(monkeypatch, kind):
+    """The two load forms feed the matrix cores the same operands in the same order: the results
+    agree bit for bit."""
+    say(f"[gpu] mfma load forms {kind}")
+    common = dict(num_q_heads=16, num_kv_heads=2, head_dim=128, q_len=4, seed=700, causal=True, window=900)
+    if kind == "contiguous":
+        w = inputs.contiguous(batch=3, kv_len=1500, seq_lens=[1500, 31, 777], **common)
+    elif kind == "sparse":
+        w = inputs.sparse(batch=2, kv_len=1024, block_size=64, seq_lens=[1024, 600], poison=True,
+                          blocks=[[[0, 3, 9, 15], [2]], [[1, 4, 8], []]], **common)
+    else:
+        w = inputs.paged(seq_lens=[1500, 31, 777, 4], page_size=16, poison=True, **common)
+        if kind == "spec":
+            w = inputs.with_spec(w, counts=[4, 2, 0, 3], tree=True, seed=2)
+    res = []
+    for form in ("0", "1"):
+        monkeypatch.setenv("AD_MFMA_ROWS", form)
+        for S in (1, 3):
+            out, lse, _ = run(w, num_splits=S)
+            res.append((out.view(torch.int16), lse))
+    for S_i in (0, 1):
+        a, b = res[S_i], res[2 + S_i]
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1]), f"split set {S_i}"

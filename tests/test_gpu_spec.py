@@ -12,11 +12,12 @@ from gpu_util import assert_matches, gpu_available, oracle_of, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-KERNELS = ["valu", "mfma"]
+KERNELS = ["valu", "mfma", "mfma_rows"]  # mfma_rows: the matrix-core kernel's whole-row load form
 
 
 def force(monkeypatch, kernel):
-    monkeypatch.setenv("AD_PARTIAL_KERNEL", kernel)
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu" if kernel == "valu" else "mfma")
+    monkeypatch.setenv("AD_MFMA_ROWS", "1" if kernel == "mfma_rows" else "0")
 
 
 def run(w, num_splits=None):
