@@ -253,7 +253,10 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
  * profile): AD_KERNEL_VECTOR (vector ALUs, up to 8 query rows per work unit), AD_KERNEL_MATRIX
  * (matrix cores, 32 rows per unit: bf16 with more than 8 rows per KV head, and every fp8 cache)
  * or AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). Honours AD_PARTIAL_KERNEL as the calls
- * do. Checks the arguments as the calls do (out is not needed). */
+ * do. Checks the arguments as the calls do (out is not needed). On a bf16 cache the matrix-core
+ * kernel reads whole K / V rows and stages K through LDS when the grid holds more work groups
+ * than compute units, else K goes from HBM straight to the matrix cores; both give the same
+ * bits, and AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
 #define AD_KERNEL_VECTOR 0
 #define AD_KERNEL_MATRIX 1
 #define AD_KERNEL_MLA 2
