@@ -56,6 +56,8 @@ constexpr int kCopiesPerWave = kTile / kWaves + 1;  // latent row copies + one r
 constexpr int kKs = (kLatent + kRope) / 16;       // k-steps (16 values) of the score product
 constexpr int kLatKs = kLatent / 16;
 constexpr int kSlabs = kLatent / 32;              // 32-column slabs of the output
+constexpr int kStoreSlabs = 4;                     // slabs per transposed store group
+constexpr int kStageStride = 32 * kStoreSlabs + 4; // floats per staged row (the pad spreads banks)
 // All matrix-core accumulators of a kernel live in one register file (the accumulation registers
 // here), which holds 256 per lane: 15 output slabs plus the score accumulator fill it exactly. The
 // last output slab is therefore summed in ordinary registers: each tile's product for it goes
@@ -428,15 +430,33 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     float lr[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) lr[j] = s_x[wave][8 * (j / 4) + 4 * half + (j % 4)];
+    float inv[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int r = 8 * (j / 4) + 4 * half + (j % 4);
-        if (r < nr) {
-            const float inv = lr[j] > 0.f ? 1.f / lr[j] : 0.f;
-            float *dst = p.part_o + (out_row(r) * S + split) * kLatent + col;
+    for (int j = 0; j < 16; ++j) inv[j] = lr[j] > 0.f ? 1.f / lr[j] : 0.f;
+    // The accumulators hold one column per lane; the partial rows go out as 16-byte stores of
+    // four columns, transposed through this wave's ring slot (free since the loop's last
+    // barrier): kStoreSlabs slabs at a time as 32 rows of kStageStride floats.
+    lds_u8 *slot = wave == 0 ? (lds_u8 *)s_lat0 : wave == 1 ? (lds_u8 *)s_lat1 : wave == 2 ? (lds_u8 *)s_lat2 : (lds_u8 *)s_lat3;
+    __attribute__((address_space(3))) float *stage = (__attribute__((address_space(3))) float *)slot;
+    static_assert(kRowsPerWave * kStageStride * 4 <= kLatBytes, "a slab group fits a ring slot");
 #pragma unroll
-            for (int s = 0; s < kSlabs; ++s) dst[32 * s] = o[s][j] * inv;
+    for (int g = 0; g < kSlabs / kStoreSlabs; ++g) {
+#pragma unroll
+        for (int sl = 0; sl < kStoreSlabs; ++sl)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                stage[(8 * (j / 4) + 4 * half + (j % 4)) * kStageStride + 32 * sl + col] =
+                    o[kStoreSlabs * g + sl][j] * inv[j];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave / 2; ++i) {
+            const int r = 2 * i + half;  // lanes 0-31 row 2i, lanes 32-63 row 2i + 1: 4 columns each
+            const f32x4 v = *(const __attribute__((address_space(3))) f32x4 *)(stage + r * kStageStride + 4 * col);
+            if (r < nr)
+                *reinterpret_cast<f32x4 *>(p.part_o + (out_row(r) * S + split) * kLatent +
+                                           32 * kStoreSlabs * g + 4 * col) = v;
         }
+        __builtin_amdgcn_wave_barrier();
     }
     if (half == 0 && col < nr) {
         const float ms = (m == -INFINITY) ? 0.f : m;
