@@ -176,6 +176,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     __shared__ __attribute__((aligned(16))) unsigned char s_buf[kWaves * kRows * D * 4];
     __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
     __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
+    __shared__ float s_fw[kWaves][kRows], s_inv[kRows];  // combine weights of the waves' partials, 1 / l
     // fp8 cache: the scales of a wave's 32 tile keys, read back in the score accumulator's key order
     __shared__ __attribute__((aligned(16))) float s_ks[FP8 ? kWaves : 1][kTile], s_vs[FP8 ? kWaves : 1][kTile];
 
@@ -561,27 +562,34 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
         for (int j = 0; j < 16; ++j) s_o[(8 * (j / 4) + 4 * half + (j % 4)) * D + 32 * s + col] = o[s][j];
     __syncthreads();
 
-    const float *s_all = reinterpret_cast<const float *>(s_buf);
-    for (int i = tid; i < nr * D; i += kThreads) {
-        const int r = i / D, d = i - r * D;
+    // Per-row factors, once per row: the weight of each wave's partial and 1 / l. Stores are
+    // agent-scope: a merging group on another XCD reads them (fused merge).
+    if (tid < nr) {
+        const int r = tid;
         float M = s_m[0][r];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
         const float ms = (M == -INFINITY) ? 0.f : M;
-        float lsum = 0.f, lfsum = 0.f, acc = 0.f;
+        float lsum = 0.f, lfsum = 0.f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float f = exp2_fast(s_m[w][r] - ms);
+            s_fw[w][r] = f;
             lsum += s_l[w][r] * f;
             lfsum += s_lf[w][r] * f;
-            acc += s_all[(w * kRows + r) * D + d] * f;
         }
-        const int64_t row = out_row(r);
-        // agent-scope stores: a merging group on another XCD reads them (fused merge)
-        store_partial(p.part_o + (row * S + split) * Dv + d, lsum > 0.f ? acc / lsum : 0.f);
-        if (d == 0)
-            store_partial(p.part_lse + row * S + split,
-                          lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY);
+        s_inv[r] = lsum > 0.f ? 1.f / lsum : 0.f;
+        store_partial(p.part_lse + out_row(r) * S + split,
+                      lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY);
+    }
+    __syncthreads();
+    const float *s_all = reinterpret_cast<const float *>(s_buf);
+    for (int i = tid; i < nr * D; i += kThreads) {
+        const int r = i / D, d = i - r * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) acc += s_all[(w * kRows + r) * D + d] * s_fw[w][r];
+        store_partial(p.part_o + (out_row(r) * S + split) * Dv + d, acc * s_inv[r]);
     }
     if (p.counters) {  // one launch per step: the unit's last split merges (s_buf is free now)
         const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
