@@ -215,7 +215,17 @@ int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
     return sp ? (int64_t)sp->max_blocks * sp->block_size : (int64_t)a->kv_len_max;
 }
 
-constexpr int64_t kRaggedChunk = 2048;  // keys per split at most, when lengths may be ragged
+// Keys per split at most when lengths may be ragged. Measured on 64 paged sequences of
+// 128..8192 keys (8 KV heads, 4 query rows each), repeated same-box runs: the vector kernel takes
+// 191.8 us at 1664 keys (5 splits), 198.0 at 2048, 196.0 at 1366; the matrix-core kernel, whose
+// work group costs more to start and to combine, 224.3 us at 4096 keys (2 splits) against 230.0
+// at 2048 with 1-8 draft tokens, and 141.4 against 146.1 on an fp8 cache. The vector kernel's
+// shorter bound applies only to grids of several rounds at 2048, where shorter splits even out
+// the ragged tail; a grid of one round would spill into a second (16 sequences of 4096 keys:
+// 50 -> 56 us). Other paths (MLA) keep 2048.
+constexpr int64_t kRaggedChunkVector = 1664;
+constexpr int64_t kRaggedChunkMatrix = 4096;
+constexpr int64_t kRaggedChunk = 2048;
 
 int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
                 Plan *out) {
@@ -233,10 +243,19 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         // caches), doubled until every compute unit has a work group, never below 256 keys each.
         S = span >= 2048 ? 2 : 1;
         while (units * S < cus && span / (2 * S) >= 256 && S * 2 <= AD_MAX_SPLITS) S *= 2;
-        // Per-sequence lengths may be ragged: splits of at most kRaggedChunk keys keep the longest
-        // work group near the average share of a compute unit (a uniform cache is best served by
-        // the fewest splits that fill the compute units, as above).
-        if (a->seq_lens) S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, kRaggedChunk)), AD_MAX_SPLITS);
+        // Per-sequence lengths may be ragged: splits of a bounded length (the bounds above) keep
+        // the longest work group near the average share of a compute unit (a uniform cache is
+        // best served by the fewest splits that fill the compute units, as above).
+        if (a->seq_lens) {
+            int64_t most = kRaggedChunk;
+            if (path != Path::Mla) {
+                if (row_plan(a).mfma)
+                    most = kRaggedChunkMatrix;
+                else if (units * std::max<int64_t>(S, cdiv(span, kRaggedChunk)) >= 2 * (int64_t)cus)
+                    most = kRaggedChunkVector;
+            }
+            S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, most)), AD_MAX_SPLITS);
+        }
     }
     int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
     chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);

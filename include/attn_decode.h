@@ -175,7 +175,9 @@ typedef struct ad_sparse {
  * with head_dim_v == 512. The choice fills every compute unit with work units of a few hundred
  * tokens or more (cf. TensorRT-LLM xqa launchMHA: sub-sequences = min(SMs / (batch * kv heads),
  * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
- * keeps splits at most 2048 keys long, so that no work group is much longer than the average.
+ * bounds the split length, so that no work group is much longer than the average: 2048 keys,
+ * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
+ * the matrix-core kernel (whose work groups cost more to start and finish).
  * Environment AD_NUM_SPLITS forces the count (testing aid, cf. xqa's XQA_NB_SUB_SEQ).
  */
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
