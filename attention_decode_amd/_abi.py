@@ -19,6 +19,7 @@ AD_F32, AD_BF16 = 0, 1
 AD_KV_SAME, AD_KV_FP8_E4M3, AD_KV_INT4 = 0, 1, 2
 AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA = 0, 1, 2
 AD_MAX_SPLITS = 256
+AD_PROBE_SINK_WORDS = 4096
 STATUS = {0: "AD_OK", -1: "AD_E_NULL", -2: "AD_E_DTYPE", -3: "AD_E_SHAPE", -4: "AD_E_ALIGN",
           -5: "AD_E_UNSUPPORTED", -6: "AD_E_WORKSPACE", -7: "AD_E_RANGE"}
 _DTYPE = {torch.float32: AD_F32, torch.bfloat16: AD_BF16}
@@ -76,13 +77,14 @@ def lib():
         L = ctypes.CDLL(LIBRARY)
         P = ctypes.POINTER
         L.attn_decode_plan.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), P(ctypes.c_int32), P(ctypes.c_int32)]
-        L.attn_decode_workspace_size.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32]
+        L.attn_decode_workspace_size.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32]
         L.attn_decode_workspace_size.restype = ctypes.c_size_t
         L.attn_decode_splitkv.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_void_p, ctypes.c_void_p]
-        L.attn_decode_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+        L.attn_decode_merge.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                        ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p, ctypes.c_void_p]
+                                        ctypes.c_int32, ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
+                                        ctypes.c_void_p]
         L.attn_decode.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
         L.attn_decode_launches.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, P(ctypes.c_int32)]
@@ -95,6 +97,8 @@ def lib():
         L.attn_decode_mla_splitkv.argtypes = [P(DecodeArgs), ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_void_p,
                                               P(ctypes.c_int64), P(Paged), ctypes.c_int32, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_decode_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+        L.attn_decode_read_probe.restype = ctypes.c_int
         L.attn_decode_last_error.restype = ctypes.c_char_p
         for fn in ("attn_decode", "attn_decode_launches", "attn_decode_kernel", "attn_decode_plan", "attn_decode_splitkv", "attn_decode_merge", "attn_decode_paged",
                    "attn_decode_mla", "attn_decode_mla_splitkv"):
@@ -204,8 +208,10 @@ def attn_decode_plan(args: DecodeArgs, paged: Paged | None = None, sparse: Spars
     return S.value, C.value
 
 
-def attn_decode_workspace_size(args: DecodeArgs, paged: Paged | None = None, num_splits: int = 0) -> int:
-    n = lib().attn_decode_workspace_size(ctypes.byref(args), ctypes.byref(paged) if paged else None, num_splits)
+def attn_decode_workspace_size(args: DecodeArgs, paged: Paged | None = None, num_splits: int = 0,
+                               sparse: Sparse | None = None) -> int:
+    n = lib().attn_decode_workspace_size(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                                         ctypes.byref(sparse) if sparse else None, num_splits)
     if n == 0:
         raise ADError("attn_decode_workspace_size", 0, attn_decode_last_error())
     return n
@@ -219,12 +225,14 @@ def attn_decode_splitkv(args: DecodeArgs, paged: Paged | None, sparse: Sparse | 
                                      _ptr(part_o), _ptr(part_lse), _stream(stream)))
 
 
-def attn_decode_merge(part_o, part_lse, num_splits, out, lse=None, stream=None):
-    """part_o [B,Q,Hq,S,Dv] fp32, part_lse [B,Q,Hq,S] -> out [B,Q,Hq,Dv] (any strides), lse [B,Q,Hq]."""
+def attn_decode_merge(part_o, part_lse, num_splits, out, lse=None, stream=None, splits_per_batch=None):
+    """part_o [B,Q,Hq,S,Dv] fp32, part_lse [B,Q,Hq,S] -> out [B,Q,Hq,Dv] (any strides), lse [B,Q,Hq];
+    splits_per_batch: optional int32 device tensor [B], the leading splits of each sequence to merge."""
     B, Q, Hq, _, Dv = part_o.shape
     _check("attn_decode_merge",
-           lib().attn_decode_merge(_ptr(part_o), _ptr(part_lse), num_splits, B, Q, Hq, Dv, _DTYPE[out.dtype],
-                                   _ptr(out), I64x3(*out.stride()[:3]), _ptr(lse), _stream(stream)))
+           lib().attn_decode_merge(_ptr(part_o), _ptr(part_lse), _ptr(splits_per_batch), num_splits, B, Q, Hq, Dv,
+                                   _DTYPE[out.dtype], _ptr(out), I64x3(*out.stride()[:3]), _ptr(lse),
+                                   _stream(stream)))
 
 
 def attn_decode(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, num_splits: int, workspace,
@@ -275,3 +283,12 @@ def attn_decode_mla(args: DecodeArgs, kpe, q_pe, paged: Paged, num_splits: int, 
            lib().attn_decode_mla(ctypes.byref(args), _ptr(kpe), _s3(kpe), _ptr(q_pe), _s3(q_pe),
                                  ctypes.byref(paged), num_splits, _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_read_probe(src, sink, stream=None):
+    """Stream all of `src` (a 16-byte aligned device tensor) through the library's read probe;
+    sink: int32/uint32 device tensor of AD_PROBE_SINK_WORDS words."""
+    nbytes = src.numel() * src.element_size()
+    if sink.numel() < AD_PROBE_SINK_WORDS:
+        raise ValueError("sink too small")
+    _check("attn_decode_read_probe", lib().attn_decode_read_probe(_ptr(src), nbytes, _ptr(sink), _stream(stream)))

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "splitkv_valu.hip", "splitkv_mfma.hip", "mla_mfma.hip", "merge.hip"]
+SOURCES = ["api.cpp", "splitkv_valu.hip", "splitkv_mfma.hip", "mla_mfma.hip", "merge.hip", "probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]

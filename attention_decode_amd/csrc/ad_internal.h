@@ -141,6 +141,8 @@ struct MergeParams {
     int64_t out_s[3];
     float *lse;
     const int32_t *q_starts;  // nullable: rows of tokens t >= Q_b are skipped, out / lse packed
+    // nullable: row b merges only its first splits_per_batch[b] splits (clamped to [0, num_splits])
+    const int32_t *splits_per_batch;
 };
 
 // Launchers (hipSuccess or the launch error). They assume the host checks already passed.
@@ -149,5 +151,6 @@ hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, 
 hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_partial_mla(const PartialParams &p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
+hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int groups, hipStream_t stream);
 
 }  // namespace ad

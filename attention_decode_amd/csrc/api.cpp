@@ -61,6 +61,21 @@ int log2_exact(int x) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Testing aids (AD_NUM_SPLITS, AD_PARTIAL_KERNEL, AD_MFMA_ROWS, AD_FUSED_MERGE) are read only when
+// AD_TEST_KNOBS=1 is set, so that a stray variable in a serving process cannot change kernels or
+// plans; every call reads them afresh, so a test can switch them between calls.
+const char *knob(const char *name) {
+    const char *on = getenv("AD_TEST_KNOBS");
+    if (!on || strcmp(on, "1") != 0) return nullptr;
+    const char *v = getenv(name);
+    return (v && *v) ? v : nullptr;
+}
+
+int knob_int(const char *name) {
+    const char *s = knob(name);
+    return s ? atoi(s) : 0;
+}
+
 // ------------------------------------------------------------------ validation
 enum class Path { Contig, Paged, Mla };
 
@@ -166,7 +181,7 @@ struct Rows {
 
 Rows row_plan(const ad_decode_args *a) {
     const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
-    const char *force = getenv("AD_PARTIAL_KERNEL");
+    const char *force = knob("AD_PARTIAL_KERNEL");
     // an fp8 cache takes the matrix cores by default (the vector path converts too slowly)
     const bool fp8 = a->kv_format == AD_KV_FP8_E4M3, int4 = a->kv_format == AD_KV_INT4;
     bool mfma = a->dtype == AD_BF16 && (r > 8 || fp8) && !int4;
@@ -200,10 +215,6 @@ int device_cus(int *cus) {
     return AD_OK;
 }
 
-int env_int(const char *name) {
-    const char *s = getenv(name);
-    return s ? atoi(s) : 0;
-}
 
 struct Plan {
     int splits;
@@ -230,7 +241,8 @@ constexpr int64_t kRaggedChunk = 2048;
 int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
                 Plan *out) {
     const int64_t span = key_span(a, sp);
-    int S = requested > 0 ? requested : env_int("AD_NUM_SPLITS");
+    const int grain = pg ? pg->page_size : (sp ? sp->block_size : 16);
+    int S = requested > 0 ? requested : knob_int("AD_NUM_SPLITS");
     if (S < 0 || S > AD_MAX_SPLITS) return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", S, AD_MAX_SPLITS);
     if (S == 0) {
         int cus = 0;
@@ -256,10 +268,14 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
             }
             S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, most)), AD_MAX_SPLITS);
         }
+        // A split over a paged cache or a block list stages its page / block ids in LDS: never
+        // more of them than the map holds, whatever the bounds above chose (a multiple of 16).
+        if (pg || sp)
+            S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, (int64_t)(ad::kMapCapacity - 2) * grain)),
+                                       AD_MAX_SPLITS);
     }
     int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
     chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);
-    const int grain = pg ? pg->page_size : (sp ? sp->block_size : 16);
     if (pg || sp) {
         if (cdiv(chunk, grain) + 2 > ad::kMapCapacity)
             return fail(AD_E_RANGE, "%d splits leave %lld keys per split; at most %d pages/blocks per split", S,
@@ -328,9 +344,8 @@ hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mod
         // the price of a round trip through LDS per tile. That pays when a compute unit runs
         // several work groups in turn (2048 groups: 258 -> 238 us) and costs when each runs one
         // (256 groups: 33.9 -> 35.5 us). AD_MFMA_ROWS=0/1 forces the choice (testing aid).
-        const char *set = getenv("AD_MFMA_ROWS");
-        if (set && *set) {
-            p.mfma_rows = env_int("AD_MFMA_ROWS") != 0;
+        if (knob("AD_MFMA_ROWS")) {
+            p.mfma_rows = knob_int("AD_MFMA_ROWS") != 0;
         } else {
             int cus = 0;
             if (device_cus(&cus) != AD_OK) return hipErrorInvalidDevice;
@@ -378,10 +393,8 @@ size_t step_bytes(const ad_decode_args *a, int S, size_t *lse_offset) {
 // (at most 8, so its merge is short); otherwise two launches. AD_FUSED_MERGE=0/1 forces the
 // choice (testing aid).
 int fuse_merge(const ad_decode_args *a, Path path, int S, bool *fused) {
-    const int force = env_int("AD_FUSED_MERGE");
-    const char *set = getenv("AD_FUSED_MERGE");
-    if (set && *set) {
-        *fused = force != 0;
+    if (knob("AD_FUSED_MERGE")) {
+        *fused = knob_int("AD_FUSED_MERGE") != 0;
         return AD_OK;
     }
     int cus = 0;
@@ -415,7 +428,7 @@ int kv_mode(ad::PartialParams &p, const ad_paged *paged, const ad_sparse *sparse
 }
 
 int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, bool count_by_len, int chunk,
-              hipStream_t stream) {
+              hipStream_t stream, const int32_t *splits_per_batch = nullptr) {
     ad::MergeParams m{};
     m.part_o = po;
     m.part_lse = pl;
@@ -433,6 +446,7 @@ int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, 
     for (int i = 0; i < 3; ++i) m.out_s[i] = a->out_stride[i];
     m.lse = a->lse;
     m.q_starts = a->q_starts;
+    m.splits_per_batch = splits_per_batch;
     hipError_t e = ad::launch_merge(m, stream);
     if (e != hipSuccess) return hip_fail(e, "merge launch");
     return AD_OK;
@@ -457,13 +471,19 @@ int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad
     return ok();
 }
 
-size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits) {
+size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                                  int32_t num_splits) {
     const bool mla = args && args->head_dim_qk == 576 && args->head_dim_v == 512;
     const Path path = mla ? Path::Mla : (paged ? Path::Paged : Path::Contig);
     if (check_args(args, path, false) != AD_OK) return 0;
+    if (paged && sparse) {
+        fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+        return 0;
+    }
     if (paged && check_paged(args, paged) != AD_OK) return 0;
+    if (sparse && check_sparse(sparse) != AD_OK) return 0;
     Plan pl{};
-    if (plan_splits(args, paged, nullptr, path, num_splits, &pl) != AD_OK) return 0;
+    if (plan_splits(args, paged, sparse, path, num_splits, &pl) != AD_OK) return 0;
     ok();
     return step_bytes(args, pl.splits, nullptr);
 }
@@ -494,9 +514,9 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
     return ok();
 }
 
-int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_splits, int32_t batch, int32_t q_len,
-                      int32_t num_q_heads, int32_t head_dim_v, int32_t out_dtype, void *out,
-                      const int64_t out_stride[3], float *lse, void *stream) {
+int attn_decode_merge(const float *part_o, const float *part_lse, const int32_t *splits_per_batch,
+                      int32_t num_splits, int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t head_dim_v,
+                      int32_t out_dtype, void *out, const int64_t out_stride[3], float *lse, void *stream) {
     if (out_dtype != AD_F32 && out_dtype != AD_BF16) return fail(AD_E_DTYPE, "out_dtype %d unknown", out_dtype);
     if (num_splits < 1 || num_splits > AD_MAX_SPLITS)
         return fail(AD_E_RANGE, "num_splits %d outside [1, %d]", num_splits, AD_MAX_SPLITS);
@@ -506,8 +526,9 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
     if (head_dim_v != 64 && head_dim_v != 128 && head_dim_v != 256 && head_dim_v != 512 && head_dim_v != 1024)
         return fail(AD_E_UNSUPPORTED, "head_dim_v %d not in {64, 128, 256, 512, 1024}", head_dim_v);
     if (!aligned16(part_o) || (reinterpret_cast<uintptr_t>(part_lse) & 3u) || !aligned16(out) ||
-        !strides_aligned(out_stride, elem_bytes(out_dtype)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
-        return fail(AD_E_ALIGN, "misaligned part_o / part_lse / out / lse");
+        !strides_aligned(out_stride, elem_bytes(out_dtype)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) ||
+        (reinterpret_cast<uintptr_t>(splits_per_batch) & 3u))
+        return fail(AD_E_ALIGN, "misaligned part_o / part_lse / splits_per_batch / out / lse");
     ad_decode_args a{};
     a.dtype = out_dtype;
     a.batch = batch;
@@ -517,7 +538,7 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
     a.out = out;
     for (int i = 0; i < 3; ++i) a.out_stride[i] = out_stride[i];
     a.lse = lse;
-    int rc = run_merge(&a, part_o, part_lse, num_splits, false, 1, static_cast<hipStream_t>(stream));
+    int rc = run_merge(&a, part_o, part_lse, num_splits, false, 1, static_cast<hipStream_t>(stream), splits_per_batch);
     return rc == AD_OK ? ok() : rc;
 }
 
@@ -694,6 +715,18 @@ int attn_decode_mla_splitkv(const ad_decode_args *args, const void *kpe, const i
     p.part_lse = part_lse;
     hipError_t e = ad::launch_partial_mla(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "MLA split-KV launch");
+    return ok();
+}
+
+int attn_decode_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream) {
+    if (!src || !sink) return fail(AD_E_NULL, "src or sink is NULL");
+    if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u))
+        return fail(AD_E_ALIGN, "src must be 16-byte and sink 4-byte aligned");
+    if (bytes == 0 || bytes % 16 || bytes > (size_t(1) << 40))
+        return fail(AD_E_RANGE, "bytes must be a nonzero multiple of 16 (at most 2^40)");
+    hipError_t e = ad::launch_read_probe(src, (int64_t)bytes, sink, AD_PROBE_SINK_WORDS / 4,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "read probe launch");
     return ok();
 }
 

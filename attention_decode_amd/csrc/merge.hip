@@ -7,7 +7,8 @@
 // partial row is read with one coalesced wave-wide load. The split weights are wave-uniform:
 // the row index is made uniform with readfirstlane, so the LSE reads become scalar loads and the
 // exponentials are computed once per split per lane without any cross-lane traffic beyond the
-// max. Ragged batches (paged path) merge only the ceil(L_b / chunk) splits that hold keys. With
+// max. Ragged batches merge only the splits that hold keys: ceil(L_b / chunk) on the whole-step
+// paths, or the caller's count per sequence (splits_per_batch) on the public merge. With
 // variable query lengths the rows of tokens past a sequence's count are skipped, and the others
 // are written to their packed output rows.
 #include "ad_internal.h"
@@ -38,6 +39,7 @@ __global__ void __launch_bounds__(64 * kRowsPerBlock) merge_kernel(const MergePa
         const int Sb = Lb > 0 ? (Lb + p.chunk - 1) / p.chunk : 0;
         S = min(S, Sb);
     }
+    if (p.splits_per_batch) S = min(S, max(p.splits_per_batch[b], 0));
     const float *ls = p.part_lse + (int64_t)row * p.num_splits;
     const float *po = p.part_o + (int64_t)row * p.num_splits * Dv + lane * VEC;
     // The partial rows of the first 4 splits are loaded before the LSEs are read, so that both

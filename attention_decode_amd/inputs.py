@@ -28,7 +28,9 @@ The workloads (sizes of the decode benchmarks this library is measured on; 6 is 
 
 Cache layouts: a contiguous cache is stored head-major ``[B, Hkv, L, D]``; a paged pool is stored
 ``[pages, Hkv, page_size, D]``. Both are handed out as token-major *views* ``[B, L, Hkv, D]`` /
-``[pages, page_size, Hkv, D]`` whose strides say where the data really is.
+``[pages, page_size, Hkv, D]`` whose strides say where the data really is. ``token_major(w)``
+re-stores the same cache token-major (``[B, L, Hkv, D]`` / ``[pages, page_size, Hkv, D]`` in
+memory, every key's heads side by side), with the same values.
 """
 from __future__ import annotations
 
@@ -84,6 +86,11 @@ class Workload:
     # [token rows, ceil(q_len / 32)])
     q_starts: torch.Tensor | None = None
     tree_mask: torch.Tensor | None = None
+    # "head": the cache (and its row scales) stored head-major; "token": stored token-major
+    layout: str = "head"
+    # False: the library is told nothing about per-sequence lengths (seq_lens = NULL, every
+    # sequence has kv_len_max keys); seq_lens still holds those lengths for the reference
+    lens_given: bool = True
     storage: dict = field(default_factory=dict)
 
     def to(self, device) -> "Workload":
@@ -121,6 +128,19 @@ class Workload:
                 row.append(n * per_tok)
             out.append(row)
         return out
+
+    def kv_bytes_listed(self) -> int:
+        """Bytes of every listed block of a block-sparse cache inside its sequence (each key once per
+        KV head), whether or not a query row sees it; kv_bytes() for other caches."""
+        if self.num_blocks is None:
+            return self.kv_bytes()
+        per_tok = self.bytes_per_key()
+        n = 0
+        for b, L in enumerate(int(x) for x in self.seq_lens.to("cpu")):
+            for h in range(self.num_kv_heads):
+                for blk in self.block_idx[b, h, :int(self.num_blocks[b, h])].tolist():
+                    n += max(0, min((blk + 1) * self.block_size, L) - blk * self.block_size)
+        return n * per_tok
 
     def q_counts(self) -> list:
         """Query tokens of each sequence: q_len, or the differences of q_starts."""
@@ -170,14 +190,34 @@ def _randn(g, shape, dtype):
 
 
 def _finish(w: Workload) -> Workload:
+    token = w.layout == "token"
     for f, (src, perm) in _VIEWS[w.kind].items():
-        setattr(w, f, w.storage[src].permute(*perm) if perm else w.storage[src])
-    for f in ("k_scale", "v_scale"):  # row scales of an fp8 cache, stored head-major like the cache
+        cache = f in ("k", "v") and w.kind != "mla"
+        setattr(w, f, w.storage[src].permute(*perm) if perm and not (cache and token) else w.storage[src])
+    for f in ("k_scale", "v_scale"):  # row scales of an fp8 cache, stored like the cache
         t = w.storage.get(f)
         if t is not None:
             rows = tuple(w.k.shape[:3])
-            setattr(w, f, t.reshape(1, 1, 1).expand(*rows) if t.numel() == 1 else t.permute(0, 2, 1))
+            setattr(w, f, t.reshape(1, 1, 1).expand(*rows) if t.numel() == 1 else t if token else t.permute(0, 2, 1))
     return w
+
+
+def token_major(w: Workload) -> Workload:
+    """The same workload with its contiguous or paged cache (and fp8 row scales) stored token-major:
+    [B, L, Hkv, D] / [pages, page_size, Hkv, D] in memory instead of head-major. Values, lengths,
+    page tables and block lists are unchanged, so the logical cache is the same bit for bit."""
+    if w.kind == "mla" or w.layout == "token":
+        raise ValueError("token_major takes a head-major contiguous or paged workload")
+    out = copy.copy(w)
+    out.storage = dict(w.storage)
+    for name in ("k", "v"):
+        out.storage[name] = w.storage[name].permute(0, 2, 1, 3).contiguous()
+    for name in ("k_scale", "v_scale"):
+        t = w.storage.get(name)
+        if t is not None and t.numel() > 1:
+            out.storage[name] = t.permute(0, 2, 1).contiguous()
+    out.layout = "token"
+    return _finish(out)
 
 
 E4M3_MAX = 448.0  # largest finite OCP E4M3 magnitude

@@ -31,7 +31,8 @@ class DecodeStep:
         self.out = torch.empty(*rows, Hq, Dv, dtype=w.dtype, device=dev) if out is None else out
         self.lse = torch.empty(*rows, Hq, dtype=torch.float32, device=dev) if lse is None else lse
         forced = num_splits if num_splits is not None else (w.num_splits or 0)
-        common = dict(scale=w.scale, seq_lens=w.seq_lens, kv_len_max=w.kv_len_max, causal=w.causal,
+        common = dict(scale=w.scale, seq_lens=w.seq_lens if w.lens_given else None, kv_len_max=w.kv_len_max,
+                      causal=w.causal,
                       window=w.window, out=self.out, lse=self.lse, q_starts=w.q_starts,
                       q_len=w.q_len if w.q_starts is not None else None, tree_mask=w.tree_mask)
         self.sparse = self.paged = None
@@ -47,7 +48,7 @@ class DecodeStep:
         self.splits = forced or _abi.attn_decode_plan(self.args, self.paged, self.sparse)[0]
         if self.fused or w.kind == "mla":
             # zero-filled once: the single-launch merge counts arrivals in it and leaves it zeroed
-            nbytes = _abi.attn_decode_workspace_size(self.args, self.paged, self.splits)
+            nbytes = _abi.attn_decode_workspace_size(self.args, self.paged, self.splits, self.sparse)
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         else:
             self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)

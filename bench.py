@@ -97,7 +97,7 @@ class Step:
         # in a workspace zero-filled once. MLA: the partial pass, then the merge kernel.
         self.fused = w.kind != "mla"
         if self.fused:
-            nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits)
+            nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits, self.sparse)
             self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
             self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
             kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
@@ -160,10 +160,11 @@ def oracle_kwargs(w):
     return kw
 
 
-def cpu_baseline(w_cpu, budget_s=12.0):
-    """The fp64 oracle, as it stands, on whole (sequence, KV head) groups of the workload (all
-    their query rows) until about budget_s seconds of host work; reported in the metric's unit
-    (algorithmic KV GB/s)."""
+def cpu_baseline(w_cpu, budget_s=24.0):
+    """The fp64 oracle, as it stands, on whole (sequence, KV head) groups of the workload (all their
+    query rows), reported in the metric's unit (algorithmic KV GB/s). A fixed sample of groups is
+    timed three times with every host thread and a smaller prefix of it three times with one
+    thread; each figure is the median of its three runs. About budget_s seconds in all."""
     import oracle
 
     orc = oracle.load()
@@ -175,45 +176,119 @@ def cpu_baseline(w_cpu, budget_s=12.0):
     by_group = w_cpu.kv_bytes_by_group()
     kw = oracle_kwargs(w_cpu)
     v = w_cpu.k if w_cpu.kind == "mla" else w_cpu.v
-    done_bytes, elapsed, groups = 0, 0.0, 0
     order = [(b, h) for b in range(w_cpu.batch) for h in range(Hkv)]
-    i = 0
-    # Whole (sequence, KV head) groups in a fixed order, wrapping around, until the budget is spent.
-    while elapsed < budget_s:
-        # next chunk of groups: grow geometrically so the timing overhead stays negligible
-        n = max(1, min(len(order) - i, 2 ** min(groups.bit_length(), 6)))
-        sel = order[i:i + n]
+
+    def run(groups):
+        sel = [order[i % len(order)] for i in range(groups)]
         rows = [(first[b] + t) * Hq + h * G + g for (b, h) in sel for t in range(counts[b]) for g in range(G)]
         t0 = time.perf_counter()
         orc.attend(w_cpu.q, w_cpu.k, v, rows=rows, **kw)
-        elapsed += time.perf_counter() - t0
-        done_bytes += sum(by_group[b][h] for (b, h) in sel)
-        groups += n
-        i = (i + n) % len(order)
-    return {"value": round(done_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": orc.threads(),
-            "kind": "oracle",
-            "sample": f"{groups} (sequence, KV head) groups of the {len(order)} in the workload (in order, "
-                      f"wrapping), all {G} x (query tokens) rows each: {done_bytes / 1e6:.1f} MB of KV in "
-                      f"{elapsed:.1f} s"}
+        return time.perf_counter() - t0, sum(by_group[b][h] for (b, h) in sel)
+
+    def sample_for(seconds):
+        """Groups (in order, wrapping) that take about `seconds` at the current thread count."""
+        n = 1
+        while True:
+            t, _ = run(n)
+            if t >= seconds / 8 or n >= 1 << 20:
+                return max(1, int(n * seconds / max(t, 1e-6)))
+            n *= 2
+
+    def median3(groups):
+        runs = sorted(run(groups) for _ in range(3))
+        t, nbytes = runs[1]
+        return nbytes / t / 1e9, nbytes, t
+
+    threads = os.cpu_count() or 1
+    orc.set_threads(threads)
+    used = orc.threads()
+    n_all = sample_for(budget_s / 6)
+    gbps, nbytes, t = median3(n_all)
+    orc.set_threads(1)
+    n_one = min(n_all, sample_for(budget_s / 6))
+    gbps1, nbytes1, t1 = median3(n_one)
+    orc.set_threads(used)
+    return {"value": round(gbps, 4), "unit": "GB/s", "cores": used, "kind": "oracle",
+            "sample": f"{n_all} (sequence, KV head) groups of the {len(order)} in the workload (in order, "
+                      f"wrapping), all {G} x (query tokens) rows each: {nbytes / 1e6:.1f} MB of KV, median of 3 "
+                      f"runs on {used} threads ({t:.2f} s)",
+            "single_thread": {"value": round(gbps1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"the first {n_one} of those groups: {nbytes1 / 1e6:.1f} MB of KV, median "
+                                        f"of 3 runs on 1 thread ({t1:.2f} s)"}}
+
+
+TRAFFIC_SOURCES = ["attention_decode_amd/csrc/api.cpp", "attention_decode_amd/csrc/ad_internal.h"]
+
+
+def sources_sha256(paths):
+    """One sha256 over the named files, in order (the kernel's source, the planner, the parameter block)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(hashlib.sha256(f.read()).digest())
+    return h.hexdigest()
 
 
 def load_traffic(kernel_tag):
     """HBM traffic of the dominant kernel from committed rocprofv3 counter runs, or None when the
-    kernel source changed since the counters were taken."""
-    import hashlib
-
+    kernel's source, the split planner or the parameter block changed since the counters were
+    taken (a planner change moves splits, and with them the traffic)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_tag}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src):
+    srcs = rec.get("sources")
+    if not srcs or any(not os.path.exists(os.path.join(ROOT, x)) for x in srcs):
         return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if h != rec.get("source_sha256"):
+    if sources_sha256(srcs) != rec.get("sources_sha256"):
         return None
     return rec.get("bytes_per_launch")
+
+
+def stream_peak(stream):
+    """Same-process streaming calibration, before the warm-up steps (it also brings the GPU out of
+    idle): the library's read probe (attn_decode_read_probe: the partial passes' load form, every
+    work group streaming its own region) over 2 GiB, and a torch device copy of 1 GiB for context;
+    5 launches each after 2 warm-ups, timed with events on `stream`. GB/s of bytes moved (read for
+    the probe; read + written for the copy)."""
+    import torch
+
+    from attention_decode_amd import _abi
+
+    out = {}
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x = torch.zeros(512 << 20, dtype=torch.int32, device="cuda")   # 2 GiB
+    sink = torch.empty(_abi.AD_PROBE_SINK_WORDS, dtype=torch.int32, device="cuda")
+    for _ in range(2):
+        _abi.attn_decode_read_probe(x, sink)
+    a.record(stream)
+    for _ in range(5):
+        _abi.attn_decode_read_probe(x, sink)
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["read_probe"] = round(x.numel() * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del x
+    y = torch.ones(256 << 20, device="cuda")             # 1 GiB
+    z = torch.empty_like(y)
+    for _ in range(2):
+        z.copy_(y)
+    a.record(stream)
+    for _ in range(5):
+        z.copy_(y)
+    b.record(stream)
+    torch.cuda.synchronize()
+    out["torch_copy"] = round(2 * y.numel() * 4 * 5 / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del y, z
+    torch.cuda.empty_cache()
+    return out
+
+
+def pct(xs, q):
+    """The q-quantile (0..1) of sorted xs, nearest rank."""
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
 
 
 def main():
@@ -265,6 +340,8 @@ def main():
         f"{copies} cache copies ({footprint / 1e6:.0f} MB each)")
 
     stream = torch.cuda.current_stream()
+    log("streaming calibration ...")
+    peak = stream_peak(stream)
     for i in range(args.warmup):
         step.partial(i)
         step.merge()
@@ -298,19 +375,29 @@ def main():
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     kern_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    # 4) the step's spread: whole steps, each between its own events
+    for i in range(K):
+        ev[i][0].record(stream)
+        step.partial(i)
+        step.merge()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = sorted(a.elapsed_time(b) for a, b in ev)
     gbps = kv_bytes / (ms_step * 1e-3) / 1e9
     achieved = kv_bytes / (kern_avg * 1e-3) / 1e9
     tflops = flops / (kern_avg * 1e-3) / 1e12
     log(f"step {ms_step * 1e3:.1f} us ({gbps:.0f} GB/s, {gbps / HBM_PEAK_GBPS:.1%} of 8 TB/s); {step.kernel_name} "
         f"alone {kern_avg * 1e3:.1f} us -> {achieved:.0f} GB/s, {tflops:.0f} TFLOP/s (one launch between events: "
-        f"p10 {kern_ms[K // 10] * 1e3:.1f}, p50 {kern_ms[K // 2] * 1e3:.1f}, p90 {kern_ms[(9 * K) // 10] * 1e3:.1f} us)")
+        f"p10 {pct(kern_ms, .1) * 1e3:.1f}, p50 {pct(kern_ms, .5) * 1e3:.1f}, p90 {pct(kern_ms, .9) * 1e3:.1f} us); "
+        f"streaming calibration {peak}")
 
     tag, kname = KERNELS[args.workload]
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": load_traffic(tag),
                 "kernel": step.kernel_name, "kernel_avg_us": round(kern_avg * 1e3, 3),
-                "kernel_event_us_p10_p50_p90": [round(kern_ms[K // 10] * 1e3, 2), round(kern_ms[K // 2] * 1e3, 2),
-                                                round(kern_ms[(9 * K) // 10] * 1e3, 2)]}
+                "kernel_event_us_p10_p50_p90": [round(pct(kern_ms, q) * 1e3, 2) for q in (.1, .5, .9)],
+                "measured_stream_GBps": peak,
+                "frac_of_measured_stream": round(achieved / peak["read_probe"], 4)}
     if w.kind == "mla":
         roofline["mfma_tflops"] = round(tflops, 1)
         roofline["mfma_frac"] = round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)
@@ -324,8 +411,14 @@ def main():
         config["tree_mask"] = True
     if w.page_size:
         config["page_size"] = w.page_size
+    config["kv_bytes_convention"] = ("each key once per KV head (K and V rows; MLA: latent + rotary row once) if "
+                                     "it is inside its sequence, inside a listed block and visible to at least "
+                                     "one query row")
     if w.num_blocks is not None:
         config["sparse_block"] = w.block_size
+        listed = w_cpu.kv_bytes_listed()
+        config["kv_bytes_listed_blocks"] = listed
+        config["value_on_listed_blocks_GBps"] = round(listed / (ms_step * 1e-3) / 1e9, 2)
     if w.causal or w.window:
         config.update(causal=bool(w.causal), window=w.window)
     result = {
@@ -337,6 +430,8 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
         "us_per_step": round(ms_step * 1e3, 2),
+        "step_event_us_p10_p50_p90": [round(pct(step_ms, q) * 1e3, 2) for q in (.1, .5, .9)],
+        "frac_of_measured_stream": round(gbps / peak["read_probe"], 4),
         "hbm_peak_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "higher_is_better": True,
         "scaling": "weak",

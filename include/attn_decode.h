@@ -18,13 +18,24 @@
  *   - Every tensor pointer is DEVICE memory owned by the caller; descriptors (the structs and
  *     the stride arrays) are HOST memory, read during the call only. The library allocates no
  *     device memory, never synchronises and never throws. Work is enqueued on `stream` (a
- *     hipStream_t; NULL = the default stream) and runs asynchronously.
+ *     hipStream_t; NULL = the default stream) and runs asynchronously. This is the launch
+ *     contract of the pages' kernels: TensorRT-LLM xqa mha.cu's launchMHA takes its semaphores
+ *     and scratch buffers from the caller and enqueues on the caller's stream, and FlashInfer
+ *     attention/mla.cuh's BatchMLAPagedAttention takes partial_o / partial_lse inside its Params
+ *     and launches on the given stream. Where xqa throws (runtime_error on an unsupported input),
+ *     this C ABI returns a status instead, as mla.cuh's launcher returns a cudaError_t.
  *   - Strides are in ELEMENTS (bytes for an fp8 cache, 32-bit words for an int4 cache). The
  *     last (feature) dimension of every tensor is contiguous, and every row start must be
  *     16-byte aligned (int4 cache rows: 4-byte aligned).
  *   - Return value: AD_OK (0), a negative AD_E_* code when the arguments were rejected on the
- *     host before anything was enqueued, or a positive hipError_t when a launch failed.
+ *     host before anything was enqueued, or a positive hipError_t when a launch failed (the
+ *     status-code style of FlashInfer mla.cuh's BatchMLAPagedAttention, which returns
+ *     cudaErrorNotSupported with a message for a configuration it has no kernel for).
  *     attn_decode_last_error() gives a message for the calling thread's last non-OK return.
+ *   - Testing aids: the environment variables AD_NUM_SPLITS (split count, cf. xqa's
+ *     XQA_NB_SUB_SEQ), AD_PARTIAL_KERNEL, AD_MFMA_ROWS and AD_FUSED_MERGE (kernel forms, named at
+ *     the calls they affect) are read only while AD_TEST_KNOBS=1 is set; otherwise the
+ *     environment changes nothing.
  *   - Data contracts that are NOT checked (they live in device memory): seq_lens[b] <=
  *     kv_len_max and >= the sequence's query tokens; q_starts nondecreasing with counts of at
  *     most q_len; block-table entries for the pages a sequence covers lie in
@@ -177,20 +188,27 @@ typedef struct ad_sparse {
  * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
  * bounds the split length, so that no work group is much longer than the average: 2048 keys,
  * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
- * the matrix-core kernel (whose work groups cost more to start and finish).
- * Environment AD_NUM_SPLITS forces the count (testing aid, cf. xqa's XQA_NB_SUB_SEQ).
+ * the matrix-core kernel (whose work groups cost more to start and finish). A split of a paged
+ * cache or a block list never covers more than 1038 pages or blocks (the ids it stages), which
+ * raises the count for very long caches of small pages. AD_NUM_SPLITS forces the count
+ * (testing aid, see the conventions above).
  */
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                      int32_t *num_splits, int32_t *chunk);
 
 /* Bytes of workspace attn_decode / attn_decode_paged / attn_decode_mla need for `num_splits`
- * splits (0: the planner's choice; with a block list, pass the count attn_decode_plan returns for
- * it). Layout, the same for every entry point, shape and split count: AD_COUNTER_BYTES of arrival
+ * splits (0: the planner's choice) with the same `paged` / `sparse` (both nullable; a block list
+ * changes the planner's choice, so pass the one the call will carry). The caller owns and sizes
+ * this memory, as TensorRT-LLM xqa mha.cu's caller provides the `scratch` buffer of its
+ * multi-block mode and FlashInfer mla.cuh's caller the partial_o / partial_lse arrays of Params.
+ * Layout, the same for every entry point, shape and split count: AD_COUNTER_BYTES of arrival
  * counters (one 4-byte counter per work unit = sequence x KV head x block of query rows, at most
- * AD_COUNTER_BYTES / 4 units per call), then the partials, rows * splits * (head_dim_v + 1) * 4
- * bytes in 256-byte aligned parts. Returns 0 for arguments the calls would reject. */
+ * AD_COUNTER_BYTES / 4 units per call; xqa's `semaphores`), then the partials,
+ * rows * splits * (head_dim_v + 1) * 4 bytes in 256-byte aligned parts. Returns 0, with a message
+ * for attn_decode_last_error(), for arguments the calls would reject. */
 #define AD_COUNTER_BYTES (1u << 20)
-size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, int32_t num_splits);
+size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                                  int32_t num_splits);
 
 /*
  * Partial pass. The cache is contiguous (paged == NULL) or paged; a contiguous cache may carry a
@@ -213,13 +231,17 @@ int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const
  * LSE-weighted merge of num_splits partials per row (mslk splitk_kernels.py, _splitK_reduce):
  *   M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
  *   lse = M + ln sum_s w_s;  M = -inf gives out = 0, lse = -inf.
- * part_o / part_lse use the layout attn_decode_splitkv writes. out [batch, q_len, num_q_heads,
- * head_dim_v] in out_dtype with element strides out_stride {b, t, hq}; lse nullable, contiguous.
- * head_dim_v is a multiple of 64, at most 1024.
+ * part_o / part_lse use the layout attn_decode_splitkv writes. splits_per_batch (device, [batch],
+ * nullable) gives the number of leading splits of each sequence that hold partials: row b merges
+ * splits 0 .. min(splits_per_batch[b], num_splits) - 1 and never reads the others, so a ragged
+ * batch whose short sequences left later slots unwritten merges correctly (a count <= 0 gives
+ * out = 0, lse = -inf). NULL merges all num_splits slots of every row. out [batch, q_len,
+ * num_q_heads, head_dim_v] in out_dtype with element strides out_stride {b, t, hq}; lse nullable,
+ * contiguous. head_dim_v is 64, 128, 256, 512 or 1024.
  */
-int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_splits, int32_t batch,
-                      int32_t q_len, int32_t num_q_heads, int32_t head_dim_v, int32_t out_dtype,
-                      void *out, const int64_t out_stride[3], float *lse, void *stream);
+int attn_decode_merge(const float *part_o, const float *part_lse, const int32_t *splits_per_batch,
+                      int32_t num_splits, int32_t batch, int32_t q_len, int32_t num_q_heads, int32_t head_dim_v,
+                      int32_t out_dtype, void *out, const int64_t out_stride[3], float *lse, void *stream);
 
 /*
  * Whole decode step, writing args->out / args->lse: the partial pass of attn_decode_splitkv
@@ -230,8 +252,8 @@ int attn_decode_merge(const float *part_o, const float *part_lse, int32_t num_sp
  * arrival (the multi-block mode of TensorRT-LLM xqa mha.cu: a semaphore increment picks the last
  * CTA, which merges). One launch is used when the step is a single round of work groups (at most
  * one group per compute unit) whose units hold at most 8 query rows, else the
- * partial pass and the merge kernel run as two launches in the same workspace. Environment
- * AD_FUSED_MERGE=0 / 1 forces two launches / one launch (testing aid).
+ * partial pass and the merge kernel run as two launches in the same workspace. AD_FUSED_MERGE=0 / 1
+ * forces two launches / one launch (testing aid, see the conventions above).
  * workspace: device memory of at least attn_decode_workspace_size(args, paged, num_splits)
  * bytes, 256-byte aligned. Its first AD_COUNTER_BYTES MUST be zero before its first use (zero
  * the allocation once); every call leaves them zero and writes its partials only after them, so
@@ -254,11 +276,11 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
 /* Which partial-pass kernel the calls above run for these arguments (e.g. to name it in a
  * profile): AD_KERNEL_VECTOR (vector ALUs, up to 8 query rows per work unit), AD_KERNEL_MATRIX
  * (matrix cores, 32 rows per unit: bf16 with more than 8 rows per KV head, and every fp8 cache)
- * or AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). Honours AD_PARTIAL_KERNEL as the calls
- * do. Checks the arguments as the calls do (out is not needed). On a bf16 cache the matrix-core
- * kernel reads whole K / V rows and stages K through LDS when the grid holds more work groups
- * than compute units, else K goes from HBM straight to the matrix cores; both give the same
- * bits, and AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
+ * or AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). Honours AD_PARTIAL_KERNEL=valu / mfma
+ * as the calls do (testing aid). Checks the arguments as the calls do (out is not needed). On a
+ * bf16 cache the matrix-core kernel reads whole K / V rows and stages K through LDS when the grid
+ * holds more work groups than compute units, else K goes from HBM straight to the matrix cores;
+ * both give the same bits, and AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
 #define AD_KERNEL_VECTOR 0
 #define AD_KERNEL_MATRIX 1
 #define AD_KERNEL_MLA 2
@@ -295,8 +317,24 @@ int attn_decode_mla_splitkv(const ad_decode_args *args, const void *kpe, const i
                             const void *q_pe, const int64_t q_pe_stride[3], const ad_paged *paged,
                             int32_t num_splits, float *part_o, float *part_lse, void *stream);
 
-/* Message for the calling thread's last non-OK return ("" if none). Valid until the thread's
- * next call into the library. */
+/*
+ * Measurement aid, not part of a decode step: reads `bytes` of device memory at `src` (16-byte
+ * aligned, a nonzero multiple of 16) with the load form of the partial passes -- every work group
+ * streams its own contiguous region with 16-byte nontemporal loads, a wave instruction covering
+ * whole 128-byte lines -- and writes AD_PROBE_SINK_WORDS 32-bit words of XOR-folded data to
+ * `sink` (device) so that no load is dropped. The time of the call divided into `bytes` is the HBM
+ * read rate this access form reaches, the practical ceiling the decode kernels are compared with
+ * beside the published peak (the pages' kernels are likewise judged by their share of the
+ * bandwidth their loads can reach).
+ */
+#define AD_PROBE_SINK_WORDS 4096
+int attn_decode_read_probe(const void *src, size_t bytes, uint32_t *sink, void *stream);
+
+/* Message for the calling thread's last non-OK return ("" if none; every successful call clears
+ * it). Valid until the thread's next call into the library. The message is the text FlashInfer
+ * mla.cuh's launcher raises with its error code (the shared-memory configuration it cannot
+ * serve) and TensorRT-LLM xqa mha.cu throws; a C ABI keeps it per thread instead, beside the
+ * status the call returned. Never NULL; owned by the library. */
 const char *attn_decode_last_error(void);
 
 #ifdef __cplusplus

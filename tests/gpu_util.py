@@ -64,3 +64,41 @@ def assert_matches(out, lse, ref_o, ref_l, dtype, what=""):
     assert mism == 0, f"{what}: rows with no visible key disagree"
     assert e_out <= tol_o, f"{what}: out error {e_out} > {tol_o}"
     assert e_lse <= tol_l, f"{what}: lse error {e_lse} > {tol_l}"
+
+
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 numbers at |x| (the most that rounding x to bf16 can move it)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.maximum(a, 2.0 ** -126))   # a = m * 2^e with m in [0.5, 1)
+    return np.ldexp(1.0, e - 9)                     # ulp 2^(e - 8), half of it
+
+
+# Regression bounds of the full-size workloads, next to the contract tolerances above: what the
+# kernels reach, with room for box-to-box noise. lse: a key dropped from a 4096-key softmax moves
+# the LSE by about 2.4e-4, which these bounds catch. out: the error beyond the output's own bf16
+# rounding (at most half a bf16 spacing of the reference value), as a maximum, and the mean error
+# against the mean of that half spacing: rounding to nearest even averages about half of it plus
+# the rounding of P, truncation about all of it, so a bias shows in the mean.
+TIGHT = {torch.float32: dict(lse=2e-6, excess=2e-6, mean_abs=1e-7),
+         torch.bfloat16: dict(lse=1e-4, excess=2e-3, mean_rel=1.2, mean_abs=2e-5)}
+
+
+def assert_tight(out, lse, ref_o, ref_l, dtype, what=""):
+    """Contract tolerances (assert_matches), then the tighter regression bounds of TIGHT."""
+    assert_matches(out, lse, ref_o, ref_l, dtype, what)
+    o = out.double().cpu().numpy().reshape(ref_o.shape)
+    l_ = lse.double().cpu().numpy().reshape(ref_l.shape)
+    fin = np.isfinite(ref_l)
+    e_lse = float(np.max(np.abs(l_[fin] - ref_l[fin]), initial=0.0))
+    d = np.abs(o - ref_o)
+    half = bf16_half_ulp(ref_o) if dtype == torch.bfloat16 else np.zeros_like(ref_o)
+    excess = float(np.max(d - half, initial=0.0))
+    mean = float(np.mean(d)) if d.size else 0.0
+    b = TIGHT[dtype]
+    mean_bound = b.get("mean_rel", 0.0) * (float(np.mean(half)) if d.size else 0.0) + b["mean_abs"]
+    say(f"  {what} regression: max|dlse| {e_lse:.2e} (bound {b['lse']:g}), max error beyond output "
+        f"rounding {excess:.2e} (bound {b['excess']:g}), mean|dout| {mean:.2e} (bound {mean_bound:.2e}; "
+        f"mean half bf16 spacing {float(np.mean(half)) if d.size else 0.0:.2e})")
+    assert e_lse <= b["lse"], f"{what}: lse error {e_lse} above the regression bound"
+    assert excess <= b["excess"], f"{what}: out error beyond rounding {excess} above the regression bound"
+    assert mean <= mean_bound, f"{what}: mean out error {mean} above the regression bound {mean_bound}"

@@ -121,7 +121,7 @@ def test_many_rows_per_kv_head_pass_validation():
         rows = 2 * Q * Hq
         # the fixed arrival-counter region, then partial outputs and partial LSEs
         expect = (1 << 20) + -(-rows * 2 * 128 * 4 // 256) * 256 + -(-rows * 2 * 4 // 256) * 256
-        assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, 2) == expect
+        assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, None, 2) == expect
 
 
 def test_splitkv_rejects_misaligned_rows():
@@ -198,7 +198,7 @@ def test_paged_rejects_small_workspace():
     # 2 splits: the 1 MiB arrival-counter region, then rows 16 * 2 * 128 * 4 = 16 KiB of partial
     # outputs + 256 B of LSEs
     need = (1 << 20) + 16384 + 256
-    assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), 2) == need
+    assert _abi.lib().attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), None, 2) == need
     assert _paged_call(a, pg, ws_bytes=need - 1)[0] == -6
 
 
@@ -216,7 +216,7 @@ def test_decode_rejections():
     ws = torch.zeros((1 << 21) + 512, dtype=torch.uint8)
     base = ws.data_ptr() + (-ws.data_ptr()) % 256
     assert _abi.lib().attn_decode(ctypes.byref(a), None, None, 2, base + 16, 1 << 21, None) == -4
-    need = _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, 2)
+    need = _abi.lib().attn_decode_workspace_size(ctypes.byref(a), None, None, 2)
     assert need > 0
     assert _decode_call(a, ws_bytes=need - 256)[0] == -6
     assert _decode_call(a, S=-1)[0] == -7
@@ -237,11 +237,11 @@ def test_merge_rejections():
     po = torch.zeros(4096, dtype=torch.float32)
     out = torch.zeros(2, 1, 8, 128, dtype=torch.bfloat16)
     s3 = _abi.I64x3(*out.stride()[:3])
-    args = [po.data_ptr(), po.data_ptr(), 2, 2, 1, 8, 128, 1, out.data_ptr(), s3, None, None]
+    args = [po.data_ptr(), po.data_ptr(), None, 2, 2, 1, 8, 128, 1, out.data_ptr(), s3, None, None]
 
     def call(**kw):
         a = list(args)
-        names = ["po", "pl", "S", "B", "Q", "Hq", "Dv", "dt", "out", "stride", "lse", "stream"]
+        names = ["po", "pl", "spb", "S", "B", "Q", "Hq", "Dv", "dt", "out", "stride", "lse", "stream"]
         for k, v in kw.items():
             a[names.index(k)] = v
         return L.attn_decode_merge(*a)
@@ -254,6 +254,7 @@ def test_merge_rejections():
     assert call(Dv=96) == -5
     assert call(Q=0) == -3
     assert call(out=out.data_ptr() + 2) == -4
+    assert call(spb=po.data_ptr() + 2) == -4   # splits_per_batch must be 4-byte aligned
     assert call(B=0) == 0  # nothing to merge: no launch, success
 
 
@@ -356,6 +357,34 @@ def test_fp8_cache_rejections():
     assert call(b) == -4
 
 
+def test_testing_aids_need_the_switch(monkeypatch):
+    """Without AD_TEST_KNOBS=1 the testing aids are ignored: a kernel override changes nothing."""
+    q, k, v, out = _tensors(Hq=2, Hkv=2)   # one query row per KV head: the vector kernel
+    a = _abi.make_args(q, k, v, scale=0.1, out=out)
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
+    assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_MATRIX
+    monkeypatch.setenv("AD_TEST_KNOBS", "0")
+    assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_VECTOR
+    monkeypatch.delenv("AD_TEST_KNOBS")
+    assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_VECTOR
+
+
+def test_workspace_size_takes_the_block_list():
+    """The workspace query plans with the block list the call will carry, and rejects what the
+    calls reject (a block list over a paged cache) with a message."""
+    a, keep = _args()
+    nb = torch.zeros(2, 2, dtype=torch.int32)
+    sp = _abi.make_sparse(nb, torch.zeros(2, 2, 4, dtype=torch.int32), 16)
+    L = _abi.lib()
+    assert L.attn_decode_workspace_size(ctypes.byref(a), None, ctypes.byref(sp), 2) == \
+        L.attn_decode_workspace_size(ctypes.byref(a), None, None, 2)
+    pg = _abi.make_paged(torch.zeros(2, 4, dtype=torch.int32), 16)
+    assert L.attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), ctypes.byref(sp), 2) == 0
+    assert "block list" in ad.attn_decode_last_error()
+    bad = _abi.make_sparse(nb, torch.zeros(2, 2, 4, dtype=torch.int32), 24)
+    assert L.attn_decode_workspace_size(ctypes.byref(a), None, ctypes.byref(bad), 2) == 0
+
+
 def test_kernel_query(monkeypatch):
     """attn_decode_kernel names the partial-pass kernel: vector ALUs for up to 8 rows per KV head
     and for fp32, matrix cores for more bf16 rows and for every fp8 cache, the MLA kernel for the
@@ -440,3 +469,14 @@ def test_int4_cache_rejections(monkeypatch):
     b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
     b.head_dim_qk = b.head_dim_v = 64
     assert kind(b) == -5
+
+
+def test_read_probe_rejections():
+    L = _abi.lib()
+    buf = torch.zeros(1024, dtype=torch.int32)
+    sink = torch.zeros(_abi.AD_PROBE_SINK_WORDS, dtype=torch.int32)
+    assert L.attn_decode_read_probe(None, 64, sink.data_ptr(), None) == -1
+    assert L.attn_decode_read_probe(buf.data_ptr(), 64, None, None) == -1
+    assert L.attn_decode_read_probe(buf.data_ptr() + 4, 64, sink.data_ptr(), None) == -4
+    assert L.attn_decode_read_probe(buf.data_ptr(), 0, sink.data_ptr(), None) == -7
+    assert L.attn_decode_read_probe(buf.data_ptr(), 40, sink.data_ptr(), None) == -7

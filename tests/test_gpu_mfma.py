@@ -10,7 +10,7 @@ import torch
 
 from attention_decode_amd import inputs
 from attention_decode_amd.step import DecodeStep
-from gpu_util import assert_matches, gpu_available, oracle_of, say
+from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -55,7 +55,7 @@ def test_workload4_full(orc):
     out, lse, step = run(w)
     say(f"  splits {step.splits}")
     ref_o, ref_l = oracle_of(orc, w)
-    assert_matches(out, lse, ref_o, ref_l, w.dtype, "workload 4")
+    assert_tight(out, lse, ref_o, ref_l, w.dtype, "workload 4")
 
 
 def test_workload4_poisoned_bit_identical():

@@ -5,9 +5,9 @@ import numpy as np
 import pytest
 import torch
 
-from attention_decode_amd import inputs
+from attention_decode_amd import _abi, inputs
 from attention_decode_amd.step import DecodeStep
-from gpu_util import assert_matches, gpu_available, oracle_of, say
+from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -25,21 +25,64 @@ def flat_rows(w):
     return w.batch * w.q_len * w.num_q_heads
 
 
-def test_workload5_sampled_rows(orc):
-    """Full size (32 sequences x 128 heads x 8192 keys, page 64): every head of sequences 0 and 31
-    plus 256 random rows, compared with the oracle row by row."""
-    say("[gpu] workload 5 (MLA) full size, sampled rows")
+def test_workload5_every_row(orc):
+    """Full size (32 sequences x 128 heads x 8192 keys, page 64): all 4096 rows against the oracle."""
+    say("[gpu] workload 5 (MLA) full size, every row")
     w = inputs.make(5)
     out, lse, step = run(w)
     say(f"  splits {step.splits}")
-    g = torch.Generator().manual_seed(5)
+    ref_o, ref_l = oracle_of(orc, w)
+    assert_tight(out, lse, ref_o, ref_l, w.dtype, f"workload 5, {flat_rows(w)} rows")
+
+
+def chunk_of(w, S):
+    """Keys per split of a forced split count: ceil(kv_len_max / S) rounded up to 16."""
+    return -(-(-(-w.kv_len_max // S)) // 16) * 16
+
+
+def mla_partials(w_cpu, S):
+    wg = w_cpu.to("cuda")
+    step = DecodeStep(wg, num_splits=S)
+    B, Q, H = w_cpu.batch, w_cpu.q_len, w_cpu.num_q_heads
+    po = torch.full((B, Q, H, S, 512), float("nan"), device="cuda")
+    pl = torch.full((B, Q, H, S), float("nan"), device="cuda")
+    _abi.attn_decode_mla_splitkv(step.args, wg.kpe, wg.q_pe, step.paged, S, po, pl)
+    torch.cuda.synchronize()
+    return po.cpu(), pl.cpu()
+
+
+def test_mla_splitkv_partials_small(orc):
+    """attn_decode_mla_splitkv writes every (row, split) slot: each equals the oracle restricted to
+    the split's key range, and splits past a short sequence's end hold (0, -inf)."""
+    lens = [1, 700, 64, 333]
+    S = 3
+    say(f"[gpu] mla split partials, lens {lens}, S={S}")
+    w = inputs.mla(batch=len(lens), num_heads=64, kv_len=max(lens), page_size=16, seq_lens=lens, q_len=2,
+                   causal=True, seed=81)
+    po, pl = mla_partials(w, S)
+    c = chunk_of(w, S)
+    for s in range(S):
+        ref_o, ref_l = oracle_of(orc, w, key_range=(s * c, (s + 1) * c))
+        assert_matches(po[:, :, :, s], pl[:, :, :, s], ref_o, ref_l, w.dtype, f"split {s} of {c} keys")
+
+
+def test_workload5_partials_sampled_rows(orc):
+    """Workload 5's own 8 splits of 1024 keys, written by attn_decode_mla_splitkv: every split of
+    the heads of sequences 0 and 31 and 64 random rows, against the oracle on each key range."""
+    say("[gpu] workload 5 split partials, sampled rows")
+    w = inputs.make(5)
+    S = 8
+    po, pl = mla_partials(w, S)
+    c = chunk_of(w, S)
     H = w.num_q_heads
+    g = torch.Generator().manual_seed(82)
     rows = sorted(set(list(range(H)) + list(range(31 * H, 32 * H)) +
-                      torch.randint(0, flat_rows(w), (256,), generator=g).tolist()))
-    ref_o, ref_l = oracle_of(orc, w, rows=rows)
-    o = out.reshape(-1, w.head_dim_v)[rows]
-    l_ = lse.reshape(-1)[rows]
-    assert_matches(o, l_, ref_o, ref_l, w.dtype, f"workload 5, {len(rows)} rows")
+                      torch.randint(0, flat_rows(w), (64,), generator=g).tolist()))
+    for s in range(S):
+        ref_o, ref_l = oracle_of(orc, w, rows=rows, key_range=(s * c, (s + 1) * c))
+        o = po[:, :, :, s].reshape(-1, 512)[rows]
+        l_ = pl[:, :, :, s].reshape(-1)[rows]
+        assert_matches(o, l_, ref_o, ref_l, w.dtype, f"split {s}")
 
 
 def test_workload5_poisoned_bit_identical():

@@ -8,7 +8,7 @@ import torch
 
 from attention_decode_amd import _abi, inputs
 from attention_decode_amd.step import DecodeStep
-from gpu_util import assert_matches, gpu_available, oracle_of, say
+from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -30,7 +30,7 @@ def test_workload_full(orc, config):
     out, lse, step = run(w)
     say(f"  splits {step.splits}")
     ref_o, ref_l = oracle_of(orc, w)
-    assert_matches(out, lse, ref_o, ref_l, w.dtype, f"workload {config}")
+    assert_tight(out, lse, ref_o, ref_l, w.dtype, f"workload {config}")
 
 
 def test_workload1_partials(orc):
