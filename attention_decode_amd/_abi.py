@@ -20,6 +20,7 @@ AD_KV_SAME, AD_KV_FP8_E4M3, AD_KV_INT4 = 0, 1, 2
 AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA = 0, 1, 2
 AD_MAX_SPLITS = 256
 AD_PROBE_SINK_WORDS = 4096
+AD_NOALLOC_SCRATCH_BYTES = 32 << 20
 STATUS = {0: "AD_OK", -1: "AD_E_NULL", -2: "AD_E_DTYPE", -3: "AD_E_SHAPE", -4: "AD_E_ALIGN",
           -5: "AD_E_UNSUPPORTED", -6: "AD_E_WORKSPACE", -7: "AD_E_RANGE"}
 _DTYPE = {torch.float32: AD_F32, torch.bfloat16: AD_BF16}
@@ -87,6 +88,8 @@ def lib():
                                         ctypes.c_void_p]
         L.attn_decode.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]
+        L.attn_decode_noalloc.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, ctypes.c_void_p]
+        L.attn_decode_noalloc.restype = ctypes.c_int
         L.attn_decode_launches.argtypes = [P(DecodeArgs), P(Paged), P(Sparse), ctypes.c_int32, P(ctypes.c_int32)]
         L.attn_decode_kernel.argtypes = [P(DecodeArgs), P(ctypes.c_int32)]
         L.attn_decode_paged.argtypes = [P(DecodeArgs), P(Paged), ctypes.c_int32, ctypes.c_void_p,
@@ -242,6 +245,14 @@ def attn_decode(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, nu
            lib().attn_decode(ctypes.byref(args), ctypes.byref(paged) if paged else None,
                              ctypes.byref(sparse) if sparse else None, num_splits, _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def attn_decode_noalloc(args: DecodeArgs, paged: Paged | None, sparse: Sparse | None, num_splits: int,
+                        stream=None):
+    """attn_decode in the library's own workspace (no workspace argument, nothing allocated)."""
+    _check("attn_decode_noalloc",
+           lib().attn_decode_noalloc(ctypes.byref(args), ctypes.byref(paged) if paged else None,
+                                     ctypes.byref(sparse) if sparse else None, num_splits, _stream(stream)))
 
 
 def attn_decode_launches(args: DecodeArgs, paged: Paged | None = None, sparse: Sparse | None = None,

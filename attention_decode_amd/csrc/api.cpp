@@ -11,6 +11,7 @@
 #include <string.h>
 
 #include <climits>
+#include <mutex>
 #include <cmath>
 #include <string>
 
@@ -452,6 +453,116 @@ int run_merge(const ad_decode_args *a, const float *po, const float *pl, int S, 
     return AD_OK;
 }
 
+// ------------------------------------------------------------------ library-owned scratch
+// attn_decode_noalloc's workspace: a file-scope device array, one copy per GPU, held until the
+// process ends. Its address on the current device comes from hipGetSymbolAddress, taken once per
+// device at the first call there; host code never passes the array's own name to a kernel (in
+// host code that name is a stand-in, not a device address). The first call on a device also
+// clears the arrival counters with a fill kernel on its stream (every call leaves them at zero).
+constexpr size_t kScratchBytes = AD_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterBytes, "room for partials after the counters");
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static __global__ void clear_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];
+
+int scratch_of_device(hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(AD_E_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        constexpr int words = (int)(kCounterBytes / sizeof(uint32_t));
+        hipLaunchKernelGGL(clear_words_kernel, dim3((words + 255) / 256), dim3(256), 0, stream,
+                           static_cast<uint32_t *>(ptr), words);
+        e = hipGetLastError();
+        if (e != hipSuccess) return hip_fail(e, "scratch counter clear");
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return AD_OK;
+}
+
+int decode_step(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
+                void *workspace, size_t workspace_bytes, void *stream, bool library_scratch) {
+    const Path path = paged ? Path::Paged : Path::Contig;
+    int rc = check_args(args, path, true);
+    if (rc != AD_OK) return rc;
+    if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+    if (args->batch == 0) return ok();
+    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
+    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
+    if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
+        return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
+    if (!library_scratch) {
+        if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
+        if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+            return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
+    }
+    Plan pl{};
+    if ((rc = plan_splits(args, paged, sparse, path, num_splits, &pl)) != AD_OK) return rc;
+    if ((int64_t)args->batch * args->q_len * args->num_q_heads > INT_MAX)
+        return fail(AD_E_UNSUPPORTED, "batch x q_len x num_q_heads must stay below 2^31");
+    if (work_units(args, path) > kMaxUnits)
+        return fail(AD_E_UNSUPPORTED, "%lld work units (batch x KV heads x query-row blocks) exceed %lld",
+                    (long long)work_units(args, path), (long long)kMaxUnits);
+    size_t lse_off = 0;
+    const size_t need = step_bytes(args, pl.splits, &lse_off);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (library_scratch) {
+        if (need > kScratchBytes)
+            return fail(AD_E_RANGE, "this step needs %zu bytes of workspace (%d splits); the library's own "
+                        "scratch holds %zu: use attn_decode with a workspace",
+                        need, pl.splits, kScratchBytes);
+        if ((rc = scratch_of_device(s, &workspace)) != AD_OK) return rc;
+    } else if (workspace_bytes < need) {
+        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed for %d splits",
+                    workspace_bytes, need, pl.splits);
+    }
+    char *ws = static_cast<char *>(workspace);
+    ad::PartialParams p = base_params(args, pl);
+    const int mode = kv_mode(p, paged, sparse);
+    p.part_o = reinterpret_cast<float *>(ws + kCounterBytes);
+    p.part_lse = reinterpret_cast<float *>(ws + lse_off);
+    bool fused = false;
+    if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
+    if (fused) {
+        p.write_empty = 0;
+        p.counters = reinterpret_cast<uint32_t *>(ws);
+        p.out = args->out;
+        for (int i = 0; i < 3; ++i) p.out_s[i] = args->out_stride[i];
+        p.out_dtype = args->dtype == AD_BF16 ? ad::DT_BF16 : ad::DT_F32;
+        p.lse = args->lse;
+        hipError_t e = launch_partial(args, p, mode, s);
+        if (e != hipSuccess) return hip_fail(e, "decode launch");
+        return ok();
+    }
+    // Two launches. A block list's length varies per (b, KV head), so every split slot is written
+    // and merged; otherwise splits past a sequence's end write nothing and row b merges only
+    // ceil(L_b / chunk) of them.
+    p.write_empty = sparse ? 1 : 0;
+    hipError_t e = launch_partial(args, p, mode, s);
+    if (e != hipSuccess) return hip_fail(e, "split-KV launch");
+    rc = run_merge(args, p.part_o, p.part_lse, pl.splits, !sparse, pl.chunk, s);
+    return rc == AD_OK ? ok() : rc;
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -544,56 +655,12 @@ int attn_decode_merge(const float *part_o, const float *part_lse, const int32_t 
 
 int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
                 void *workspace, size_t workspace_bytes, void *stream) {
-    const Path path = paged ? Path::Paged : Path::Contig;
-    int rc = check_args(args, path, true);
-    if (rc != AD_OK) return rc;
-    if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
-    if (args->batch == 0) return ok();
-    if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
-    if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
-    if (num_splits < 0 || num_splits > AD_MAX_SPLITS)
-        return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", num_splits, AD_MAX_SPLITS);
-    if (!workspace) return fail(AD_E_WORKSPACE, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(AD_E_ALIGN, "workspace must be 256-byte aligned");
-    Plan pl{};
-    if ((rc = plan_splits(args, paged, sparse, path, num_splits, &pl)) != AD_OK) return rc;
-    if ((int64_t)args->batch * args->q_len * args->num_q_heads > INT_MAX)
-        return fail(AD_E_UNSUPPORTED, "batch x q_len x num_q_heads must stay below 2^31");
-    if (work_units(args, path) > kMaxUnits)
-        return fail(AD_E_UNSUPPORTED, "%lld work units (batch x KV heads x query-row blocks) exceed %lld",
-                    (long long)work_units(args, path), (long long)kMaxUnits);
-    size_t lse_off = 0;
-    const size_t need = step_bytes(args, pl.splits, &lse_off);
-    if (workspace_bytes < need)
-        return fail(AD_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed for %d splits",
-                    workspace_bytes, need, pl.splits);
-    char *ws = static_cast<char *>(workspace);
-    ad::PartialParams p = base_params(args, pl);
-    const int mode = kv_mode(p, paged, sparse);
-    p.part_o = reinterpret_cast<float *>(ws + kCounterBytes);
-    p.part_lse = reinterpret_cast<float *>(ws + lse_off);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    bool fused = false;
-    if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
-    if (fused) {
-        p.write_empty = 0;
-        p.counters = reinterpret_cast<uint32_t *>(ws);
-        p.out = args->out;
-        for (int i = 0; i < 3; ++i) p.out_s[i] = args->out_stride[i];
-        p.out_dtype = args->dtype == AD_BF16 ? ad::DT_BF16 : ad::DT_F32;
-        p.lse = args->lse;
-        hipError_t e = launch_partial(args, p, mode, s);
-        if (e != hipSuccess) return hip_fail(e, "decode launch");
-        return ok();
-    }
-    // Two launches. A block list's length varies per (b, KV head), so every split slot is written
-    // and merged; otherwise splits past a sequence's end write nothing and row b merges only
-    // ceil(L_b / chunk) of them.
-    p.write_empty = sparse ? 1 : 0;
-    hipError_t e = launch_partial(args, p, mode, s);
-    if (e != hipSuccess) return hip_fail(e, "split-KV launch");
-    rc = run_merge(args, p.part_o, p.part_lse, pl.splits, !sparse, pl.chunk, s);
-    return rc == AD_OK ? ok() : rc;
+    return decode_step(args, paged, sparse, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int attn_decode_noalloc(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                        int32_t num_splits, void *stream) {
+    return decode_step(args, paged, sparse, num_splits, nullptr, 0, stream, true);
 }
 
 int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,

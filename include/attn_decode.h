@@ -266,6 +266,23 @@ int attn_decode_merge(const float *part_o, const float *part_lse, const int32_t 
 int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse, int32_t num_splits,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * attn_decode for callers that cannot allocate or pass device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same step, kernels, plan and
+ * result bit for bit as attn_decode with the same arguments, but the workspace is the library's
+ * own: a static device array of AD_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held
+ * until the process ends. The call allocates nothing (no hipMalloc / hipFree, no allocating
+ * library routine). A step that needs more workspace than that (attn_decode_workspace_size
+ * tells: AD_COUNTER_BYTES plus the partials) is rejected with AD_E_RANGE before anything is
+ * enqueued. The first call on a device looks the array up there and clears its arrival counters
+ * with a small kernel on `stream`; every call leaves them at zero. All calls on one GPU share the
+ * array: calls that overlap on one GPU (other streams, other threads) race and give wrong
+ * results; serialise them.
+ */
+#define AD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int attn_decode_noalloc(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
+                        int32_t num_splits, void *stream);
+
 /* Number of kernel launches attn_decode makes for these arguments and num_splits (0 = the
  * planner's choice): 1 when the merge runs inside the partial pass, 2 when the merge kernel
  * follows, 0 for an empty batch (e.g. to plan graph capture, or to time the partial kernel on

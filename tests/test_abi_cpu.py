@@ -480,3 +480,14 @@ def test_read_probe_rejections():
     assert L.attn_decode_read_probe(buf.data_ptr() + 4, 64, sink.data_ptr(), None) == -4
     assert L.attn_decode_read_probe(buf.data_ptr(), 0, sink.data_ptr(), None) == -7
     assert L.attn_decode_read_probe(buf.data_ptr(), 40, sink.data_ptr(), None) == -7
+
+
+def test_noalloc_rejects_a_step_beyond_its_scratch():
+    """A step whose workspace exceeds the library's own array is rejected on the host, before any
+    HIP call: 2048 query rows x 256 splits x 129 words is far beyond 32 MiB."""
+    q, k, v, out = _tensors(B=64, Hq=32, Hkv=8)
+    a = _abi.make_args(q, k, v, scale=0.1, out=out)
+    rc = _abi.lib().attn_decode_noalloc(ctypes.byref(a), None, None, 256, None)
+    assert rc == -7
+    assert "scratch" in ad.attn_decode_last_error()
+    assert _abi.lib().attn_decode_noalloc(None, None, None, 2, None) == -1
