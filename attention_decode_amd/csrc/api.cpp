@@ -17,6 +17,7 @@
 
 #include "ad_internal.h"
 #include "attn_decode.h"
+#include "mla_layout.h"
 
 namespace {
 
@@ -243,6 +244,8 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
                 Plan *out) {
     const int64_t span = key_span(a, sp);
     const int grain = pg ? pg->page_size : (sp ? sp->block_size : 16);
+    // page / block ids one split can stage (the MLA kernel keeps a smaller map: its LDS holds the ring)
+    const int map_capacity = path == Path::Mla ? ad::mla::kMapCapacity : ad::kMapCapacity;
     int S = requested > 0 ? requested : knob_int("AD_NUM_SPLITS");
     if (S < 0 || S > AD_MAX_SPLITS) return fail(AD_E_RANGE, "num_splits %d outside [0, %d]", S, AD_MAX_SPLITS);
     if (S == 0) {
@@ -272,15 +275,15 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         // A split over a paged cache or a block list stages its page / block ids in LDS: never
         // more of them than the map holds, whatever the bounds above chose (a multiple of 16).
         if (pg || sp)
-            S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, (int64_t)(ad::kMapCapacity - 2) * grain)),
+            S = (int)std::min<int64_t>(std::max<int64_t>(S, cdiv(span, (int64_t)(map_capacity - 2) * grain)),
                                        AD_MAX_SPLITS);
     }
     int64_t chunk = cdiv(std::max<int64_t>(span, 1), S);
     chunk = std::max<int64_t>(cdiv(chunk, 16) * 16, 16);
     if (pg || sp) {
-        if (cdiv(chunk, grain) + 2 > ad::kMapCapacity)
+        if (cdiv(chunk, grain) + 2 > map_capacity)
             return fail(AD_E_RANGE, "%d splits leave %lld keys per split; at most %d pages/blocks per split", S,
-                        (long long)chunk, ad::kMapCapacity - 2);
+                        (long long)chunk, map_capacity - 2);
     }
     if (chunk > (1 << 30)) return fail(AD_E_RANGE, "key range too long");
     out->splits = S;

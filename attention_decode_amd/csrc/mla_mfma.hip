@@ -8,26 +8,32 @@
 // partial o_s = acc / l (512 values) and a natural-log LSE, like the other split-KV passes
 // (mslk splitk_kernels.py, _fwd_kernel_splitK epilogue). Rows are r = t * H + h.
 //
-// Design for CDNA4:
+// Design for CDNA4 (LDS layout and copy addressing: mla_layout.h):
 //
-//   * 128 query heads per work group, 32 per wave: every wave keeps its Q (576 bf16 per head) in
-//     registers as the B operand of S^T = K Q^T and its 32 x 512 fp32 output in the accumulation
-//     registers. The KV tile (32 keys x 1152 B) is shared by the 4 waves through LDS, so HBM
-//     delivers each key once per unit and LDS feeds the matrix cores.
-//   * Tiles are copied HBM -> LDS with buffer_load ... lds (no register staging) into a 4-slot
-//     ring: while tile i is computed, tiles i+1 .. i+3 are in flight. Each slot is its own LDS
-//     object and the loop is unrolled by 4, so the compiler knows which copies a read depends
-//     on; a wave waits for its own copies of tile i (vmcnt) and a barrier publishes everybody's.
-//   * A key row in LDS is 72 chunks of 16 B (64 latent + 8 rotary); chunk c of key k sits at
-//     position c ^ f(k). With f(k) = 4*bit1(k) + bits2..3(k), the score operand reads
-//     (ds_read_b128: 16 keys, one chunk) and the transposing value reads (ds_read_b64_tr_b16:
-//     4 keys x 4 chunks per 32 lanes) are both free of bank conflicts.
-//   * Scores, online softmax (base 2, lazy rescale), P rounding and the P.V product follow the
-//     generic matrix-core pass: lane l ends with 16 keys of query row l%32, P in bf16 is the A
-//     operand of P.V with the matching key order, V comes from the transposing LDS reads.
+//   * Scores by rows, values by columns. Wave w computes the scores of rows 32w .. 32w + 31: it
+//     keeps their Q (576 bf16 per row) in registers as the B operand of S^T = K Q^T and reads K
+//     from LDS. The value product is split the other way: wave w accumulates output columns
+//     128w .. 128w + 127 of ALL 128 rows, reading only its quarter of each V row from LDS. The
+//     probabilities cross between the waves through LDS once per tile (8 KB of bf16 A operands),
+//     the sharding of mla.cuh's compute_mla_pv (QK_SHARD), where each warpgroup multiplies its
+//     own slice of the 512 latent columns with the gathered P. Every V element read from LDS then
+//     feeds 4 row blocks instead of 1: per 32-key tile and compute unit the transposing V reads
+//     drop from 128 KB to 32 KB, the reads the LDS serves slowest.
+//   * Each row's reference max is fixed at its first tile with a visible key and never moves, so
+//     the value accumulators are never rescaled, and a wave can accumulate rows whose scores
+//     another wave computed without any per-tile exchange of maxima. Later scores may exceed the
+//     reference by up to 2^64 (probabilities up to 2^64 stay finite in bf16 and fp32); a row that
+//     goes further makes the work group recompute its unit exactly: one pass for every row's true
+//     max, then the main pass with that max.
+//   * Tiles (32 keys: 32 KB latent + 4 KB rotary) are copied HBM -> LDS with buffer_load ... lds
+//     (no register staging) into a 4-slot ring: while tile i is computed, tiles i+1 .. i+3 are in
+//     flight. Each slot is its own LDS object and the loop is unrolled by 4, so the compiler knows
+//     which copies a read depends on; a wave waits for its own copies of tile i (vmcnt) and a
+//     barrier publishes everybody's. A second barrier per tile publishes the probabilities.
 //   * Keys past the split or the sequence are never read from the cache (their copies read the
 //     unit's own query row) and get probability 0.
 #include "ad_internal.h"
+#include "mla_layout.h"
 
 #include <limits.h>
 #include <math.h>
@@ -35,43 +41,33 @@
 namespace ad {
 namespace {
 
+using namespace mla;
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 32;
-constexpr int kRows = kWaves * kRowsPerWave;      // query rows per work unit
-constexpr int kTile = 32;                         // keys per tile
-constexpr int kLatent = 512, kRope = 64;
-constexpr int kLatBytes = kTile * kLatent * 2;    // latent part of a ring slot: 32 rows x 1 KB
-constexpr int kRopeBytes = kTile * kRope * 2;     // rotary part: 32 rows x 128 B
-constexpr int kCopiesPerWave = kTile / kWaves + 1;  // latent row copies + one rotary copy, per tile and wave
-constexpr int kKs = (kLatent + kRope) / 16;       // k-steps (16 values) of the score product
+constexpr int kKs = (kLatent + kRope) / 16;  // k-steps (16 values) of the score product
 constexpr int kLatKs = kLatent / 16;
-constexpr int kSlabs = kLatent / 32;              // 32-column slabs of the output
-constexpr int kStoreSlabs = 4;                     // slabs per transposed store group
-constexpr int kStageStride = 32 * kStoreSlabs + 4; // floats per staged row (the pad spreads banks)
-// All matrix-core accumulators of a kernel live in one register file (the accumulation registers
-// here), which holds 256 per lane: 15 output slabs plus the score accumulator fill it exactly. The
-// last output slab is therefore summed in ordinary registers: each tile's product for it goes
-// into a fresh accumulator (the score accumulator's registers, free by then) and is added.
-constexpr int kAccSlabs = kSlabs - 1;
-// A row's reference max is fixed at its first tile with a visible key; later scores may exceed it
-// by up to 2^64 (probabilities up to 2^64 stay finite in bf16 and in the fp32 sums). A row that
-// goes further makes the work group recompute its unit exactly: one pass for every row's true
-// max, then the main pass with that max as the reference. The accumulators are never rescaled.
+constexpr int kBlocks = kWaves;              // row blocks of 32 rows
+// Value accumulators: 4 row blocks x 4 slabs of 32 columns. All matrix-core accumulators of a
+// kernel live in one register file (the accumulation registers here), which holds 256 per lane:
+// 15 of the 16 blocks plus the score accumulator fill it exactly. The last block (row block 3,
+// slab 3) is summed in ordinary registers: each tile's products for it go into a fresh
+// accumulator (the score accumulator's registers, free by then) and are added.
+constexpr int kAcc = kBlocks * kSlabsPerWave;
+constexpr int kVgprAcc = kAcc - 1;
 constexpr float kHeadroom = 64.f;
-constexpr int kPipe = 4;  // LDS operand reads in flight ahead of the matrix products
+constexpr int kPipe = 4;  // score-operand reads in flight ahead of the matrix products
 
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+// s_waitcnt lgkmcnt(0) with no wait on the other counters.
+constexpr int kLgkmZero = 15 | (3 << 14) | (7 << 4);
 // Buffer descriptor word 3 for raw (untyped, unswizzled) buffer accesses on the gfx9 family.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -96,20 +92,14 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
 }
+__device__ __forceinline__ u32x4 lds16(const lds_u8 *p) { return *(const __attribute__((address_space(3))) u32x4 *)p; }
 
-// LDS layout of a ring slot. Latent chunk c (16 B) of key k sits at k*1024 + 16*(c ^ F(k)) of the
-// slot's latent object; rotary chunk c of key k at k*128 + 16*(c ^ Hr(k)) of its rotary object. With these permutations the score
-// operand reads (ds_read_b128: 16 keys, one chunk) and the transposing value reads
-// (ds_read_b64_tr_b16: 4 keys x 4 chunks per 32 lanes) hit distinct banks.
 // The 64-bit value held as (hi, lo) words in lane `l`. The lane read returns a signed int: each
 // word is widened as unsigned, or a low word with bit 31 set would fill the high word with ones.
 __device__ __forceinline__ uint64_t lane_u64(uint32_t hi, uint32_t lo, int l) {
     return ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, l) << 32) |
            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)lo, l);
 }
-
-__device__ __forceinline__ int swz_lat(int k) { return ((k & 3) << 2) | ((k >> 2) & 3); }
-__device__ __forceinline__ int swz_rope(int k) { return (k >> 1) & 7; }
 
 // Work-group placement. The dispatcher deals work groups to the 8 XCDs round robin (group L to
 // XCD L % 8), and each XCD has its own L2. Unit u = (b * row_blocks + rb) * splits + split is
@@ -130,31 +120,31 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, half = lane >> 5;
     const int H = p.group, Q = p.q_len, R = H * Q, S = p.num_splits;
-    const int r0 = rb * kRows + wave * kRowsPerWave;   // this wave's first row
-    const int nr = max(0, min(kRowsPerWave, R - r0));  // its valid rows
     const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
     const int t0 = split * p.chunk;
     const int t1 = min(t0 + p.chunk, L);
-
-    auto out_row = [&](int r) -> int64_t {  // r: row of this wave
-        const int ra = r0 + r, t = ra / H, g = ra - t * H;
+    // valid rows of row block hb (32 rows each) of this unit
+    auto rows_of = [&](int hb) { return max(0, min(kRowsPerWave, R - (rb * kRows + hb * kRowsPerWave))); };
+    auto out_row = [&](int hb, int r) -> int64_t {  // r: row inside row block hb
+        const int ra = rb * kRows + hb * kRowsPerWave + r, t = ra / H, g = ra - t * H;
         return (int64_t)(b * Q + t) * p.num_q_heads + g;
     };
+    const int nr = rows_of(wave);  // rows whose scores this wave computes
 
     if (t0 >= t1) {  // uniform over the work group
         if (p.write_empty) {
             for (int i = lane; i < nr * kLatent; i += 64) {
                 const int r = i / kLatent, d = i - r * kLatent;
-                p.part_o[(out_row(r) * S + split) * kLatent + d] = 0.f;
+                p.part_o[(out_row(wave, r) * S + split) * kLatent + d] = 0.f;
             }
-            for (int r = lane; r < nr; r += 64) p.part_lse[out_row(r) * S + split] = -INFINITY;
+            for (int r = lane; r < nr; r += 64) p.part_lse[out_row(wave, r) * S + split] = -INFINITY;
         }
         return;
     }
 
-    __shared__ int s_map[kMapCapacity];
+    __shared__ int s_map[mla::kMapCapacity];
     // Ring slots: separate LDS objects, so that the compiler can tell which copies a read or a
-    // store depends on (the rotary parts are written by ordinary stores, never by copies).
+    // store depends on.
     __shared__ __attribute__((aligned(16))) unsigned char s_lat0[kLatBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_lat1[kLatBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_lat2[kLatBytes];
@@ -163,27 +153,28 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     __shared__ __attribute__((aligned(16))) unsigned char s_rope1[kRopeBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_rope2[kRopeBytes];
     __shared__ __attribute__((aligned(16))) unsigned char s_rope3[kRopeBytes];
-    __shared__ float s_x[kWaves][kRowsPerWave];  // per-row exchange inside a wave
+    __shared__ __attribute__((aligned(16))) unsigned char s_p[kPBytes];  // probabilities, all rows
+    __shared__ float s_l[kRows];                                          // row sums, all rows
     __shared__ int s_flag[kWaves];
 
     const int map_shift = p.page_shift, map_mask = (1 << map_shift) - 1;
     const int map_first = t0 >> map_shift;
     {
-        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;  // <= kMapCapacity (host plan)
         const int32_t *bt = p.block_table + b * p.bt_stride + map_first;
         for (int i = tid; i < n; i += kThreads) s_map[i] = bt[i];
     }
     __syncthreads();
 
-    // ---- this lane's query row (row col of the wave): B operand, 32 latent + 4 rotary k-steps
+    // ---- this lane's query row (row col of this wave's block): B operand, 32 latent + 4 rotary k-steps
     const uint16_t *q_nope = static_cast<const uint16_t *>(p.q);
     const uint16_t *q_pe = static_cast<const uint16_t *>(p.q2);
-    const uint16_t *safe_n = q_nope + b * p.q_s[0];  // row (b, 0, 0): finite, always readable
+    const uint16_t *safe_n = q_nope + b * p.q_s[0];  // row (b, 0, 0): finite, always readable, 1 KB
     const uint16_t *safe_p = q_pe + b * p.q2_s[0];
     u32x4 qb[kKs];
     int lo_r = INT_MIN, hi_r = INT_MAX;
     if (col < nr) {
-        const int ra = r0 + col, t = ra / H, g = ra - t * H;
+        const int ra = rb * kRows + wave * kRowsPerWave + col, t = ra / H, g = ra - t * H;
         const uint16_t *qn = q_nope + b * p.q_s[0] + t * p.q_s[1] + g * p.q_s[2];
         const uint16_t *qp = q_pe + b * p.q2_s[0] + t * p.q2_s[1] + g * p.q2_s[2];
 #pragma unroll
@@ -197,32 +188,26 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         for (int ks = 0; ks < kKs; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
     }
     // keys [lo_max, hi_min) are visible to every row of the unit
-    const int t_first = __builtin_amdgcn_readfirstlane((rb * kRows) / H);
-    const int t_last = __builtin_amdgcn_readfirstlane((min(R, (rb + 1) * kRows) - 1) / H);
-    const int hi_min = p.causal ? L - Q + t_first + 1 : INT_MAX;
-    const int lo_max = p.window ? L - Q + t_last - p.window + 1 : INT_MIN;
+    const int r_first = rb * kRows, r_last = min(R, (rb + 1) * kRows) - 1;
+    const int hi_min = p.causal ? L - Q + r_first / H + 1 : INT_MAX;
+    const int lo_max = p.window ? L - Q + r_last / H - p.window + 1 : INT_MIN;
 
     const uint16_t *ckv = static_cast<const uint16_t *>(p.k);
     const uint16_t *kpe = static_cast<const uint16_t *>(p.k2);
 
     // ---- copy tile [base, base + 32) of the split into a ring slot, HBM -> LDS with
-    // buffer_load ... lds (no register staging). Wave w copies the latent rows of keys w, w+4, ..,
-    // w+28 (one 1-KB copy per row, lane i bringing chunk i ^ F(key)) and the rotary rows of keys
-    // 8w .. 8w+7 (lane i: key 8w + i/8, chunk (i%8) ^ Hr(key)). Those 8 keys lie in one page:
-    // tiles start at multiples of 16 and pages hold 16, 32 or 64 keys. Every descriptor covers
-    // only rows the copy may read, so the hardware range check confines it: a latent row is
-    // 1 KB, a rotary group ends after its last key inside the split; lanes beyond read zeros
-    // (the scores of those keys are masked). Latent rows past the split read the unit's query
-    // row instead. The buffer form of the LDS copy matters: the compiler treats the global form
-    // as a possible LDS access of unknown order and would make every LDS read wait for all.
-    // The copies are nontemporal (cache-policy bit 1 of the buffer instruction): each reads whole
-    // lines once: 128 -> 113 us for 32 sequences of 8192 keys under 128 heads.
+    // buffer_load ... lds (mla_layout.h: lat_copy_*, rope_copy_*). Every descriptor covers only the
+    // rows the copy may read, so the hardware range check confines it. Latent rows past the split
+    // read the unit's query row instead. The buffer form of the LDS copy matters: the compiler
+    // treats the global form as a possible LDS access of unknown order and would make every LDS
+    // read wait for all. The copies are nontemporal (cache-policy bit 1): each reads whole lines
+    // once.
     constexpr int kStreamPolicy = 2;
     const int64_t rope_stride = p.k2_s[1] * 2;  // bytes between the rotary rows of two slots of a page
     auto issue = [&](lds_u8 *lat_slot, lds_u8 *rope_slot, int base) {
         // Row addresses of key base + i in lane i (i < 32), computed once per tile on the vector
         // unit; each copy takes its row with a lane read. Keys past the split get the query row.
-        const int vl = base + (lane & 31);
+        const int vl = base + col;
         const int vlc = min(vl, t1 - 1);
         const int64_t pg = s_map[(vlc >> map_shift) - map_first];
         const int sl = vlc & map_mask;
@@ -231,70 +216,63 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         const uint32_t lat_lo = (uint32_t)lat_row, lat_hi = (uint32_t)(lat_row >> 32);
         const uint32_t rope_lo = (uint32_t)rope_row, rope_hi = (uint32_t)(rope_row >> 32);
 #pragma unroll
-        for (int j = 0; j < kTile / kWaves; ++j) {
-            const int kk = wave + kWaves * j;  // uniform
+        for (int j = 0; j < kLatCopiesPerWave; ++j) {
+            const int kk = lat_copy_key(wave, j);  // uniform
             const uint64_t row = lane_u64(lat_hi, lat_lo, kk);
             const __amdgpu_buffer_rsrc_t rsrc =
-                __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, kLatent * 2, kBufferFlags);
+                __builtin_amdgcn_make_buffer_rsrc((void *)row, (short)0, kLatRowBytes, kBufferFlags);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rsrc, (__attribute__((address_space(3))) void *)(lat_slot + kk * 1024), 16, (lane ^ swz_lat(kk)) << 4,
-                0, 0, kStreamPolicy);
+                rsrc, (__attribute__((address_space(3))) void *)(lat_slot + lat_copy_lds(kk)), 16,
+                lat_copy_src(kk, lane), 0, 0, kStreamPolicy);
         }
-        const int v0 = base + 8 * wave;  // uniform: first key of this wave's rotary group
+        const int v0 = base + rope_copy_key(wave, 0);  // uniform: first key of this wave's rotary group
         const int nv = min(max(t1 - v0, 0), 8);
-        const uint64_t row = lane_u64(rope_hi, rope_lo, 8 * wave);
-        const int k = 8 * wave + (lane >> 3);
+        const uint64_t row = lane_u64(rope_hi, rope_lo, rope_copy_key(wave, 0));
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)row, (short)0, nv > 0 ? (int)((nv - 1) * rope_stride) + kRope * 2 : 0, kBufferFlags);
+            (void *)row, (short)0, (int)rope_copy_records(nv, rope_stride), kBufferFlags);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (__attribute__((address_space(3))) void *)(rope_slot + wave * 1024), 16,
-            (int)((lane >> 3) * rope_stride) + (((lane & 7) ^ swz_rope(k)) << 4), 0, 0, kStreamPolicy);
+            rsrc, (__attribute__((address_space(3))) void *)(rope_slot + rope_copy_lds(wave)), 16,
+            (int)rope_copy_src(wave, lane, rope_stride), 0, 0, kStreamPolicy);
     };
 
-    // Per-lane LDS offsets inside a slot; every read adds a compile-time offset that fits the DS
+    // Per-lane LDS offsets inside a slot (mla_layout.h, the split forms): a base and a rotation per
+    // lane, one XOR and one shifted add per read, and a compile-time offset that fits the DS
     // instruction's immediate field.
-    //   score operand, k-step ks < 32: key col, latent chunk 2ks + half = k_off[ks % 8] + 256 (ks / 8)
-    //   score operand, k-step 32 + i:  key col, rotary chunk 2i + half  = r_off[i]
-    //   value read (k-step t, read rd, slab s): key 16t + 8rd + tr_row, chunk 4s + tr_chunk
-    //                                          = v_off[4rd + s % 4] + (16t + 8rd) * 1024 + 256 (s / 4)
-    int k_off[8], r_off[4], v_off[8];
-    {
-        const int tr_row = 4 * half + ((lane & 15) >> 2);
-        const int tr_chunk = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) k_off[i] = col * 1024 + (((2 * i + half) ^ swz_lat(col)) << 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r_off[i] = col * 128 + (((2 * i + half) ^ swz_rope(col)) << 4);
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                v_off[4 * rd + i] = tr_row * 1024 + (((4 * i + tr_chunk) ^ swz_lat(8 * rd + tr_row)) << 4) + ((lane & 1) << 3);
-    }
+    // The values pass through an empty asm statement at every tile (opaque()), so that the
+    // compiler computes each read's offset at the read instead of hoisting all of them out of the
+    // loop into registers it does not have.
+    int klb = k_lat_base(lane), klr = k_lat_rot(lane);
+    int krb = k_rope_base(lane), krr = k_rope_rot(lane);
+    int vb_0 = v_base(lane, 0) + 256 * wave, vb_1 = v_base(lane, 1) + 256 * wave, vr = v_rot(lane);
+    auto opaque = [&]() {
+        asm volatile("" : "+v"(klb), "+v"(klr), "+v"(krb), "+v"(krr), "+v"(vb_0), "+v"(vb_1), "+v"(vr));
+    };
 
     float m = -INFINITY, l = 0.f, lf = 0.f;  // row col's reference max and sums (this lane's keys)
     bool overflow = false;
-    f32x16 o[kSlabs];  // o[0 .. kAccSlabs-1]: matrix-core accumulators; o[kAccSlabs]: summed by the VALU
+    // o[hb * 4 + s]: row block hb, slab s (columns 128 wave + 32 s ..); o[0 .. kVgprAcc-1] are
+    // matrix-core accumulators, o[kVgprAcc] is summed by the VALU.
+    f32x16 o[kAcc];
     // Zeros are produced as a product with zero operands: every value that reaches the loop-carried
     // accumulators then comes out of the matrix core, and the compiler keeps them in the
-    // accumulation registers for the whole loop (a plain 0.f start made it carry all 240 in
-    // ordinary registers and copy them over at every iteration, spilling the queries).
+    // accumulation registers for the whole loop (a plain 0.f start made it carry them in ordinary
+    // registers and copy them over at every iteration).
     auto clear = [&]() {
 #pragma unroll
-        for (int s = 0; s < kAccSlabs; ++s) o[s] = mfma(u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, f32x16{});
+        for (int a = 0; a < kVgprAcc; ++a) o[a] = mfma(u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0}, f32x16{});
 #pragma unroll
-        for (int j = 0; j < 16; ++j) o[kAccSlabs][j] = 0.f;
+        for (int j = 0; j < 16; ++j) o[kVgprAcc][j] = 0.f;
     };
     clear();
 
-    // Scores of tile `base` (base-2 units, masked) for row col, 16 keys of this lane.
-    // LDS operand reads run kPipe matrix products ahead of their use: a read issued right before
-    // the product that needs it would stall every product for the full LDS latency.
+    // Scores of tile `base` (base-2 units, masked) for row col of this wave's block, 16 keys of
+    // this lane. LDS operand reads run kPipe matrix products ahead of their use.
     auto k_operand = [&](const lds_u8 *cur, const lds_u8 *rcur, int ks) -> u32x4 {
-        const lds_u8 *at = ks < kLatKs ? cur + k_off[ks & 7] + 256 * (ks >> 3) : rcur + r_off[ks - kLatKs];
-        return *(const __attribute__((address_space(3))) u32x4 *)at;
+        return lds16(ks < kLatKs ? cur + (klb + 32 * ((ks & 7) ^ klr)) + 256 * (ks >> 3)
+                                 : rcur + (krb + 32 * ((ks - kLatKs) ^ krr)));
     };
     auto scores = [&](const lds_u8 *cur, const lds_u8 *rcur, int base, float (&sv)[16]) {
+        opaque();
         f32x16 sc;
 #pragma unroll
         for (int j = 0; j < 16; ++j) sc[j] = 0.f;
@@ -311,30 +289,34 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         for (int j = 0; j < 16; ++j) sv[j] = sc[j] * p.scale_log2;
         const bool full = base + kTile <= t1 && base >= lo_max && base + kTile <= hi_min;  // uniform
         if (!full) {
+            // key of element j: base + acc_row(lane, j) = (base + 4 half) + 8 (j / 4) + j % 4
+            const int pos0 = base + 4 * half;
+            const int lim = min(t1, hi_r);
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const int pos = base + 8 * (j / 4) + 4 * half + (j % 4);
-                const bool vis = pos < t1 && pos >= lo_r && pos < hi_r;
-                sv[j] = vis ? sv[j] : -INFINITY;
+                const int pos = pos0 + 8 * (j >> 2) + (j & 3);
+                sv[j] = (pos < lim && pos >= lo_r) ? sv[j] : -INFINITY;
             }
         }
     };
 
+    // value operand of key step t, slab s of this wave's columns (global slab 4 wave + s)
     auto v_operand = [&](const lds_u8 *cur, int t, int s) -> u32x4 {
+        const int rot = 64 * (s ^ vr);
         s16x4 part[2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd)
             part[rd] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4 *)(cur + v_off[4 * rd + (s & 3)] + (16 * t + 8 * rd) * 1024 +
-                                                            256 * (s >> 2)));
+                (__attribute__((address_space(3))) s16x4 *)(cur + ((rd ? vb_1 : vb_0) + rot) + 16384 * t));
         return __builtin_bit_cast(u32x4, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    lds_u8 *const pbuf = (lds_u8 *)s_p;
+
     auto compute = [&](const lds_u8 *cur, const lds_u8 *rcur, int base) {
         float sv[16];
         scores(cur, rcur, base, sv);
-        u32x4 vb_pipe[kPipe];  // first value operands, loading while the softmax runs
-#pragma unroll
-        for (int i = 0; i < kPipe; ++i) vb_pipe[i] = v_operand(cur, i / kAccSlabs, i % kAccSlabs);
+        // the first value operands do not depend on P: they load while the softmax runs
+        u32x4 vb0 = v_operand(cur, 0, 0), vb1 = v_operand(cur, 0, 1);
         float mx = sv[0];
 #pragma unroll
         for (int j = 1; j < 16; ++j) mx = fmaxf(mx, sv[j]);
@@ -351,26 +333,46 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
             l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
             lf += p0 + p1;
         }
-        // products in order: (t, s) for s < kAccSlabs, t = 0 then 1; then the summed slab, t = 0, 1
-        constexpr int kProducts = 2 * kSlabs;
-        auto prod_t = [](int i) { return i < 2 * kAccSlabs ? i / kAccSlabs : i - 2 * kAccSlabs; };
-        auto prod_s = [](int i) { return i < 2 * kAccSlabs ? i % kAccSlabs : kAccSlabs; };
-        u32x4 pa[2];
+        // this wave's rows' P, as the A operands of key steps 0 and 1, to every wave
 #pragma unroll
-        for (int t = 0; t < 2; ++t) pa[t] = u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+        for (int t = 0; t < kKeySteps; ++t)
+            *(__attribute__((address_space(3))) u32x4 *)(pbuf + p_off(wave, t, lane)) =
+                u32x4{pk[4 * t], pk[4 * t + 1], pk[4 * t + 2], pk[4 * t + 3]};
+        __builtin_amdgcn_s_waitcnt(kLgkmZero);
+        asm volatile("s_barrier" ::: "memory");
+        // products in order: key step t, slab s, row block hb (i = 16 t + 4 s + hb); the value
+        // operand (t, s) serves 4 consecutive products, the P operands of step t all 16. Each
+        // value operand is read two slabs ahead; each P operand of step 1 replaces its step-0
+        // operand right after that operand's last product.
+        u32x4 pa[kBlocks];
+#pragma unroll
+        for (int hb = 0; hb < kBlocks; ++hb) pa[hb] = lds16(pbuf + p_off(hb, 0, lane));
         f32x16 part;
 #pragma unroll
-        for (int i = 0; i < kProducts; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            const int t = prod_t(i), s = prod_s(i);
-            const u32x4 vb = vb_pipe[i % kPipe];
-            if (i + kPipe < kProducts) vb_pipe[i % kPipe] = v_operand(cur, prod_t(i + kPipe), prod_s(i + kPipe));
-            if (s < kAccSlabs)
-                o[s] = mfma(pa[t], vb, o[s]);
-            else
-                part = mfma(pa[t], vb, t == 0 ? f32x16{} : part);
+        for (int t = 0; t < kKeySteps; ++t) {
+#pragma unroll
+            for (int s = 0; s < kSlabsPerWave; ++s) {
+                const u32x4 vb = s % 2 ? vb1 : vb0;
+#pragma unroll
+                for (int hb = 0; hb < kBlocks; ++hb) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int a = hb * kSlabsPerWave + s;
+                    if (a < kVgprAcc)
+                        o[a] = mfma(pa[hb], vb, o[a]);
+                    else
+                        part = mfma(pa[hb], vb, t == 0 ? f32x16{} : part);
+                    if (t + 1 < kKeySteps && s == kSlabsPerWave - 1) pa[hb] = lds16(pbuf + p_off(hb, t + 1, lane));
+                }
+                const int nt = t + (s + 2) / kSlabsPerWave, ns = (s + 2) % kSlabsPerWave;
+                if (nt < kKeySteps) {
+                    if (s % 2)
+                        vb1 = v_operand(cur, nt, ns);
+                    else
+                        vb0 = v_operand(cur, nt, ns);
+                }
+            }
         }
-        o[kAccSlabs] += part;
+        o[kVgprAcc] += part;
     };
 
     auto max_only = [&](const lds_u8 *cur, const lds_u8 *rcur, int base) {
@@ -385,9 +387,10 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     // The ring over the split (4 slots, 3 tiles in flight): before tile `base` is used, each wave
     // waits for its own copies of it (vmcnt: the copies of the next two tiles may stay in flight)
     // and a barrier publishes all of them; the barrier also ends every read of the slot the copy
-    // of tile base + 3*32 then overwrites. Copies past the end read nothing or the query row, so
-    // every step issues the same number of copies and the vmcnt count is exact. At the end every
-    // copy has landed and every read is done.
+    // of tile base + 3*32 then overwrites, and every read of the probabilities of the previous
+    // tile. Copies past the end read nothing or the query row, so every step issues the same
+    // number of copies and the vmcnt count is exact. At the end every copy has landed and every
+    // read is done.
     auto run = [&](auto body) {
         lds_u8 *l0 = (lds_u8 *)s_lat0, *l1 = (lds_u8 *)s_lat1, *l2 = (lds_u8 *)s_lat2, *l3 = (lds_u8 *)s_lat3;
         lds_u8 *q0 = (lds_u8 *)s_rope0, *q1 = (lds_u8 *)s_rope1, *q2 = (lds_u8 *)s_rope2, *q3 = (lds_u8 *)s_rope3;
@@ -423,45 +426,46 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         run(compute);  // m is every row's true max: no score exceeds it
     }
 
-    // ---- o_s = acc / l, lse_s = (m + log2 lf) * ln 2 for this wave's rows
+    // ---- row sums of every row, then o_s = acc / l for this wave's columns of all rows and
+    // lse_s = (m + log2 lf) * ln 2 for this wave's score rows
     l = pair_sum(l);
     lf = pair_sum(lf);
-    if (half == 0) s_x[wave][col] = l;
-    float lr[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) lr[j] = s_x[wave][8 * (j / 4) + 4 * half + (j % 4)];
-    float inv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) inv[j] = lr[j] > 0.f ? 1.f / lr[j] : 0.f;
-    // The accumulators hold one column per lane; the partial rows go out as 16-byte stores of
-    // four columns, transposed through this wave's ring slot (free since the loop's last
-    // barrier): kStoreSlabs slabs at a time as 32 rows of kStageStride floats.
+    if (half == 0) s_l[wave * kRowsPerWave + col] = l;
+    if (half == 0 && col < nr) {
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        p.part_lse[out_row(wave, col) * S + split] =
+            l > 0.f ? (ms + __builtin_amdgcn_logf(lf)) * 0.69314718055994531f : -INFINITY;
+    }
+    __syncthreads();
+    // The accumulators hold one column per lane; the partial rows go out as 16-byte stores of four
+    // columns, transposed through this wave's ring slot (free since the loop's last barrier): one
+    // row block (32 rows x 128 columns) at a time.
     lds_u8 *slot = wave == 0 ? (lds_u8 *)s_lat0 : wave == 1 ? (lds_u8 *)s_lat1 : wave == 2 ? (lds_u8 *)s_lat2 : (lds_u8 *)s_lat3;
-    __attribute__((address_space(3))) float *stage = (__attribute__((address_space(3))) float *)slot;
-    static_assert(kRowsPerWave * kStageStride * 4 <= kLatBytes, "a slab group fits a ring slot");
 #pragma unroll
-    for (int g = 0; g < kSlabs / kStoreSlabs; ++g) {
+    for (int hb = 0; hb < kBlocks; ++hb) {
+        const int nb = rows_of(hb);
+        float inv[16];
 #pragma unroll
-        for (int sl = 0; sl < kStoreSlabs; ++sl)
+        for (int j = 0; j < 16; ++j) {
+            const float lr = s_l[hb * kRowsPerWave + acc_row(lane, j)];
+            inv[j] = lr > 0.f ? 1.f / lr : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < kSlabsPerWave; ++s)
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                stage[(8 * (j / 4) + 4 * half + (j % 4)) * kStageStride + 32 * sl + col] =
-                    o[kStoreSlabs * g + sl][j] * inv[j];
+                *(__attribute__((address_space(3))) float *)(slot + stage_write_off(lane, j, s)) =
+                    o[hb * kSlabsPerWave + s][j] * inv[j];
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int i = 0; i < kRowsPerWave / 2; ++i) {
-            const int r = 2 * i + half;  // lanes 0-31 row 2i, lanes 32-63 row 2i + 1: 4 columns each
-            const f32x4 v = *(const __attribute__((address_space(3))) f32x4 *)(stage + r * kStageStride + 4 * col);
-            if (r < nr)
-                *reinterpret_cast<f32x4 *>(p.part_o + (out_row(r) * S + split) * kLatent +
-                                           32 * kStoreSlabs * g + 4 * col) = v;
+            const int r = 2 * i + half;
+            const f32x4 v = *(const __attribute__((address_space(3))) f32x4 *)(slot + stage_read_off(lane, i));
+            if (r < nb)
+                *reinterpret_cast<f32x4 *>(p.part_o + (out_row(hb, r) * S + split) * kLatent + kColsPerWave * wave +
+                                           4 * col) = v;
         }
         __builtin_amdgcn_wave_barrier();
-    }
-    if (half == 0 && col < nr) {
-        const float ms = (m == -INFINITY) ? 0.f : m;
-        p.part_lse[out_row(col) * S + split] =
-            l > 0.f ? (ms + __builtin_amdgcn_logf(lf)) * 0.69314718055994531f : -INFINITY;
     }
 }
 
