@@ -669,10 +669,12 @@ int attn_decode_noalloc(const ad_decode_args *args, const ad_paged *paged, const
 int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                          int32_t num_splits, int32_t *launches) {
     if (!launches) return fail(AD_E_NULL, "launches is NULL");
-    const Path path = paged ? Path::Paged : Path::Contig;
+    const bool mla = args && args->head_dim_qk == 576 && args->head_dim_v == 512;
+    const Path path = mla ? Path::Mla : paged ? Path::Paged : Path::Contig;
     int rc = check_args(args, path, false);
     if (rc != AD_OK) return rc;
     if (paged && sparse) return fail(AD_E_UNSUPPORTED, "a block list over a paged cache is not supported");
+    if (mla && (!paged || sparse)) return fail(AD_E_UNSUPPORTED, "MLA reads a paged cache without a block list");
     if (paged && (rc = check_paged(args, paged)) != AD_OK) return rc;
     if (sparse && (rc = check_sparse(sparse)) != AD_OK) return rc;
     if (args->batch == 0) {
@@ -681,8 +683,8 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
     }
     Plan pl{};
     if ((rc = plan_splits(args, paged, sparse, path, num_splits, &pl)) != AD_OK) return rc;
-    bool fused = false;
-    if ((rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
+    bool fused = false;  // the MLA step is always the partial pass and the merge kernel
+    if (!mla && (rc = fuse_merge(args, path, pl.splits, &fused)) != AD_OK) return rc;
     *launches = fused ? 1 : 2;
     return ok();
 }

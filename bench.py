@@ -43,7 +43,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     2: ("partial_valu_contiguous", "partial_valu_kernel, merge fused in (one launch per step)"),
     3: ("partial_valu_paged", "partial_valu_kernel + merge_kernel (two launches per step)"),
     4: ("partial_mfma_sparse", "partial_mfma_kernel + merge_kernel (two launches per step)"),
-    5: ("mla_partial", "mla_partial_kernel (MLA split-KV partial pass, matrix cores; merge_kernel follows)"),
+    5: ("mla_partial", "mla_partial_kernel + merge_kernel (two launches per step)"),
     6: ("partial_mfma_paged_fp8", "partial_mfma_kernel, fp8 cache + merge_kernel (two launches per step)"),
     7: ("partial_mfma_paged_spec", "partial_mfma_kernel, whole-row loads, draft trees + merge_kernel (two launches per step)"),
     8: ("partial_valu_paged_int4", "partial_valu_kernel_int4 + merge_kernel (two launches per step)"),
@@ -93,51 +93,41 @@ class Step:
         self.splits, self.chunk = _abi.attn_decode_plan(self.sets[0][0], self.paged, self.sparse)
         if w.num_splits:
             self.splits = w.num_splits
-        # GQA caches: one launch per step (attn_decode: the last split of each work unit merges),
-        # in a workspace zero-filled once. MLA: the partial pass, then the merge kernel.
-        self.fused = w.kind != "mla"
-        if self.fused:
-            nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits, self.sparse)
-            self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
-            self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
-            kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
-            if w.kv_format == "int4":  # the vector kernel's int4 form has a symbol of its own
-                kind += "_int4"
-            if self.launches == 1:
-                self.kernel_name = f"{kind} (merge inside; the whole step)"
-            else:  # the partial pass alone, into buffers of its own
-                self.kernel_name = f"{kind} (partial pass alone; the merge kernel follows it in a step)"
-                self.kpart_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
-                self.kpart_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+        # The whole step through its entry point (attn_decode; attn_decode_mla), in a workspace
+        # zero-filled once: one launch where the merge runs inside the partial pass, else the
+        # partial pass and the merge kernel.
+        self.mla = w.kind == "mla"
+        nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits, self.sparse)
+        self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
+        kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
+        if w.kv_format == "int4":  # the vector kernel's int4 form has a symbol of its own
+            kind += "_int4"
+        if self.launches == 1:
+            self.kernel_name = f"{kind} (merge inside; the whole step)"
+        else:  # the partial pass alone, into buffers of its own
+            self.kernel_name = f"{kind} (partial pass alone; the merge kernel follows it in a step)"
+            self.kpart_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
+            self.kpart_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+
+    def step(self, i):
+        """One whole decode step on cache copy i."""
+        a, k, x = self.sets[i % len(self.sets)][:3]
+        if self.mla:
+            self.abi.attn_decode_mla(a, x, self.w.q_pe, self.paged, self.splits, self.workspace)
         else:
-            self.launches = 2
-            self.kernel_name = "mla_partial_kernel (partial pass alone; the merge kernel follows it in a step)"
-            self.part_o = torch.empty(B, Q, Hq, self.splits, Dv, dtype=torch.float32, device=dev)
-            self.part_lse = torch.empty(B, Q, Hq, self.splits, dtype=torch.float32, device=dev)
+            self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
 
     def kernel(self, i):
-        """The step's dominant kernel alone: the partial pass (with the merge inside it where
-        attn_decode makes one launch)."""
+        """The step's dominant kernel alone: the partial pass (the whole step where the merge runs
+        inside it)."""
         a, k, x = self.sets[i % len(self.sets)][:3]
         if self.launches == 1:
-            self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
-        elif self.fused:
+            self.step(i)
+        elif self.mla:
+            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.kpart_o, self.kpart_lse)
+        else:
             self.abi.attn_decode_splitkv(a, self.paged, self.sparse, self.splits, self.kpart_o, self.kpart_lse)
-        else:
-            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
-
-    def partial(self, i):
-        """The step's partial pass (the whole step where the merge is fused into it)."""
-        a, k, x = self.sets[i % len(self.sets)][:3]
-        if self.fused:
-            self.abi.attn_decode(a, self.paged, self.sparse, self.splits, self.workspace)
-        else:
-            self.abi.attn_decode_mla_splitkv(a, x, self.w.q_pe, self.paged, self.splits, self.part_o, self.part_lse)
-
-    def merge(self):
-        """The separate merge launch, where the step has one."""
-        if not self.fused:
-            self.abi.attn_decode_merge(self.part_o, self.part_lse, self.splits, self.out, self.lse)
 
 
 def oracle_kwargs(w):
@@ -343,8 +333,7 @@ def main():
     log("streaming calibration ...")
     peak = stream_peak(stream)
     for i in range(args.warmup):
-        step.partial(i)
-        step.merge()
+        step.step(i)
         step.kernel(i)
     torch.cuda.synchronize()
 
@@ -354,8 +343,7 @@ def main():
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(K):
-        step.partial(i)
-        step.merge()
+        step.step(i)
     end.record(stream)
     torch.cuda.synchronize()
     ms_step = start.elapsed_time(end) / K
@@ -378,8 +366,7 @@ def main():
     # 4) the step's spread: whole steps, each between its own events
     for i in range(K):
         ev[i][0].record(stream)
-        step.partial(i)
-        step.merge()
+        step.step(i)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     step_ms = sorted(a.elapsed_time(b) for a, b in ev)

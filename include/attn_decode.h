@@ -189,8 +189,8 @@ typedef struct ad_sparse {
  * bounds the split length, so that no work group is much longer than the average: 2048 keys,
  * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
  * the matrix-core kernel (whose work groups cost more to start and finish). A split of a paged
- * cache or a block list never covers more than 1038 pages or blocks (the ids it stages), which
- * raises the count for very long caches of small pages. AD_NUM_SPLITS forces the count
+ * cache or a block list never covers more than 1038 pages or blocks (258 pages for MLA: the ids
+ * it stages), which raises the count for very long caches of small pages. AD_NUM_SPLITS forces the count
  * (testing aid, see the conventions above).
  */
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
@@ -283,10 +283,11 @@ int attn_decode(const ad_decode_args *args, const ad_paged *paged, const ad_spar
 int attn_decode_noalloc(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                         int32_t num_splits, void *stream);
 
-/* Number of kernel launches attn_decode makes for these arguments and num_splits (0 = the
- * planner's choice): 1 when the merge runs inside the partial pass, 2 when the merge kernel
- * follows, 0 for an empty batch (e.g. to plan graph capture, or to time the partial kernel on
- * its own). Checks the arguments as attn_decode does (out is not needed). */
+/* Number of kernel launches attn_decode (or, for MLA head dims 576 / 512, attn_decode_mla: always
+ * 2) makes for these arguments and num_splits (0 = the planner's choice): 1 when the merge runs
+ * inside the partial pass, 2 when the merge kernel follows, 0 for an empty batch (e.g. to plan
+ * graph capture, or to time the partial kernel on its own). Checks the arguments as the call does
+ * (out is not needed). */
 int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                          int32_t num_splits, int32_t *launches);
 
