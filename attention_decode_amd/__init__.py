@@ -7,7 +7,7 @@ a prepared-step helper. Importing the package does not load the library; the fir
 and raises if it is not built.
 """
 from ._abi import (  # noqa: F401
-    AD_BF16, AD_F32, AD_KERNEL_MATRIX, AD_KERNEL_MLA, AD_KERNEL_VECTOR, AD_KV_FP8_E4M3, AD_KV_INT4, AD_KV_SAME,
+    AD_BF16, AD_F32, AD_KERNEL_MATRIX, AD_KERNEL_MATRIX16, AD_KERNEL_MLA, AD_KERNEL_VECTOR, AD_KV_FP8_E4M3, AD_KV_INT4, AD_KV_SAME,
     AD_MAX_SPLITS, KERNEL_NAMES, ADError, attn_decode, attn_decode_kernel, attn_decode_last_error,
     attn_decode_launches,
     attn_decode_merge, attn_decode_mla, attn_decode_paged, attn_decode_plan, attn_decode_splitkv,

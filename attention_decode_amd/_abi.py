@@ -17,7 +17,7 @@ LIBRARY = os.path.join(HERE, "libattn_decode.so")
 
 AD_F32, AD_BF16 = 0, 1
 AD_KV_SAME, AD_KV_FP8_E4M3, AD_KV_INT4 = 0, 1, 2
-AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA = 0, 1, 2
+AD_KERNEL_VECTOR, AD_KERNEL_MATRIX, AD_KERNEL_MLA, AD_KERNEL_MATRIX16 = 0, 1, 2, 3
 AD_MAX_SPLITS = 256
 AD_PROBE_SINK_WORDS = 4096
 AD_NOALLOC_SCRATCH_BYTES = 32 << 20
@@ -264,11 +264,12 @@ def attn_decode_launches(args: DecodeArgs, paged: Paged | None = None, sparse: S
     return n.value
 
 
-KERNEL_NAMES = {0: "partial_valu_kernel", 1: "partial_mfma_kernel", 2: "mla_partial_kernel"}
+KERNEL_NAMES = {0: "partial_valu_kernel", 1: "partial_mfma_kernel", 2: "mla_partial_kernel",
+                3: "partial_mfma16_kernel"}
 
 
 def attn_decode_kernel(args: DecodeArgs) -> int:
-    """AD_KERNEL_VECTOR / AD_KERNEL_MATRIX / AD_KERNEL_MLA: the partial-pass kernel the calls run
+    """AD_KERNEL_VECTOR / AD_KERNEL_MATRIX16 / AD_KERNEL_MATRIX / AD_KERNEL_MLA: the partial-pass kernel the calls run
     (KERNEL_NAMES maps it to the kernel's name in a profile)."""
     k = ctypes.c_int32()
     _check("attn_decode_kernel", lib().attn_decode_kernel(ctypes.byref(args), ctypes.byref(k)))

@@ -20,14 +20,15 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "splitkv_valu.hip", "splitkv_mfma.hip", "mla_mfma.hip", "merge.hip", "probe.hip"]
+SOURCES = ["api.cpp", "splitkv_valu.hip", "splitkv_mfma.hip", "splitkv_mfma16.hip", "mla_mfma.hip", "merge.hip", "probe.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-result"]
 DEVICE = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-# Per-file device flags. The matrix-core kernel keeps its accumulators in VGPRs: with the default
+# Per-file device flags. The matrix-core kernels keep their accumulators in VGPRs: with the default
 # heuristic they live in AGPRs and every loop iteration copies all of them to VGPRs and back.
-EXTRA = {"splitkv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"splitkv_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "splitkv_mfma16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

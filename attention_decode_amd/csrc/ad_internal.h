@@ -149,6 +149,7 @@ struct MergeParams {
 hipError_t launch_partial_valu(const PartialParams &p, int dtype, int head_dim, int rows_padded, int mode,
                                hipStream_t stream);
 hipError_t launch_partial_mfma(const PartialParams &p, int head_dim, int mode, hipStream_t stream);
+hipError_t launch_partial_mfma16(const PartialParams &p, int head_dim, int mode, hipStream_t stream);
 hipError_t launch_partial_mla(const PartialParams &p, hipStream_t stream);
 hipError_t launch_merge(const MergeParams &p, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, int64_t bytes, uint32_t *sink, int groups, hipStream_t stream);

@@ -172,11 +172,13 @@ int check_sparse(const ad_sparse *sp) {
 int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, 128); }
 
 // Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
-// units: the matrix-core kernel takes 32 rows per unit (bf16 with more than 8 rows, and any fp8
-// cache), the vector kernel up to 8 (4 with an fp8 or int4 cache; an int4 cache always runs
-// there). AD_PARTIAL_KERNEL=valu|mfma overrides the choice (bf16 caches and fp8 only).
+// units: the matrix-core kernels (bf16 with more than 8 rows, and any fp8 cache) take 16 rows per
+// unit when the rows fit 16 and 32 otherwise; the vector kernel takes up to 8 (4 with an fp8 or
+// int4 cache; an int4 cache always runs there). AD_PARTIAL_KERNEL=valu|mfma overrides the choice
+// of kernel (bf16 caches and fp8 only) and AD_MFMA_TILE=16|32 the matrix-core tile (testing aids).
 struct Rows {
     bool mfma;
+    bool tile16;   // matrix cores, 16-row units (v_mfma_f32_16x16x32_bf16)
     int per_unit;  // rows one unit holds (the vector kernel's padded row count)
     int blocks;    // units per KV head
 };
@@ -193,9 +195,17 @@ Rows row_plan(const ad_decode_args *a) {
     }
     Rows x{};
     x.mfma = mfma;
-    // an fp8 or int4 unit takes at most 4 rows (8 would exceed a lane's registers)
-    const int valu_max = (fp8 || int4) ? 4 : 8;
-    x.per_unit = mfma ? 32 : std::min(valu_max, r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8);
+    if (mfma) {
+        // 16-row units when the rows fit them: a unit of r <= 16 rows padded to 32 makes twice the
+        // matrix-core products and holds twice the registers of the 16-row form
+        x.tile16 = r <= 16;
+        if (const char *t = knob("AD_MFMA_TILE")) x.tile16 = !strcmp(t, "16");
+        x.per_unit = x.tile16 ? 16 : 32;
+    } else {
+        // an fp8 or int4 unit takes at most 4 rows (8 would exceed a lane's registers)
+        const int valu_max = (fp8 || int4) ? 4 : 8;
+        x.per_unit = std::min(valu_max, r <= 1 ? 1 : r <= 2 ? 2 : r <= 4 ? 4 : 8);
+    }
     x.blocks = (int)cdiv(r, x.per_unit);
     return x;
 }
@@ -230,12 +240,13 @@ int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
 
 // Keys per split at most when lengths may be ragged. Measured on 64 paged sequences of
 // 128..8192 keys (8 KV heads, 4 query rows each), repeated same-box runs: the vector kernel takes
-// 191.8 us at 1664 keys (5 splits), 198.0 at 2048, 196.0 at 1366; the matrix-core kernel, whose
-// work group costs more to start and to combine, 224.3 us at 4096 keys (2 splits) against 230.0
-// at 2048 with 1-8 draft tokens, and 141.4 against 146.1 on an fp8 cache. The vector kernel's
-// shorter bound applies only to grids of several rounds at 2048, where shorter splits even out
-// the ragged tail; a grid of one round would spill into a second (16 sequences of 4096 keys:
-// 50 -> 56 us). Other paths (MLA) keep 2048.
+// 191.8 us at 1664 keys (5 splits), 198.0 at 2048, 196.0 at 1366; the 32-row matrix-core kernel,
+// whose work group costs more to start and to combine, 224.3 us at 4096 keys (2 splits) against
+// 230.0 at 2048 with 1-8 draft tokens (32 rows per KV head). The 16-row matrix-core kernel, two
+// work groups per compute unit, on the fp8 cache: 131.8 us at 2048 keys (4 splits), 134.4 at 2731,
+// 137.6 at 4096. The vector kernel's shorter bound applies only to grids of several rounds at
+// 2048, where shorter splits even out the ragged tail; a grid of one round would spill into a
+// second (16 sequences of 4096 keys: 50 -> 56 us). Other paths (MLA) keep 2048.
 constexpr int64_t kRaggedChunkVector = 1664;
 constexpr int64_t kRaggedChunkMatrix = 4096;
 constexpr int64_t kRaggedChunk = 2048;
@@ -265,8 +276,11 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
         if (a->seq_lens) {
             int64_t most = kRaggedChunk;
             if (path != Path::Mla) {
-                if (row_plan(a).mfma)
+                const Rows rows = row_plan(a);
+                if (rows.mfma && !rows.tile16)
                     most = kRaggedChunkMatrix;
+                else if (rows.mfma)
+                    most = kRaggedChunk;
                 else if (units * std::max<int64_t>(S, cdiv(span, kRaggedChunk)) >= 2 * (int64_t)cus)
                     most = kRaggedChunkVector;
             }
@@ -343,6 +357,7 @@ hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mod
     // one work group per (split, b, KV head, row block) on a 1-D grid
     const int64_t groups = (int64_t)p.num_splits * a->batch * a->num_kv_heads * rows.blocks;
     if (groups > INT_MAX) return hipErrorInvalidConfiguration;
+    if (rows.mfma && rows.tile16) return ad::launch_partial_mfma16(p, a->head_dim_qk, mode, stream);
     if (rows.mfma && a->kv_format == AD_KV_SAME) {
         // Whole-row loads staged through LDS (bf16 caches): every load reads whole lines once, at
         // the price of a round trip through LDS per tile. That pays when a compute unit runs
@@ -695,7 +710,12 @@ int attn_decode_kernel(const ad_decode_args *args, int32_t *kind) {
     const bool mla = args->head_dim_qk == 576 && args->head_dim_v == 512;
     const int rc = check_args(args, mla ? Path::Mla : Path::Contig, false);
     if (rc != AD_OK) return rc;
-    *kind = mla ? AD_KERNEL_MLA : row_plan(args).mfma ? AD_KERNEL_MATRIX : AD_KERNEL_VECTOR;
+    if (mla) {
+        *kind = AD_KERNEL_MLA;
+    } else {
+        const Rows rows = row_plan(args);
+        *kind = !rows.mfma ? AD_KERNEL_VECTOR : rows.tile16 ? AD_KERNEL_MATRIX16 : AD_KERNEL_MATRIX;
+    }
     return ok();
 }
 

@@ -1,0 +1,516 @@
+// splitkv_mfma16.hip -- partial split-KV pass on the matrix cores for work units of at most 16 query
+// rows (bf16 or fp8 caches): small GQA groups times speculative tokens, e.g. 4 query heads per KV
+// head over an fp8 cache.
+//
+// It computes what the 32-row matrix-core pass (splitkv_mfma.hip) computes: per work unit (split s,
+// block of up to 16 query rows r = t*G + g of KV head h, sequence b) the attention of those rows
+// restricted to the split's keys, stored as o_s = acc / l with a natural-log LSE (mslk
+// splitk_kernels.py, _fwd_kernel_splitK epilogue), online softmax in base-2 units. The group of
+// query heads sharing a KV head is padded to 16 rows rather than 32 (TensorRT-LLM mha.cu rounds its
+// warp tile of heads x tokens up to a multiple of 16), so a 4-row group makes 4x the needed
+// matrix-core products instead of 8x, and a wave needs half the registers: several work groups
+// share a compute unit and cover each other's arithmetic with their loads.
+//
+// Layout on v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16 and 8 reduction elements chosen by
+// l/16; B likewise with column l%16; C: lane l holds column l%16 of rows 4(l/16) .. +3):
+//
+//   * Scores transposed, S^T = K Q^T, per 16-key block kb of a 32-key tile: K is the A operand, a
+//     lane holding 8 head-dim elements of key 16kb + l%16 straight from HBM; Q is the B operand,
+//     lane l holding query row l%16, in registers for the whole unit. The result leaves lane l with
+//     keys 16kb + 4(l/16) .. +3 of query row l%16: 8 keys per tile, so the row max and sum are an
+//     in-lane reduction and two lane swaps (l^16, l^32).
+//   * Those 8 probabilities, rounded to bf16, are the A operand of P.V as they stand: reduction
+//     index 8(l/16) + i of lane l is key 16(i/4) + 4(l/16) + i%4. V is the B operand with the same
+//     key order, read from a per-wave LDS tile with ds_read_b64_tr_b16 (the tile's 16-byte chunks
+//     XOR-swizzled by row as in the 32-row pass: both the stores of 16 rows and the transposing
+//     reads of 4 rows x 2 chunks are free of bank conflicts).
+//   * Head-dim order of the score reduction: k-step ks of a bf16 cache covers elements 32ks ..
+//     32ks+31, lane group l/16 taking 8 of them; an fp8 lane loads 16 bytes (elements 64j + 16(l/16)
+//     .. +15) and converts them into the operands of k-steps 2j and 2j+1. Q is loaded in the same
+//     order (the order of a reduction is free as long as both operands share it).
+//   * Everything else follows the 32-row pass: a work group of 4 waves each taking every 4th 32-key
+//     tile with loads one tile ahead; keys outside the split, past the sequence, seen by no row of
+//     the unit or in unlisted blocks never read (their loads go to the unit's own query row, their
+//     probability is 0); masking only on tiles that are not fully visible; lazy rescaling through a
+//     small LDS exchange; P rounded to bf16 with the normaliser summing the rounded values
+//     (TensorRT-LLM mha.cu computeRowSum) and the LSE the fp32 ones; fp8 (OCP E4M3) rows times
+//     their fp32 scales (TensorRT-LLM mha.cu kvCacheScale; mslk splitk_kernels.py,
+//     _process_fp8_quantization), key scales on the fp32 scores, value scales in P before its bf16
+//     rounding, the normaliser summing each rounded product divided by its scale; the 4 waves
+//     combined once through LDS; the in-pass merge when the host asks for one launch.
+#include "ad_internal.h"
+#include "fused_merge.h"
+#include "mfma_util.h"
+
+#include <limits.h>
+#include <math.h>
+
+#include <type_traits>
+
+namespace ad {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;  // keys per wave per step: two 16-key blocks
+constexpr int kRows = 16;  // query rows per work unit
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+}
+
+// All four lanes l, l^16, l^32, l^48 get the max / sum of their four values.
+__device__ __forceinline__ float quad_max(float x) { return pair_max(pair16_max(x)); }
+__device__ __forceinline__ float quad_sum(float x) { return pair_sum(pair16_sum(x)); }
+
+template <int D, int MODE, bool FP8>
+__global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialParams p) {
+    constexpr int kKs = D / 32;                   // k-steps of the score product
+    constexpr int kCols = D / 16;                 // 16-column blocks of the output
+    constexpr int kRowBytes = D * 2;              // one bf16 row of the LDS V tile
+    constexpr int kLoads = FP8 ? D / 64 : kKs;    // 16-byte pieces per lane, key block and operand
+    static_assert(!FP8 || D == 128, "an fp8 cache has head dim 128");
+
+    const UnitId wu = decode_unit(p);
+    const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c16 = lane & 15, grp = lane >> 4;
+    const int G = p.group, Q = p.q_len, S = p.num_splits, Dv = p.head_dim_v;
+    const QRows qrows = q_rows(p.q_starts, Q, b);
+    const int Qb = qrows.n, R = G * Qb;
+    const int r0 = rb * kRows, nr = min(kRows, R - r0);
+    if (nr <= 0) return;  // uniform: a row block past the sequence's last token
+    const int L = p.seq_lens ? p.seq_lens[b] : p.kv_len_max;
+
+    int vlen = L;
+    if constexpr (MODE == KV_SPARSE) vlen = p.num_blocks[b * p.nb_s[0] + h * p.nb_s[1]] << p.block_shift;
+    const int t0 = split * p.chunk;
+    const int t1 = min(t0 + p.chunk, vlen);
+
+    auto out_row = [&](int r) -> int64_t {  // r: row inside the unit
+        const int ra = r0 + r, t = ra / G, g = ra - t * G;
+        return (int64_t)(b * Q + t) * p.num_q_heads + h * G + g;
+    };
+
+    if (t0 >= t1) {  // uniform
+        if (p.counters) {  // fused merge: only a unit without keys writes here (out = 0, lse = -inf)
+            if (vlen <= 0 && split == 0) fused_write_empty<kThreads, D>(p, nr, out_row);
+            return;
+        }
+        if (p.write_empty) {
+            for (int i = tid; i < nr * Dv; i += kThreads) {
+                const int r = i / Dv, d = i - r * Dv;
+                p.part_o[(out_row(r) * S + split) * Dv + d] = 0.f;
+            }
+            for (int r = tid; r < nr; r += kThreads) p.part_lse[out_row(r) * S + split] = -INFINITY;
+        }
+        return;
+    }
+
+    __shared__ int s_map[kMapCapacity];
+    // per-wave V tiles during the loop, per-wave fp32 accumulators for the final combine
+    constexpr int kBufBytes = kWaves * kRows * D * 4 > kWaves * kTile * kRowBytes ? kWaves * kRows * D * 4
+                                                                                  : kWaves * kTile * kRowBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
+    __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
+    __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
+    __shared__ float s_fw[kWaves][kRows], s_inv[kRows];  // combine weights of the waves' partials, 1 / l
+    // fp8 cache: per wave and tile key, the key scale, the value scale and its reciprocal (0 for a key
+    // that is not read), read back in the score accumulator's key order
+    __shared__ __attribute__((aligned(16))) float s_ks[FP8 ? kWaves : 1][kTile], s_vs[FP8 ? kWaves : 1][kTile],
+        s_vr[FP8 ? kWaves : 1][kTile];
+
+    const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
+    const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
+    if constexpr (MODE == KV_PAGED) {
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
+        const int32_t *bt = p.block_table + b * p.bt_stride + map_first;
+        for (int i = tid; i < n; i += kThreads) s_map[i] = bt[i];
+    } else if constexpr (MODE == KV_SPARSE) {
+        const int n = ((t1 - 1) >> map_shift) - map_first + 1;
+        const int32_t *ix = p.block_idx + b * p.ix_s[0] + h * p.ix_s[1];
+        for (int i = tid; i < n; i += kThreads) s_map[i] = ix[(int64_t)(map_first + i) * p.ix_s[2]];
+    }
+    if constexpr (MODE != KV_CONTIG) __syncthreads();
+    const int map_mask = (1 << map_shift) - 1;
+
+    // ---- this lane's query row (row c16 of the unit) as the B operand, and its visible range
+    const uint16_t *qbase = static_cast<const uint16_t *>(p.q) +
+                            (p.q_starts ? (int64_t)qrows.first * p.q_s[1] : b * p.q_s[0]) +
+                            (int64_t)(h * G) * p.q_s[2];
+    u32x4 qb[kKs];
+    int lo_r = INT_MIN, hi_r = INT_MAX;
+    // Tree mask: the last Qb keys are the drafts; this lane's row sees draft i only with bit i of
+    // its token's mask row (tm0: drafts 0-31, tm1: 32-63).
+    const int first_draft = L - Qb;
+    uint32_t tm0 = ~0u, tm1 = ~0u;
+    {
+        const int ra = r0 + c16;
+        const int t = ra / G, g = ra - t * G;
+        if (c16 < nr) {
+            const uint16_t *qr = qbase + t * p.q_s[1] + g * p.q_s[2];
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks)  // fp8: the head-dim order of the fp8 K operand
+                qb[ks] = ld16(qr + (FP8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks % 2) : 32 * ks + 8 * grp));
+            const int qpos = L - Qb + t;
+            if (p.causal) hi_r = qpos + 1;
+            if (p.window) lo_r = qpos - p.window + 1;
+            if (p.tree_mask) {
+                const uint32_t *mr = p.tree_mask + (int64_t)(qrows.first + t) * p.mask_words;
+                tm0 = mr[0];
+                tm1 = p.mask_words > 1 ? mr[1] : 0u;
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < kKs; ++ks) qb[ks] = u32x4{0, 0, 0, 0};
+        }
+    }
+    // Visible range of the unit: keys outside [lo_min, hi_max) are seen by no row; keys inside
+    // [lo_max, hi_min) by every row.
+    const int t_first = __builtin_amdgcn_readfirstlane(r0 / G);
+    const int t_last = __builtin_amdgcn_readfirstlane((r0 + nr - 1) / G);
+    // (tree mask: keys from the first draft on are never seen by every row for certain)
+    const int hi_min = min(p.causal ? L - Qb + t_first + 1 : INT_MAX, p.tree_mask ? first_draft : INT_MAX);
+    const int hi_max = p.causal ? L - Qb + t_last + 1 : INT_MAX;
+    const int lo_min = p.window ? L - Qb + t_first - p.window + 1 : INT_MIN;
+    const int lo_max = p.window ? L - Qb + t_last - p.window + 1 : INT_MIN;
+
+    // ---- key addressing: virtual key index v (position in the split's key range) -> logical
+    // position and row offsets. Only called with v < t1.
+    using KV = std::conditional_t<FP8, uint8_t, uint16_t>;  // one K / V element
+    const KV *kbase = static_cast<const KV *>(p.k) + (int64_t)h * p.k_s[2];
+    const KV *vbase = static_cast<const KV *>(p.v) + (int64_t)h * p.v_s[2];
+    const float *ksbase = p.k_scale + (int64_t)h * p.ks_s[2];  // fp8: row scales, indexed like the rows
+    const float *vsbase = p.v_scale + (int64_t)h * p.vs_s[2];
+    if constexpr (MODE != KV_PAGED) {
+        kbase += b * p.k_s[0];
+        vbase += b * p.v_s[0];
+        if constexpr (FP8) {
+            ksbase += b * p.ks_s[0];
+            vsbase += b * p.vs_s[0];
+        }
+    }
+    auto logical = [&](int v) -> int {
+        if constexpr (MODE == KV_SPARSE) return (s_map[(v >> map_shift) - map_first] << map_shift) + (v & map_mask);
+        return v;
+    };
+    // finite (bf16), always readable, at least D elements; an fp8 cache's bytes read from it may
+    // be NaN codes, which never reach the sums (masked scores, zeroed values)
+    const KV *safe = reinterpret_cast<const KV *>(qbase);
+
+    // Lane l loads key 16 kb + l%16 of the tile for kb = 0, 1: bf16 pieces at elements 32 ks +
+    // 8 (l/16), fp8 pieces at bytes 64 j + 16 (l/16).
+    struct Buf {
+        u32x4 k[2][kLoads];
+        u32x4 v[2][kLoads];
+        float ks[2], vs[2];  // fp8: this lane's key scales as loaded (any value for a key that is not read)
+        bool live[2];        // fp8: this lane's key is read
+        int base;
+    };
+    auto fetch = [&](Buf &f, int base) {
+        f.base = base;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int vb = base + 16 * kb;  // uniform
+            const int v = vb + c16;
+            const KV *kp = safe, *vp = safe;
+            const float *ksp = p.k_scale, *vsp = p.v_scale;  // the arrays' first scales: always readable
+            if (v < t1) {
+                if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
+                    if (v >= lo_min && v < hi_max) {
+                        const int64_t page = s_map[(v >> map_shift) - map_first];
+                        const int slot = v & map_mask;
+                        kp = kbase + page * p.k_s[0] + slot * p.k_s[1];
+                        vp = vbase + page * p.v_s[0] + slot * p.v_s[1];
+                        if constexpr (FP8) {
+                            ksp = ksbase + page * p.ks_s[0] + slot * p.ks_s[1];
+                            vsp = vsbase + page * p.vs_s[0] + slot * p.vs_s[1];
+                        }
+                    }
+                } else {
+                    const int pos = logical(v);
+                    if (pos < L && pos >= lo_min && pos < hi_max) {
+                        kp = kbase + (int64_t)pos * p.k_s[1];
+                        vp = vbase + (int64_t)pos * p.v_s[1];
+                        if constexpr (FP8) {
+                            ksp = ksbase + (int64_t)pos * p.ks_s[1];
+                            vsp = vsbase + (int64_t)pos * p.vs_s[1];
+                        }
+                    }
+                }
+            }
+            if constexpr (FP8) {
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j)
+                    f.k[kb][j] = j == kLoads - 1 ? ld16_last(kp + 64 * j + 16 * grp) : ld16(kp + 64 * j + 16 * grp);
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j)
+                    f.v[kb][j] = j == kLoads - 1 ? ld16_last(vp + 64 * j + 16 * grp) : ld16(vp + 64 * j + 16 * grp);
+                // used only once this buffer is current (a select here would wait for the prefetch)
+                f.ks[kb] = *ksp;
+                f.vs[kb] = *vsp;
+                f.live[kb] = kp != safe;
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) f.k[kb][ks] = ld16(kp + 32 * ks + 8 * grp);
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) f.v[kb][ks] = ld16(vp + 32 * ks + 8 * grp);
+            }
+        }
+    };
+
+    lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;  // this wave's V tile
+    // Transposing-read address of this lane for read rd and output block c: row 16 rd + 4 grp +
+    // (lane&15)/4, chunk 2c + (lane&3)/2, half-chunk lane&1.
+    const int tr_row = 4 * grp + (c16 >> 2);
+    const int tr_chunk = (lane & 3) >> 1;
+    const int tr_byte = (lane & 1) << 3;
+
+    float m = -INFINITY, l = 0.f, lf = 0.f;  // row c16's running state (this lane's keys)
+    f32x4 o[kCols];
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](const Buf &cur, bool full) {
+        // V tile -> LDS: row 16 kb + c16; bf16 chunk 4 ks + grp; fp8 piece j as chunks 8 j + 2 grp (+1)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int row = 16 * kb + c16;
+            lds_u8 *vr = vw + row * kRowBytes;
+            if constexpr (FP8) {
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j) {
+                    u32x4 w = cur.v[kb][j];
+                    if (!full && !cur.live[kb]) w = u32x4{0, 0, 0, 0};  // a key that is not read may hold NaN codes
+                    const int c0 = 8 * j + 2 * grp;
+                    *(__attribute__((address_space(3))) u32x4 *)(vr + ((c0 ^ swz<D>(row)) << 4)) = e4m3_x8(w[0], w[1]);
+                    *(__attribute__((address_space(3))) u32x4 *)(vr + (((c0 + 1) ^ swz<D>(row)) << 4)) =
+                        e4m3_x8(w[2], w[3]);
+                }
+                if (grp == 0) {  // a key that is not read takes scale 0
+                    const float vsv = cur.live[kb] ? cur.vs[kb] : 0.f;
+                    s_ks[wave][row] = cur.live[kb] ? cur.ks[kb] : 0.f;
+                    s_vs[wave][row] = vsv;
+                    s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks)
+                    *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * ks + grp) ^ swz<D>(row)) << 4)) =
+                        cur.v[kb][ks];
+            }
+        }
+        // S^T = K Q^T, one 16-key block at a time
+        f32x4 sc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (FP8) {
+#pragma unroll
+                for (int j = 0; j < kLoads; ++j) {
+                    const u32x4 w = cur.k[kb][j];
+                    sc[kb] = mfma16(e4m3_x8(w[0], w[1]), qb[2 * j], sc[kb]);
+                    sc[kb] = mfma16(e4m3_x8(w[2], w[3]), qb[2 * j + 1], sc[kb]);
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < kKs; ++ks) sc[kb] = mfma16(cur.k[kb][ks], qb[ks], sc[kb]);
+            }
+        }
+        // this lane's keys: 16 kb + 4 grp + e of the tile
+        float sv[2][4];
+        f32x4 vs4[FP8 ? 2 : 1], vr4[FP8 ? 2 : 1];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            if constexpr (FP8) {
+                const f32x4 k4 = *(const f32x4 *)&s_ks[wave][16 * kb + 4 * grp];
+                vs4[kb] = *(const f32x4 *)&s_vs[wave][16 * kb + 4 * grp];
+                vr4[kb] = *(const f32x4 *)&s_vr[wave][16 * kb + 4 * grp];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[kb][e] = sc[kb][e] * (p.scale_log2 * k4[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sv[kb][e] = sc[kb][e] * p.scale_log2;
+            }
+        }
+        if (!full) {  // uniform
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int v4 = cur.base + 16 * kb + 4 * grp;  // keys v4 .. v4+3 share a page / block
+                const int pos4 = v4 < t1 ? logical(v4) : 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int pos = pos4 + e;
+                    bool vis = v4 + e < t1 && pos < L && pos >= lo_r && pos < hi_r;
+                    if (p.tree_mask && vis && pos >= first_draft) {
+                        const int i = pos - first_draft;  // < Qb <= 64: a visible key lies below L
+                        vis = ((i < 32 ? tm0 : tm1) >> (i & 31)) & 1u;
+                    }
+                    sv[kb][e] = vis ? sv[kb][e] : -INFINITY;
+                }
+            }
+        }
+        float mx = sv[0][0];
+#pragma unroll
+        for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j / 4][j % 4]);
+        mx = quad_max(mx);
+        const bool raise = mx > m + kLazyRescale;
+        if (__builtin_amdgcn_ballot_w64(raise) != 0) {  // wave-uniform
+            // Rows that do not move keep factor 1 exactly (exp2(m - m) is NaN while m = -inf).
+            const float alpha = raise ? exp2_fast(m - mx) : 1.f;
+            m = raise ? mx : m;
+            l *= alpha;
+            lf *= alpha;
+            if (grp == 0) s_alpha[wave][c16] = alpha;
+            // output rows of this lane: 4 grp + j
+            const f32x4 a4 = *(const f32x4 *)&s_alpha[wave][4 * grp];
+#pragma unroll
+            for (int c = 0; c < kCols; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) o[c][j] *= a4[j];
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        uint32_t pk[4];
+        const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3F803F80u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int kb = i / 2, e = 2 * (i % 2);
+            const float p0 = exp2_fast(sv[kb][e] - ms), p1 = exp2_fast(sv[kb][e + 1] - ms);  // exp2(-inf) = 0
+            if constexpr (FP8) {  // value scales into P; normaliser from the rounded products / scales
+                const float vs0 = vs4[kb][e], vs1 = vs4[kb][e + 1];
+                pk[i] = pack_bf16(p0 * vs0, p1 * vs1);
+                const float q0 = __uint_as_float(pk[i] << 16), q1 = __uint_as_float(pk[i] & 0xFFFF0000u);
+                l += (vs0 != 0.f ? q0 * vr4[kb][e] : p0) + (vs1 != 0.f ? q1 * vr4[kb][e + 1] : p1);
+            } else {
+                pk[i] = pack_bf16(p0, p1);
+                l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, l, false);
+            }
+            lf += p0 + p1;
+        }
+        // O += P V over the tile's 32 keys, one 16-column block at a time
+        const u32x4 pa = u32x4{pk[0], pk[1], pk[2], pk[3]};
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+            s16x4 part[2];
+#pragma unroll
+            for (int rd = 0; rd < 2; ++rd) {
+                const int row = 16 * rd + tr_row;
+                const int chunk = 2 * c + tr_chunk;
+                part[rd] = ds_read_tr(vw + row * kRowBytes + ((chunk ^ swz<D>(row)) << 4) + tr_byte);
+            }
+            const s16x8 vb = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            o[c] = mfma16(pa, __builtin_bit_cast(u32x4, vb), o[c]);
+        }
+    };
+
+    constexpr int kStride = kWaves * kTile;
+    auto iterate = [&](Buf &cur, Buf &nxt) {
+        fetch(nxt, cur.base + kStride);
+        __builtin_amdgcn_sched_barrier(0);
+        bool full = cur.base + kTile <= t1;
+        if (full) {
+            const int pf = logical(cur.base), pl = logical(cur.base + kTile - 1);
+            full = pl - pf == kTile - 1 && pl < L && pf >= lo_max && pl < hi_min;
+        }
+        compute(cur, full);
+    };
+
+    // Pairs of tiles with the loop's only exit test at the back edge (the loads in flight are the
+    // same on every path into the loop), and an odd last tile after it. One tile in flight per
+    // wave is what the registers hold at two waves per SIMD: a third buffer (two tiles ahead)
+    // spills or halves the occupancy, and either way is slower.
+    const int first = t0 + wave * kTile;
+    const int ntiles = first < t1 ? (t1 - first + kStride - 1) / kStride : 0;
+    Buf A, B;
+    fetch(A, first);
+    int i = 0;
+    for (; i + 2 <= ntiles; i += 2) {
+        iterate(A, B);
+        iterate(B, A);
+    }
+    if (i < ntiles) iterate(A, B);
+
+    // ---- combine the waves: o_s = acc / l, lse_s = (m + log2 lf) * ln 2
+    l = quad_sum(l);
+    lf = quad_sum(lf);
+    __syncthreads();  // every wave is done with its tiles: s_buf now holds the accumulators
+    float *s_o = reinterpret_cast<float *>(s_buf) + wave * kRows * D;
+    if (grp == 0) {
+        s_m[wave][c16] = m;
+        s_l[wave][c16] = l;
+        s_lf[wave][c16] = lf;
+    }
+#pragma unroll
+    for (int c = 0; c < kCols; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s_o[(4 * grp + j) * D + 16 * c + c16] = o[c][j];
+    __syncthreads();
+
+    // Per-row factors, once per row: the weight of each wave's partial and 1 / l. Stores are
+    // agent-scope: a merging group on another XCD reads them (fused merge).
+    if (tid < nr) {
+        const int r = tid;
+        float M = s_m[0][r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+        const float ms = (M == -INFINITY) ? 0.f : M;
+        float lsum = 0.f, lfsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = exp2_fast(s_m[w][r] - ms);
+            s_fw[w][r] = f;
+            lsum += s_l[w][r] * f;
+            lfsum += s_lf[w][r] * f;
+        }
+        s_inv[r] = lsum > 0.f ? 1.f / lsum : 0.f;
+        store_partial(p.part_lse + out_row(r) * S + split,
+                      lsum > 0.f ? (ms + __builtin_amdgcn_logf(lfsum)) * 0.69314718055994531f : -INFINITY);
+    }
+    __syncthreads();
+    const float *s_all = reinterpret_cast<const float *>(s_buf);
+    for (int i = tid; i < nr * D; i += kThreads) {
+        const int r = i / D, d = i - r * D;
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) acc += s_all[(w * kRows + r) * D + d] * s_fw[w][r];
+        store_partial(p.part_o + (out_row(r) * S + split) * Dv + d, acc * s_inv[r]);
+    }
+    if (p.counters) {  // one launch per step: the unit's last split merges (s_buf is free now)
+        const int nsplit = min(S, (vlen + p.chunk - 1) / p.chunk);
+        constexpr int kPerThread = (kRows * D + kThreads - 1) / kThreads;
+        fused_arrive_merge<kThreads, D, kPerThread>(p, wu.unit, nsplit, nr, out_row,
+                                                 reinterpret_cast<float *>(s_buf));
+    }
+}
+
+template <int D, bool FP8>
+hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
+    const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
+    switch (mode) {
+        case KV_CONTIG:
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_CONTIG, FP8>), grid, dim3(kThreads), 0, s, p);
+            break;
+        case KV_PAGED:
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_PAGED, FP8>), grid, dim3(kThreads), 0, s, p);
+            break;
+        default:
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_SPARSE, FP8>), grid, dim3(kThreads), 0, s, p);
+            break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_partial_mfma16(const PartialParams &p, int head_dim, int mode, hipStream_t stream) {
+    if (p.kv_int4) return hipErrorInvalidValue;  // int4 caches run on the vector kernel only
+    if (p.kv_fp8) {  // the host admits an fp8 cache with head dim 128 only
+        if (head_dim != 128) return hipErrorInvalidValue;
+        return by_mode<128, true>(p, mode, stream);
+    }
+    return head_dim == 64 ? by_mode<64, false>(p, mode, stream) : by_mode<128, false>(p, mode, stream);
+}
+
+}  // namespace ad

@@ -33,8 +33,8 @@
  *     cudaErrorNotSupported with a message for a configuration it has no kernel for).
  *     attn_decode_last_error() gives a message for the calling thread's last non-OK return.
  *   - Testing aids: the environment variables AD_NUM_SPLITS (split count, cf. xqa's
- *     XQA_NB_SUB_SEQ), AD_PARTIAL_KERNEL, AD_MFMA_ROWS and AD_FUSED_MERGE (kernel forms, named at
- *     the calls they affect) are read only while AD_TEST_KNOBS=1 is set; otherwise the
+ *     XQA_NB_SUB_SEQ), AD_PARTIAL_KERNEL, AD_MFMA_TILE, AD_MFMA_ROWS and AD_FUSED_MERGE (kernel
+ *     forms, named at the calls they affect) are read only while AD_TEST_KNOBS=1 is set; otherwise the
  *     environment changes nothing.
  *   - Data contracts that are NOT checked (they live in device memory): seq_lens[b] <=
  *     kv_len_max and >= the sequence's query tokens; q_starts nondecreasing with counts of at
@@ -188,10 +188,10 @@ typedef struct ad_sparse {
  * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
  * bounds the split length, so that no work group is much longer than the average: 2048 keys,
  * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
- * the matrix-core kernel (whose work groups cost more to start and finish). A split of a paged
- * cache or a block list never covers more than 1038 pages or blocks (258 pages for MLA: the ids
- * it stages), which raises the count for very long caches of small pages. AD_NUM_SPLITS forces the count
- * (testing aid, see the conventions above).
+ * the 32-row matrix-core kernel (whose work groups cost more to start and finish). A split of a
+ * paged cache or a block list never covers more than 1038 pages or blocks (258 pages for MLA:
+ * the ids it stages), which raises the count for very long caches of small pages. AD_NUM_SPLITS
+ * forces the count (testing aid, see the conventions above).
  */
 int attn_decode_plan(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                      int32_t *num_splits, int32_t *chunk);
@@ -292,16 +292,20 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
                          int32_t num_splits, int32_t *launches);
 
 /* Which partial-pass kernel the calls above run for these arguments (e.g. to name it in a
- * profile): AD_KERNEL_VECTOR (vector ALUs, up to 8 query rows per work unit), AD_KERNEL_MATRIX
- * (matrix cores, 32 rows per unit: bf16 with more than 8 rows per KV head, and every fp8 cache)
- * or AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). Honours AD_PARTIAL_KERNEL=valu / mfma
- * as the calls do (testing aid). Checks the arguments as the calls do (out is not needed). On a
- * bf16 cache the matrix-core kernel reads whole K / V rows and stages K through LDS when the grid
- * holds more work groups than compute units, else K goes from HBM straight to the matrix cores;
- * both give the same bits, and AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
+ * profile): AD_KERNEL_VECTOR (vector ALUs, up to 8 query rows per work unit), the matrix cores
+ * for bf16 with more than 8 rows per KV head and for every fp8 cache, as AD_KERNEL_MATRIX16
+ * (16 rows per unit, when G * q_len <= 16) or AD_KERNEL_MATRIX (32 rows per unit), or
+ * AD_KERNEL_MLA (head_dim_qk 576 with head_dim_v 512). The rows of a KV head's group padded to
+ * 16 are the warp tile of TensorRT-LLM mha.cu (heads x tokens rounded up to a multiple of 16).
+ * Honours AD_PARTIAL_KERNEL=valu / mfma and AD_MFMA_TILE=16 / 32 as the calls do (testing aids).
+ * Checks the arguments as the calls do (out is not needed). On a bf16 cache the 32-row kernel
+ * reads whole K / V rows and stages K through LDS when the grid holds more work groups than
+ * compute units, else K goes from HBM straight to the matrix cores; both give the same bits, and
+ * AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
 #define AD_KERNEL_VECTOR 0
 #define AD_KERNEL_MATRIX 1
 #define AD_KERNEL_MLA 2
+#define AD_KERNEL_MATRIX16 3
 int attn_decode_kernel(const ad_decode_args *args, int32_t *kind);
 
 /* attn_decode over a paged cache (paged must not be NULL); the same workspace contract. */

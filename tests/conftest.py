@@ -10,8 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 if HERE not in sys.path:
     sys.path.insert(0, HERE)
 
-# The library's testing aids (AD_NUM_SPLITS, AD_PARTIAL_KERNEL, AD_MFMA_ROWS, AD_FUSED_MERGE) are
-# read only while this switch is set; the tests set them per case.
+# The library's testing aids (AD_NUM_SPLITS, AD_PARTIAL_KERNEL, AD_MFMA_TILE, AD_MFMA_ROWS,
+# AD_FUSED_MERGE) are read only while this switch is set; the tests set them per case.
 os.environ["AD_TEST_KNOBS"] = "1"
 
 

@@ -362,6 +362,8 @@ def test_testing_aids_need_the_switch(monkeypatch):
     q, k, v, out = _tensors(Hq=2, Hkv=2)   # one query row per KV head: the vector kernel
     a = _abi.make_args(q, k, v, scale=0.1, out=out)
     monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
+    assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_MATRIX16
+    monkeypatch.setenv("AD_MFMA_TILE", "32")
     assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_MATRIX
     monkeypatch.setenv("AD_TEST_KNOBS", "0")
     assert _abi.attn_decode_kernel(a) == _abi.AD_KERNEL_VECTOR
@@ -387,23 +389,34 @@ def test_workspace_size_takes_the_block_list():
 
 def test_kernel_query(monkeypatch):
     """attn_decode_kernel names the partial-pass kernel: vector ALUs for up to 8 rows per KV head
-    and for fp32, matrix cores for more bf16 rows and for every fp8 cache, the MLA kernel for the
-    576 / 512 head dims; AD_PARTIAL_KERNEL overrides the bf16 choice."""
+    and for fp32, matrix cores for more bf16 rows and for every fp8 cache (16-row units up to 16
+    rows per KV head, 32-row units above), the MLA kernel for the 576 / 512 head dims;
+    AD_PARTIAL_KERNEL overrides the bf16 choice and AD_MFMA_TILE the matrix-core units."""
     monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+    monkeypatch.delenv("AD_MFMA_TILE", raising=False)
     a, keep = _args()  # 8 / 2 heads: 4 rows per KV head
     assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
     q, k, v, out = _tensors(Hq=64, Hkv=2)
     assert ad.attn_decode_kernel(_abi.make_args(q, k, v, scale=0.1, out=out)) == ad.AD_KERNEL_MATRIX
+    for Hq, kind in ((18, ad.AD_KERNEL_MATRIX16), (32, ad.AD_KERNEL_MATRIX16), (34, ad.AD_KERNEL_MATRIX)):
+        q, k, v, out = _tensors(Hq=Hq, Hkv=2)   # 9, 16 and 17 rows per KV head
+        assert ad.attn_decode_kernel(_abi.make_args(q, k, v, scale=0.1, out=out)) == kind, Hq
+    monkeypatch.setenv("AD_MFMA_TILE", "32")
+    assert ad.attn_decode_kernel(_abi.make_args(q, k, v, scale=0.1, out=out)) == ad.AD_KERNEL_MATRIX
+    monkeypatch.setenv("AD_MFMA_TILE", "16")
+    assert ad.attn_decode_kernel(_abi.make_args(q, k, v, scale=0.1, out=out)) == ad.AD_KERNEL_MATRIX16
+    monkeypatch.delenv("AD_MFMA_TILE")
+    assert ad.KERNEL_NAMES[ad.AD_KERNEL_MATRIX16] == "partial_mfma16_kernel"
     q32, k32, v32, o32 = _tensors(dtype=torch.float32, Hq=64, Hkv=2)
     assert ad.attn_decode_kernel(_abi.make_args(q32, k32, v32, scale=0.1, out=o32)) == ad.AD_KERNEL_VECTOR
     kb = torch.zeros(2, 2, 64, 128, dtype=torch.uint8).permute(0, 2, 1, 3)
     ks = torch.ones(2, 2, 64, dtype=torch.float32).permute(0, 2, 1)
     f = _abi.make_args(keep[0], kb, kb, scale=0.1, out=keep[3], k_scale=ks, v_scale=ks)
-    assert ad.attn_decode_kernel(f) == ad.AD_KERNEL_MATRIX
+    assert ad.attn_decode_kernel(f) == ad.AD_KERNEL_MATRIX16
     monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
     assert ad.attn_decode_kernel(f) == ad.AD_KERNEL_VECTOR
     monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
-    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX16
     qm = torch.zeros(2, 1, 16, 512, dtype=torch.bfloat16)
     ckv = torch.zeros(4, 64, 1, 512, dtype=torch.bfloat16)
     m = _abi.make_args(qm, ckv, None, head_dim_qk=576, scale=0.1)

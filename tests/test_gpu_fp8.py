@@ -12,7 +12,9 @@ from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-KERNELS = ["mfma", "valu"]  # the matrix-core default, and the vector form (AD_PARTIAL_KERNEL=valu)
+# the matrix-core kernel in its 16-row and 32-row units (AD_MFMA_TILE), and the vector form
+# (AD_PARTIAL_KERNEL=valu)
+KERNELS = ["mfma16", "mfma32", "valu"]
 
 
 def force(monkeypatch, kernel):
@@ -20,6 +22,7 @@ def force(monkeypatch, kernel):
         monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
     else:
         monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+        monkeypatch.setenv("AD_MFMA_TILE", kernel[4:])
 
 
 def run(w, num_splits=None, fused=True):
@@ -29,8 +32,12 @@ def run(w, num_splits=None, fused=True):
     return out.cpu(), lse.cpu(), step
 
 
-def test_workload6_full(orc):
-    say("[gpu] workload 6 (fp8 paged ragged): full size, every row")
+@pytest.mark.parametrize("tile", ["default", "32"])
+def test_workload6_full(orc, monkeypatch, tile):
+    """The planner's choice (16-row units) and the 32-row units, every row."""
+    if tile != "default":
+        monkeypatch.setenv("AD_MFMA_TILE", tile)
+    say(f"[gpu] workload 6 (fp8 paged ragged): full size, every row, tile {tile}")
     w = inputs.make(6)
     out, lse, step = run(w)
     say(f"  splits {step.splits}")

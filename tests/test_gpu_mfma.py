@@ -30,10 +30,13 @@ def kernel(name):
             os.environ["AD_PARTIAL_KERNEL"] = old
 
 
-@pytest.fixture(autouse=True, params=["cols", "rows"])
+@pytest.fixture(autouse=True, params=["cols", "rows", "tile16"])
 def load_form(request, monkeypatch):
-    """Every test runs with both load forms of the bf16 matrix-core kernel: lane pairs that read
-    K as the matrix operand straight from HBM (cols), and whole rows staged through LDS (rows)."""
+    """Every test runs in the three forms of the bf16 matrix-core pass: 32-row units whose lane
+    pairs read K as the matrix operand straight from HBM (cols) or whose waves read whole rows and
+    stage them through LDS (rows), and 16-row units (tile16; a KV head with more rows takes several
+    units)."""
+    monkeypatch.setenv("AD_MFMA_TILE", "16" if request.param == "tile16" else "32")
     monkeypatch.setenv("AD_MFMA_ROWS", "1" if request.param == "rows" else "0")
     return request.param
 
@@ -157,7 +160,7 @@ def test_split_invariance():
 # ------------------------------------------------------------------------------ forced kernel choice
 @pytest.mark.parametrize("G,Q", [(1, 1), (4, 1), (8, 1), (2, 3)])
 def test_mfma_forced_on_few_rows(orc, G, Q):
-    """The matrix-core kernel also serves 1..8 rows (padded to 32)."""
+    """The matrix-core kernels also serve 1..8 rows (padded to 32 or 16)."""
     say(f"[gpu] forced mfma G={G} Q={Q}")
     w = inputs.contiguous(batch=3, num_q_heads=G * 2, num_kv_heads=2, head_dim=128, kv_len=600, q_len=Q,
                           seq_lens=[600, 77, 5], seed=400 + G + Q, causal=True, window=200)

@@ -12,12 +12,14 @@ from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-KERNELS = ["valu", "mfma", "mfma_rows"]  # mfma_rows: the matrix-core kernel's whole-row load form
+# mfma: 32-row matrix-core units, mfma_rows: their whole-row load form, mfma16: 16-row units
+KERNELS = ["valu", "mfma", "mfma_rows", "mfma16"]
 
 
 def force(monkeypatch, kernel):
     monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu" if kernel == "valu" else "mfma")
     monkeypatch.setenv("AD_MFMA_ROWS", "1" if kernel == "mfma_rows" else "0")
+    monkeypatch.setenv("AD_MFMA_TILE", "16" if kernel == "mfma16" else "32")
 
 
 def run(w, num_splits=None):
