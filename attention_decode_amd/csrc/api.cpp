@@ -172,10 +172,11 @@ int check_sparse(const ad_sparse *sp) {
 int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, 128); }
 
 // Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
-// units: the matrix-core kernels (bf16 with more than 8 rows, and any fp8 cache) take 16 rows per
-// unit when the rows fit 16 and 32 otherwise; the vector kernel takes up to 8 (4 with an fp8 or
-// int4 cache; an int4 cache always runs there). AD_PARTIAL_KERNEL=valu|mfma overrides the choice
-// of kernel (bf16 caches and fp8 only) and AD_MFMA_TILE=16|32 the matrix-core tile (testing aids).
+// units: the matrix-core kernels (bf16 with more than 8 rows, any fp8 cache, and an int4 cache of
+// one coefficient group per row) take 16 rows per unit when the rows fit 16 and 32 otherwise (an
+// int4 cache always 16); the vector kernel takes up to 8 (4 with an fp8 or int4 cache; an int4
+// cache of 2, 4 or 8 groups per row always runs there). AD_PARTIAL_KERNEL=valu|mfma overrides the
+// choice of kernel where both exist, and AD_MFMA_TILE=16|32 the matrix-core tile (testing aids).
 struct Rows {
     bool mfma;
     bool tile16;   // matrix cores, 16-row units (v_mfma_f32_16x16x32_bf16)
@@ -186,10 +187,12 @@ struct Rows {
 Rows row_plan(const ad_decode_args *a) {
     const int r = (a->num_q_heads / a->num_kv_heads) * a->q_len;
     const char *force = knob("AD_PARTIAL_KERNEL");
-    // an fp8 cache takes the matrix cores by default (the vector path converts too slowly)
+    // quantised caches take the matrix cores by default (the vector path converts every key's
+    // values once per row block, and is bound by its ALUs)
     const bool fp8 = a->kv_format == AD_KV_FP8_E4M3, int4 = a->kv_format == AD_KV_INT4;
-    bool mfma = a->dtype == AD_BF16 && (r > 8 || fp8) && !int4;
-    if (force && a->dtype == AD_BF16 && !int4) {  // an int4 cache has the vector kernel only
+    const bool int4_mfma = int4 && a->kv_groups == 1;  // the matrix-core int4 form: one group per row
+    bool mfma = a->dtype == AD_BF16 && (r > 8 || fp8 || int4_mfma) && (!int4 || int4_mfma);
+    if (force && a->dtype == AD_BF16 && (!int4 || int4_mfma)) {
         if (!strcmp(force, "mfma")) mfma = true;
         if (!strcmp(force, "valu")) mfma = false;
     }
@@ -200,6 +203,7 @@ Rows row_plan(const ad_decode_args *a) {
         // matrix-core products and holds twice the registers of the 16-row form
         x.tile16 = r <= 16;
         if (const char *t = knob("AD_MFMA_TILE")) x.tile16 = !strcmp(t, "16");
+        if (int4) x.tile16 = true;  // the int4 form exists in 16-row units only
         x.per_unit = x.tile16 ? 16 : 32;
     } else {
         // an fp8 or int4 unit takes at most 4 rows (8 would exceed a lane's registers)

@@ -46,7 +46,7 @@ KERNELS = {  # traffic tag, the launches attn_decode makes for the workload (tim
     5: ("mla_partial", "mla_partial_kernel + merge_kernel (two launches per step)"),
     6: ("partial_mfma16_paged_fp8", "partial_mfma16_kernel, fp8 cache, 16-row units + merge_kernel (two launches per step)"),
     7: ("partial_mfma_paged_spec", "partial_mfma_kernel, whole-row loads, draft trees + merge_kernel (two launches per step)"),
-    8: ("partial_valu_paged_int4", "partial_valu_kernel_int4 + merge_kernel (two launches per step)"),
+    8: ("partial_mfma16_paged_int4", "partial_mfma16_kernel, int4 cache, 16-row units + merge_kernel (two launches per step)"),
 }
 
 

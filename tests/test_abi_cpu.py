@@ -455,7 +455,8 @@ def test_spec_decoding_rejections():
 
 def test_int4_cache_rejections(monkeypatch):
     """An int4 cache: bf16 queries, head dim 128, kv_groups 1/2/4/8, 4-byte aligned rows, not with
-    MLA, always the vector kernel."""
+    MLA; rows of one group on the 16-row matrix-core kernel (the vector kernel on request), rows of
+    more groups always on the vector kernel."""
     q, _, _, out = _tensors()
     kw = torch.zeros(2, 2, 64, 17, dtype=torch.int32).permute(0, 2, 1, 3)
     a = _abi.make_args(q, kw, kw, scale=0.1, out=out)
@@ -464,10 +465,18 @@ def test_int4_cache_rejections(monkeypatch):
     def kind(args):
         return _abi.lib().attn_decode_kernel(ctypes.byref(args), ctypes.byref(ctypes.c_int32()))
 
-    assert kind(a) == 0 and ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    assert kind(a) == 0 and ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX16
+    monkeypatch.setenv("AD_MFMA_TILE", "32")   # the int4 form exists in 16-row units only
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_MATRIX16
+    monkeypatch.delenv("AD_MFMA_TILE")
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    a.kv_groups = 4
     monkeypatch.setenv("AD_PARTIAL_KERNEL", "mfma")
     assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
     monkeypatch.delenv("AD_PARTIAL_KERNEL")
+    assert ad.attn_decode_kernel(a) == ad.AD_KERNEL_VECTOR
+    a.kv_groups = 1
     b = _abi.make_args(q, kw, kw, scale=0.1, out=out)
     b.kv_groups = 3
     assert kind(b) == -7
