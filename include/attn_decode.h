@@ -221,8 +221,9 @@ size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *pa
  *            key gets o_s = 0, lse_s = -inf (mslk splitk_kernels.py: zeros when l == 0).
  * args->out and args->lse are ignored. num_splits in [1, AD_MAX_SPLITS]; 0 = the planner's
  * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, any G * q_len (bf16 with
- * more than 8 rows per KV head, and every fp8 cache, runs on the matrix cores, 32 rows per work
- * unit; otherwise the vector ALUs take up to 8 rows per work unit; attn_decode_kernel tells which).
+ * more than 8 rows per KV head, every fp8 cache and an int4 cache of one coefficient group per row
+ * run on the matrix cores, 16 or 32 rows per work unit; otherwise the vector ALUs take up to 8 rows
+ * per work unit; attn_decode_kernel tells which).
  */
 int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                         int32_t num_splits, float *part_o, float *part_lse, void *stream);
