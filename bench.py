@@ -103,8 +103,9 @@ class Step:
         nbytes = _abi.attn_decode_workspace_size(self.sets[0][0], self.paged, self.splits, self.sparse)
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
         self.launches = _abi.attn_decode_launches(self.sets[0][0], self.paged, self.sparse, self.splits)
-        kind = _abi.KERNEL_NAMES[_abi.attn_decode_kernel(self.sets[0][0])]
-        if w.kv_format == "int4":  # the vector kernel's int4 form has a symbol of its own
+        kid = _abi.attn_decode_kernel(self.sets[0][0])
+        kind = _abi.KERNEL_NAMES[kid]
+        if w.kv_format == "int4" and kid == _abi.AD_KERNEL_VECTOR:  # the vector kernel's int4 form has a symbol of its own
             kind += "_int4"
         if self.launches == 1:
             self.kernel_name = f"{kind} (merge inside; the whole step)"
