@@ -71,6 +71,8 @@ struct PartialParams {
     int64_t q2_s[3];
     const void *k2;
     int64_t k2_s[3];
+    // Longest-piece-first placement (decode_unit_lpt): set by the host for ragged lengths.
+    int32_t lpt;
 };
 
 // Work-group placement of the GQA partial passes: a 1-D grid of (units x splits) groups, unit =
@@ -90,6 +92,106 @@ __device__ __forceinline__ UnitId decode_unit(const PartialParams &p) {
     const int bh = u.unit / p.row_blocks;
     u.h = bh % p.num_kv_heads;
     u.b = bh / p.num_kv_heads;
+    return u;
+}
+
+// Longest-piece-first placement, for per-sequence (ragged) lengths on grids of several rounds. A
+// piece is (sequence b, split s), and its Hkv x row_blocks work groups are consecutive in the grid.
+// Pieces go out in order of decreasing size, the classic longest-processing-time order for
+// scheduling jobs on identical machines: every full split (chunk keys) first, sequence by
+// sequence, then each sequence's remainder split from the longest down (ties by sequence), then
+// the empty splits. The dispatcher hands the groups out in grid order, so the short remainders
+// fill the last gaps instead of long splits starting last. Every work group ranks the pieces
+// itself from the lengths with the same arithmetic (no launch before the pass), so the groups
+// cover every piece exactly once. The host sets p.lpt only with seq_lens given, no block list, at
+// most kLptMaxBatch sequences, and more work groups than compute units. Every thread of the work
+// group (NT threads) must call it; it synchronises the group.
+constexpr int kLptMaxBatch = 256;
+
+__device__ __forceinline__ int wave_incl_sum(int x) {  // inclusive prefix sum over the wave's lanes
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+template <int NT>
+__device__ __forceinline__ UnitId decode_unit_lpt(const PartialParams &p) {
+    static_assert(NT >= kLptMaxBatch, "one thread per sequence");
+    constexpr int kW = NT / 64;
+    __shared__ int s_rem[kLptMaxBatch];  // remainder keys per sequence (0: none)
+    __shared__ int s_tot[3][kW];          // per wave: full splits, empty splits, remainders
+    __shared__ int s_piece[2];            // (b, split) of this group's piece
+    const int tid = threadIdx.x, wave = tid >> 6;
+    const int B = p.batch, S = p.num_splits, C = p.chunk;
+    const int U = p.num_kv_heads * p.row_blocks;
+    const int k = blockIdx.x / U, sub = blockIdx.x - k * U;
+    // thread tid = sequence tid: full splits n, remainder keys r (in split n), first empty split e
+    int n = 0, r = 0;
+    if (tid < B) {
+        const int L = max(p.seq_lens[tid], 0);
+        n = min(L / C, S);
+        r = n < S ? L - n * C : 0;
+    }
+    const int e = n + (r > 0), ne = tid < B ? S - e : 0;
+    if (tid < kLptMaxBatch) s_rem[tid] = r;
+    const int pn = wave_incl_sum(n), pe = wave_incl_sum(ne);
+    const int nr = __builtin_popcountll(__builtin_amdgcn_ballot_w64(r > 0));
+    if ((tid & 63) == 63) {
+        s_tot[0][wave] = pn;
+        s_tot[1][wave] = pe;
+    }
+    if ((tid & 63) == 0) s_tot[2][wave] = nr;
+    if (tid == 0) {  // overwritten below by the one thread whose piece has rank k (always in range)
+        s_piece[0] = 0;
+        s_piece[1] = 0;
+    }
+    __syncthreads();
+    int F = 0, R = 0, bn = 0, be = 0;  // totals, and the sums of the waves before this one
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+        F += s_tot[0][w];
+        R += s_tot[2][w];
+        if (w < wave) {
+            bn += s_tot[0][w];
+            be += s_tot[1][w];
+        }
+    }
+    const int first_n = bn + pn - n, first_e = be + pe - ne;  // exclusive prefixes
+    if (k < F) {  // uniform: the full split k - first_n of this sequence
+        if (k >= first_n && k < first_n + n) {
+            s_piece[0] = tid;
+            s_piece[1] = k - first_n;
+        }
+    } else if (k < F + R) {  // uniform: the remainder of rank k - F
+        if (r > 0) {
+            int rank = 0;
+            for (int b = 0; b < B; ++b) {
+                const int rb = s_rem[b];
+                rank += (rb > r) | ((rb == r) & (b < tid));
+            }
+            if (rank == k - F) {
+                s_piece[0] = tid;
+                s_piece[1] = n;
+            }
+        }
+    } else {  // the empty split k - F - R - first_e past this sequence's keys
+        const int j = k - F - R;
+        if (j >= first_e && j < first_e + ne) {
+            s_piece[0] = tid;
+            s_piece[1] = e + (j - first_e);
+        }
+    }
+    __syncthreads();
+    UnitId u;
+    u.b = s_piece[0];
+    u.split = s_piece[1];
+    u.rb = sub % p.row_blocks;
+    u.h = sub / p.row_blocks;
+    u.unit = (u.b * p.num_kv_heads + u.h) * p.row_blocks + u.rb;
     return u;
 }
 

@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma_kernel(const PartialPar
     constexpr int kRowBytes = D * 2;  // one bf16 row of the LDS V tile
     constexpr int kLoads = FP8 ? kKs / 2 : kKs;  // 16-byte pieces of K (and of V) per lane and key
 
-    const UnitId wu = decode_unit(p);
+    const UnitId wu = p.lpt ? decode_unit_lpt<kThreads>(p) : decode_unit(p);
     const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     constexpr int kLoads = FP8 ? D / 64 : INT4 ? 1 : kKs;
     static_assert(!QUANT || D == 128, "a quantised cache has head dim 128");
 
-    const UnitId wu = decode_unit(p);
+    const UnitId wu = p.lpt ? decode_unit_lpt<kThreads>(p) : decode_unit(p);
     const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

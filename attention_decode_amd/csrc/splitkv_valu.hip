@@ -139,7 +139,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
                   "a step must stay inside one page / listed block (both are >= 16 keys)");
     static_assert(!kBf16 || INT4 || U % 2 == 0, "bf16 P.V pairs keys");
 
-    const UnitId wu = decode_unit(p);
+    const UnitId wu = p.lpt ? decode_unit_lpt<kThreads>(p) : decode_unit(p);
     const int split = wu.split, rb = wu.rb, h = wu.h, b = wu.b;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps step bases scalar

@@ -33,8 +33,8 @@
  *     cudaErrorNotSupported with a message for a configuration it has no kernel for).
  *     attn_decode_last_error() gives a message for the calling thread's last non-OK return.
  *   - Testing aids: the environment variables AD_NUM_SPLITS (split count, cf. xqa's
- *     XQA_NB_SUB_SEQ), AD_PARTIAL_KERNEL, AD_MFMA_TILE, AD_MFMA_ROWS and AD_FUSED_MERGE (kernel
- *     forms, named at the calls they affect) are read only while AD_TEST_KNOBS=1 is set; otherwise the
+ *     XQA_NB_SUB_SEQ), AD_PARTIAL_KERNEL, AD_MFMA_TILE, AD_MFMA_ROWS, AD_FUSED_MERGE and AD_LPT
+ *     (kernel forms and work-group placement, named at the calls they affect) are read only while AD_TEST_KNOBS=1 is set; otherwise the
  *     environment changes nothing.
  *   - Data contracts that are NOT checked (they live in device memory): seq_lens[b] <=
  *     kv_len_max and >= the sequence's query tokens; q_starts nondecreasing with counts of at
@@ -223,7 +223,11 @@ size_t attn_decode_workspace_size(const ad_decode_args *args, const ad_paged *pa
  * choice. Supported: head dims 64 and 128 (qk == v), fp32 or bf16, any G * q_len (bf16 with
  * more than 8 rows per KV head, every fp8 cache and an int4 cache of one coefficient group per row
  * run on the matrix cores, 16 or 32 rows per work unit; otherwise the vector ALUs take up to 8 rows
- * per work unit; attn_decode_kernel tells which).
+ * per work unit; attn_decode_kernel tells which). With per-sequence lengths (seq_lens, no block
+ * list, at most 256 sequences) on a grid of more work groups than compute units, the work groups
+ * take the (sequence, split) pieces longest first (full splits, then the remainders by length,
+ * then empty splits), the longest-processing-time order for identical machines; which group
+ * computes a piece changes, the values do not (AD_LPT=0/1 forces the order, testing aid).
  */
 int attn_decode_splitkv(const ad_decode_args *args, const ad_paged *paged, const ad_sparse *sparse,
                         int32_t num_splits, float *part_o, float *part_lse, void *stream);

@@ -11,7 +11,7 @@ if HERE not in sys.path:
     sys.path.insert(0, HERE)
 
 # The library's testing aids (AD_NUM_SPLITS, AD_PARTIAL_KERNEL, AD_MFMA_TILE, AD_MFMA_ROWS,
-# AD_FUSED_MERGE) are read only while this switch is set; the tests set them per case.
+# AD_FUSED_MERGE, AD_LPT) are read only while this switch is set; the tests set them per case.
 os.environ["AD_TEST_KNOBS"] = "1"
 
 
