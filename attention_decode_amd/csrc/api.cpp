@@ -247,12 +247,14 @@ int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
 // 191.8 us at 1664 keys (5 splits), 198.0 at 2048, 196.0 at 1366; the 32-row matrix-core kernel,
 // whose work group costs more to start and to combine, 224.3 us at 4096 keys (2 splits) against
 // 230.0 at 2048 with 1-8 draft tokens (32 rows per KV head). The 16-row matrix-core kernel, two
-// work groups per compute unit, on the fp8 cache: 131.8 us at 2048 keys (4 splits), 134.4 at 2731,
-// 137.6 at 4096. The vector kernel's shorter bound applies only to grids of several rounds at
-// 2048, where shorter splits even out the ragged tail; a grid of one round would spill into a
-// second (16 sequences of 4096 keys: 50 -> 56 us). Other paths (MLA) keep 2048.
+// work groups per compute unit, with longest-first placement: fp8 114.1 us at 2048 keys (4
+// splits), 113.3 at 1648, 114.5 at 2736; int4, whose keys are half as many bytes, 85.5 at 2048,
+// 81.9 at 2736, 95.2 at 4096. The vector kernel's shorter bound applies only to grids of several
+// rounds at 2048, where shorter splits even out the ragged tail; a grid of one round would spill
+// into a second (16 sequences of 4096 keys: 50 -> 56 us). Other paths (MLA) keep 2048.
 constexpr int64_t kRaggedChunkVector = 1664;
 constexpr int64_t kRaggedChunkMatrix = 4096;
+constexpr int64_t kRaggedChunkInt4 = 3072;
 constexpr int64_t kRaggedChunk = 2048;
 
 int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
@@ -284,7 +286,7 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
                 if (rows.mfma && !rows.tile16)
                     most = kRaggedChunkMatrix;
                 else if (rows.mfma)
-                    most = kRaggedChunk;
+                    most = a->kv_format == AD_KV_INT4 ? kRaggedChunkInt4 : kRaggedChunk;
                 else if (units * std::max<int64_t>(S, cdiv(span, kRaggedChunk)) >= 2 * (int64_t)cus)
                     most = kRaggedChunkVector;
             }

@@ -188,7 +188,8 @@ typedef struct ad_sparse {
  * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
  * bounds the split length, so that no work group is much longer than the average: 2048 keys,
  * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
- * the 32-row matrix-core kernel (whose work groups cost more to start and finish). A split of a
+ * the 32-row matrix-core kernel (whose work groups cost more to start and finish), 3072 for an
+ * int4 cache on the 16-row kernel (its keys are the fewest bytes). A split of a
  * paged cache or a block list never covers more than 1038 pages or blocks (258 pages for MLA:
  * the ids it stages), which raises the count for very long caches of small pages. AD_NUM_SPLITS
  * forces the count (testing aid, see the conventions above).
