@@ -247,15 +247,22 @@ int64_t key_span(const ad_decode_args *a, const ad_sparse *sp) {
 // 191.8 us at 1664 keys (5 splits), 198.0 at 2048, 196.0 at 1366; the 32-row matrix-core kernel,
 // whose work group costs more to start and to combine, 224.3 us at 4096 keys (2 splits) against
 // 230.0 at 2048 with 1-8 draft tokens (32 rows per KV head). The 16-row matrix-core kernel, two
-// work groups per compute unit, with longest-first placement: fp8 114.1 us at 2048 keys (4
-// splits), 113.3 at 1648, 114.5 at 2736; int4, whose keys are half as many bytes, 85.5 at 2048,
-// 81.9 at 2736, 95.2 at 4096. The vector kernel's shorter bound applies only to grids of several
-// rounds at 2048, where shorter splits even out the ragged tail; a grid of one round would spill
-// into a second (16 sequences of 4096 keys: 50 -> 56 us). Other paths (MLA) keep 2048.
+// work groups per compute unit, with longest-first placement: fp8 with whole-row loads 109.1 us
+// at 2048 keys (4 splits), 105.8 at 2736, 121.8 at 4096 (with half-row loads 114.1 at 2048, 113.3
+// at 1648, 114.5 at 2736); int4, whose keys are half as many bytes, 85.5 at 2048, 81.9 at 2736,
+// 95.2 at 4096. The vector kernel's shorter bound applies only to grids of several rounds at
+// 2048, where shorter splits even out the ragged tail; a grid of one round would spill into a
+// second (16 sequences of 4096 keys: 50 -> 56 us). Other paths (MLA) keep 2048.
 constexpr int64_t kRaggedChunkVector = 1664;
 constexpr int64_t kRaggedChunkMatrix = 4096;
-constexpr int64_t kRaggedChunkInt4 = 3072;
+constexpr int64_t kRaggedChunkQuant = 3072;
 constexpr int64_t kRaggedChunk = 2048;
+
+// fp8 caches on the 16-row kernel: each load reads whole 128-byte rows and K reaches the matrix
+// cores through LDS (109.1 us against 114.1 on the ragged fp8 workload above, both at 2048 keys),
+// or each reads half rows of 16 keys straight into the operand registers. AD_MFMA_ROWS=0/1 forces
+// either (testing aid).
+bool fp8_whole_rows() { return knob("AD_MFMA_ROWS") ? knob_int("AD_MFMA_ROWS") != 0 : true; }
 
 int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp, Path path, int requested,
                 Plan *out) {
@@ -286,7 +293,9 @@ int plan_splits(const ad_decode_args *a, const ad_paged *pg, const ad_sparse *sp
                 if (rows.mfma && !rows.tile16)
                     most = kRaggedChunkMatrix;
                 else if (rows.mfma)
-                    most = a->kv_format == AD_KV_INT4 ? kRaggedChunkInt4 : kRaggedChunk;
+                    most = a->kv_format == AD_KV_INT4 || (a->kv_format == AD_KV_FP8_E4M3 && fp8_whole_rows())
+                               ? kRaggedChunkQuant
+                               : kRaggedChunk;
                 else if (units * std::max<int64_t>(S, cdiv(span, kRaggedChunk)) >= 2 * (int64_t)cus)
                     most = kRaggedChunkVector;
             }
@@ -376,7 +385,10 @@ hipError_t launch_partial(const ad_decode_args *a, ad::PartialParams &p, int mod
         if (device_cus(&cus) != AD_OK) return hipErrorInvalidDevice;
         p.lpt = lpt_ok && groups > cus;
     }
-    if (rows.mfma && rows.tile16) return ad::launch_partial_mfma16(p, a->head_dim_qk, mode, stream);
+    if (rows.mfma && rows.tile16) {
+        p.mfma_rows = a->kv_format == AD_KV_FP8_E4M3 && fp8_whole_rows();
+        return ad::launch_partial_mfma16(p, a->head_dim_qk, mode, stream);
+    }
     if (rows.mfma && a->kv_format == AD_KV_SAME) {
         // Whole-row loads staged through LDS (bf16 caches): every load reads whole lines once, at
         // the price of a round trip through LDS per tile. That pays when a compute unit runs

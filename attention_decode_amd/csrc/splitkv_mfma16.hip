@@ -60,6 +60,12 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    0, 0, 0);
 }
 
+// 16-byte LDS store and load.
+__device__ __forceinline__ void st_lds16(lds_u8 *at, u32x4 x) { *(__attribute__((address_space(3))) u32x4 *)at = x; }
+__device__ __forceinline__ u32x4 ld_lds16(const lds_u8 *at) {
+    return *(const __attribute__((address_space(3))) u32x4 *)at;
+}
+
 // All four lanes l, l^16, l^32, l^48 get the max / sum of their four values.
 __device__ __forceinline__ float quad_max(float x) { return pair_max(pair16_max(x)); }
 __device__ __forceinline__ float quad_sum(float x) { return pair_sum(pair16_sum(x)); }
@@ -91,9 +97,13 @@ __device__ __forceinline__ void int4_coef(uint32_t cw, float &scale, float &shif
 // one fp16 scale / shift pair (kQfInt4).
 enum { kQfBf16 = 0, kQfFp8 = 1, kQfInt4 = 2 };
 
-template <int D, int MODE, int QF>
+// ROWS (fp8): each load instruction reads whole 128-byte rows (lane l: byte piece l%8 of key
+// l/8 of an 8-key group) instead of half rows of 16 keys, and K goes through a per-wave LDS tile
+// to the matrix operand; see the load forms below.
+template <int D, int MODE, int QF, bool ROWS>
 __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialParams p) {
     constexpr bool FP8 = QF == kQfFp8, INT4 = QF == kQfInt4, QUANT = FP8 || INT4;
+    static_assert(!ROWS || FP8, "the whole-row form is built for fp8 caches");
     constexpr int kKs = D / 32;                   // k-steps of the score product
     constexpr int kCols = D / 16;                 // 16-column blocks of the output
     constexpr int kRowBytes = D * 2;              // one bf16 row of the LDS V tile
@@ -153,6 +163,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     __shared__ __attribute__((aligned(16))) float s_ks[kQW][kTile], s_vs[kQW][kTile], s_vr[kQW][kTile];
     __shared__ __attribute__((aligned(16))) float s_kz[kIW][kTile], s_vz[kIW][kTile];
     __shared__ float s_corr[kIW][kRows];  // int4: the shifts' share of each wave's rows
+    // ROWS: the wave's K tile as loaded (32 keys x 128 bytes), piece c of key k at c ^ (k % 8)
+    __shared__ __attribute__((aligned(16))) unsigned char s_kt[ROWS ? kWaves : 1][ROWS ? kTile * 128 : 16];
 
     const int map_shift = MODE == KV_PAGED ? p.page_shift : p.block_shift;
     const int map_first = (MODE == KV_CONTIG) ? 0 : (t0 >> map_shift);
@@ -247,21 +259,25 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
 
     // Lane l loads key 16 kb + l%16 of the tile for kb = 0, 1: bf16 pieces at elements 32 ks +
     // 8 (l/16), fp8 pieces at bytes 64 j + 16 (l/16), int4 words 1 + 4 (l/16) .. + 3 (after the
-    // coefficient word) and the coefficient word.
+    // coefficient word) and the coefficient word. ROWS: lane l loads bytes 16 (l%8) .. + 15 of
+    // keys 16 kb + 8 jr + l/8 for jr = 0, 1 (8 lanes read a whole row in one instruction).
+    constexpr int kR = ROWS ? 2 : 1;  // keys per lane and 16-key block
     struct Buf {
         u32x4 k[2][kLoads];
         u32x4 v[2][kLoads];
-        float ks[2], vs[2];  // fp8: this lane's key scales as loaded (any value for a key that is not read)
+        float ks[2][kR], vs[2][kR];  // fp8: the keys' scales as loaded (any value for a key that is not read)
         uint32_t kc[2], vc[2];  // int4: the coefficient words
-        bool live[2];        // quantised: this lane's key is read
+        bool live[2][kR];      // quantised: the lane's key is read
         int base;
     };
     auto fetch = [&](Buf &f, int base) {
         f.base = base;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int jr = 0; jr < kR; ++jr) {
             const int vb = base + 16 * kb;  // uniform
-            const int v = vb + c16;
+            const int v = vb + (ROWS ? 8 * jr + (lane >> 3) : c16);
             const KV *kp = safe, *vp = safe;
             const float *ksp = p.k_scale, *vsp = p.v_scale;  // the arrays' first scales: always readable
             if (v < t1) {
@@ -294,7 +310,13 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                 f.v[kb][0] = u32x4{vw[0], vw[1], vw[2], vw[3]};
                 f.kc[kb] = kp[0];
                 f.vc[kb] = vp[0];
-                f.live[kb] = kp != safe;
+                f.live[kb][0] = kp != safe;
+            } else if constexpr (ROWS) {
+                f.k[kb][jr] = ld16_stream(kp + 16 * (lane & 7));
+                f.v[kb][jr] = ld16_stream(vp + 16 * (lane & 7));
+                f.ks[kb][jr] = *ksp;
+                f.vs[kb][jr] = *vsp;
+                f.live[kb][jr] = kp != safe;
             } else if constexpr (FP8) {
 #pragma unroll
                 for (int j = 0; j < kLoads; ++j)
@@ -303,9 +325,9 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                 for (int j = 0; j < kLoads; ++j)
                     f.v[kb][j] = j == kLoads - 1 ? ld16_last(vp + 64 * j + 16 * grp) : ld16(vp + 64 * j + 16 * grp);
                 // used only once this buffer is current (a select here would wait for the prefetch)
-                f.ks[kb] = *ksp;
-                f.vs[kb] = *vsp;
-                f.live[kb] = kp != safe;
+                f.ks[kb][0] = *ksp;
+                f.vs[kb][0] = *vsp;
+                f.live[kb][0] = kp != safe;
             } else {
 #pragma unroll
                 for (int ks = 0; ks < kKs; ++ks) f.k[kb][ks] = ld16(kp + 32 * ks + 8 * grp);
@@ -316,6 +338,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     };
 
     lds_u8 *vw = (lds_u8 *)s_buf + wave * kTile * kRowBytes;  // this wave's V tile
+    lds_u8 *kt = (lds_u8 *)s_kt[ROWS ? wave : 0];                 // and its K tile (ROWS)
     // Transposing-read address of this lane for read rd and output block c: row 16 rd + 4 grp +
     // (lane&15)/4, chunk 2c + (lane&3)/2, half-chunk lane&1.
     const int tr_row = 4 * grp + (c16 >> 2);
@@ -329,49 +352,73 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     for (int c = 0; c < kCols; ++c) o[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](const Buf &cur, bool full) {
-        // V tile -> LDS: row 16 kb + c16; bf16 chunk 4 ks + grp; fp8 piece j as chunks 8 j + 2 grp (+1)
+        if constexpr (ROWS) {  // K as loaded and V converted to bf16 -> LDS: row 16 kb + 8 jr + lane / 8
+            const int pc = lane & 7;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int row = 16 * kb + c16;
-            lds_u8 *vr = vw + row * kRowBytes;
-            if constexpr (INT4) {  // word j of the lane's 4 as chunk 4 grp + j (fields in int4_x8 order)
-                const u32x4 w = cur.v[kb][0];
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * grp + j) ^ swz<D>(row)) << 4)) =
-                        int4_x8(w[j]);
-                if (grp == 0) {  // a key that is not read takes scales and shifts 0
-                    const bool live = cur.live[kb];
-                    float ksc, ksh, vsc, vsh;
-                    int4_coef(cur.kc[kb], ksc, ksh);
-                    int4_coef(cur.vc[kb], vsc, vsh);
-                    s_ks[wave][row] = live ? ksc : 0.f;
-                    s_kz[wave][row] = live ? fmaf(-128.f, ksc, ksh) : 0.f;
-                    s_vs[wave][row] = live ? vsc : 0.f;
-                    s_vr[wave][row] = live && vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
-                    s_vz[wave][row] = live ? vsh : 0.f;
+                for (int jr = 0; jr < kR; ++jr) {
+                    const int row = 16 * kb + 8 * jr + (lane >> 3);
+                    const bool live = cur.live[kb][jr];
+                    st_lds16(kt + row * 128 + ((pc ^ (row & 7)) << 4), cur.k[kb][jr]);
+                    u32x4 w = cur.v[kb][jr];
+                    if (!full && !live) w = u32x4{0, 0, 0, 0};  // a key that is not read may hold NaN codes
+                    lds_u8 *vr = vw + row * kRowBytes;
+                    st_lds16(vr + (((2 * pc) ^ swz<D>(row)) << 4), e4m3_x8(w[0], w[1]));
+                    st_lds16(vr + (((2 * pc + 1) ^ swz<D>(row)) << 4), e4m3_x8(w[2], w[3]));
+                    if (pc == 0) {  // a key that is not read takes scale 0
+                        const float vsv = live ? cur.vs[kb][jr] : 0.f;
+                        s_ks[wave][row] = live ? cur.ks[kb][jr] : 0.f;
+                        s_vs[wave][row] = vsv;
+                        s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
+                    }
                 }
-            } else if constexpr (FP8) {
+        }
+        // Other forms: V tile -> LDS, row 16 kb + c16; bf16 chunk 4 ks + grp; fp8 piece j as chunks
+        // 8 j + 2 grp (+1)
+        if constexpr (!ROWS) {
 #pragma unroll
-                for (int j = 0; j < kLoads; ++j) {
-                    u32x4 w = cur.v[kb][j];
-                    if (!full && !cur.live[kb]) w = u32x4{0, 0, 0, 0};  // a key that is not read may hold NaN codes
-                    const int c0 = 8 * j + 2 * grp;
-                    *(__attribute__((address_space(3))) u32x4 *)(vr + ((c0 ^ swz<D>(row)) << 4)) = e4m3_x8(w[0], w[1]);
-                    *(__attribute__((address_space(3))) u32x4 *)(vr + (((c0 + 1) ^ swz<D>(row)) << 4)) =
-                        e4m3_x8(w[2], w[3]);
-                }
-                if (grp == 0) {  // a key that is not read takes scale 0
-                    const float vsv = cur.live[kb] ? cur.vs[kb] : 0.f;
-                    s_ks[wave][row] = cur.live[kb] ? cur.ks[kb] : 0.f;
-                    s_vs[wave][row] = vsv;
-                    s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
-                }
-            } else {
+            for (int kb = 0; kb < 2; ++kb) {
+                const int row = 16 * kb + c16;
+                lds_u8 *vr = vw + row * kRowBytes;
+                if constexpr (INT4) {  // word j of the lane's 4 as chunk 4 grp + j (fields in int4_x8 order)
+                    const u32x4 w = cur.v[kb][0];
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks)
-                    *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * ks + grp) ^ swz<D>(row)) << 4)) =
-                        cur.v[kb][ks];
+                    for (int j = 0; j < 4; ++j)
+                        *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * grp + j) ^ swz<D>(row)) << 4)) =
+                            int4_x8(w[j]);
+                    if (grp == 0) {  // a key that is not read takes scales and shifts 0
+                        const bool live = cur.live[kb][0];
+                        float ksc, ksh, vsc, vsh;
+                        int4_coef(cur.kc[kb], ksc, ksh);
+                        int4_coef(cur.vc[kb], vsc, vsh);
+                        s_ks[wave][row] = live ? ksc : 0.f;
+                        s_kz[wave][row] = live ? fmaf(-128.f, ksc, ksh) : 0.f;
+                        s_vs[wave][row] = live ? vsc : 0.f;
+                        s_vr[wave][row] = live && vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
+                        s_vz[wave][row] = live ? vsh : 0.f;
+                    }
+                } else if constexpr (FP8) {
+#pragma unroll
+                    for (int j = 0; j < kLoads; ++j) {
+                        u32x4 w = cur.v[kb][j];
+                        if (!full && !cur.live[kb][0]) w = u32x4{0, 0, 0, 0};  // a key not read may hold NaN codes
+                        const int c0 = 8 * j + 2 * grp;
+                        st_lds16(vr + ((c0 ^ swz<D>(row)) << 4), e4m3_x8(w[0], w[1]));
+                        st_lds16(vr + (((c0 + 1) ^ swz<D>(row)) << 4), e4m3_x8(w[2], w[3]));
+                    }
+                    if (grp == 0) {  // a key that is not read takes scale 0
+                        const float vsv = cur.live[kb][0] ? cur.vs[kb][0] : 0.f;
+                        s_ks[wave][row] = cur.live[kb][0] ? cur.ks[kb][0] : 0.f;
+                        s_vs[wave][row] = vsv;
+                        s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
+                    }
+                } else {
+#pragma unroll
+                    for (int ks = 0; ks < kKs; ++ks)
+                        *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * ks + grp) ^ swz<D>(row)) << 4)) =
+                            cur.v[kb][ks];
+                }
             }
         }
         // S^T = K Q^T, one 16-key block at a time
@@ -385,7 +432,9 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
             } else if constexpr (FP8) {
 #pragma unroll
                 for (int j = 0; j < kLoads; ++j) {
-                    const u32x4 w = cur.k[kb][j];
+                    // ROWS: bytes 64 j + 16 grp of key 16 kb + c16 from the LDS tile
+                    const int key = 16 * kb + c16;
+                    const u32x4 w = ROWS ? ld_lds16(kt + key * 128 + (((4 * j + grp) ^ (key & 7)) << 4)) : cur.k[kb][j];
                     sc[kb] = mfma16(e4m3_x8(w[0], w[1]), qb[2 * j], sc[kb]);
                     sc[kb] = mfma16(e4m3_x8(w[2], w[3]), qb[2 * j + 1], sc[kb]);
                 }
@@ -580,18 +629,18 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     }
 }
 
-template <int D, int QF>
+template <int D, int QF, bool ROWS = false>
 hipError_t by_mode(const PartialParams &p, int mode, hipStream_t s) {
     const dim3 grid(p.num_splits * p.batch * p.num_kv_heads * p.row_blocks);  // see decode_unit
     switch (mode) {
         case KV_CONTIG:
-            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_CONTIG, QF>), grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_CONTIG, QF, ROWS>), grid, dim3(kThreads), 0, s, p);
             break;
         case KV_PAGED:
-            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_PAGED, QF>), grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_PAGED, QF, ROWS>), grid, dim3(kThreads), 0, s, p);
             break;
         default:
-            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_SPARSE, QF>), grid, dim3(kThreads), 0, s, p);
+            hipLaunchKernelGGL((partial_mfma16_kernel<D, KV_SPARSE, QF, ROWS>), grid, dim3(kThreads), 0, s, p);
             break;
     }
     return hipGetLastError();
@@ -607,7 +656,7 @@ hipError_t launch_partial_mfma16(const PartialParams &p, int head_dim, int mode,
     }
     if (p.kv_fp8) {
         if (head_dim != 128) return hipErrorInvalidValue;
-        return by_mode<128, kQfFp8>(p, mode, stream);
+        return p.mfma_rows ? by_mode<128, kQfFp8, true>(p, mode, stream) : by_mode<128, kQfFp8>(p, mode, stream);
     }
     return head_dim == 64 ? by_mode<64, kQfBf16>(p, mode, stream) : by_mode<128, kQfBf16>(p, mode, stream);
 }

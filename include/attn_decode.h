@@ -188,8 +188,8 @@ typedef struct ad_sparse {
  * tiles per sequence)); with per-sequence lengths (seq_lens != NULL, possibly ragged) it also
  * bounds the split length, so that no work group is much longer than the average: 2048 keys,
  * 1664 on the vector kernel when that grid already takes several rounds of work groups, 4096 on
- * the 32-row matrix-core kernel (whose work groups cost more to start and finish), 3072 for an
- * int4 cache on the 16-row kernel (its keys are the fewest bytes). A split of a
+ * the 32-row matrix-core kernel (whose work groups cost more to start and finish), 3072 for
+ * fp8 and int4 caches on the 16-row kernel (keys of fewer bytes, read as whole rows). A split of a
  * paged cache or a block list never covers more than 1038 pages or blocks (258 pages for MLA:
  * the ids it stages), which raises the count for very long caches of small pages. AD_NUM_SPLITS
  * forces the count (testing aid, see the conventions above).
@@ -307,7 +307,9 @@ int attn_decode_launches(const ad_decode_args *args, const ad_paged *paged, cons
  * Checks the arguments as the calls do (out is not needed). On a bf16 cache the 32-row kernel
  * reads whole K / V rows and stages K through LDS when the grid holds more work groups than
  * compute units, else K goes from HBM straight to the matrix cores; both give the same bits, and
- * AD_MFMA_ROWS=0 / 1 forces either (testing aid). */
+ * AD_MFMA_ROWS=0 / 1 forces either (testing aid). On an fp8 cache the 16-row kernel reads whole
+ * rows and stages K through LDS unless AD_MFMA_ROWS=0 asks for half rows of 16 keys straight into
+ * the operand registers (same bits again). */
 #define AD_KERNEL_VECTOR 0
 #define AD_KERNEL_MATRIX 1
 #define AD_KERNEL_MLA 2

@@ -12,9 +12,10 @@ from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
 
-# the matrix-core kernel in its 16-row and 32-row units (AD_MFMA_TILE), and the vector form
+# the matrix-core kernel in its 16-row units (operands straight from the loads, and whole-row
+# loads with K through LDS: AD_MFMA_ROWS) and 32-row units (AD_MFMA_TILE), and the vector form
 # (AD_PARTIAL_KERNEL=valu)
-KERNELS = ["mfma16", "mfma32", "valu"]
+KERNELS = ["mfma16", "mfma16rows", "mfma32", "valu"]
 
 
 def force(monkeypatch, kernel):
@@ -22,7 +23,8 @@ def force(monkeypatch, kernel):
         monkeypatch.setenv("AD_PARTIAL_KERNEL", "valu")
     else:
         monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
-        monkeypatch.setenv("AD_MFMA_TILE", kernel[4:])
+        monkeypatch.setenv("AD_MFMA_TILE", kernel[4:6])
+        monkeypatch.setenv("AD_MFMA_ROWS", "1" if kernel.endswith("rows") else "0")
 
 
 def run(w, num_splits=None, fused=True):
@@ -32,11 +34,12 @@ def run(w, num_splits=None, fused=True):
     return out.cpu(), lse.cpu(), step
 
 
-@pytest.mark.parametrize("tile", ["default", "32"])
+@pytest.mark.parametrize("tile", ["default", "16rows", "16regs", "32"])
 def test_workload6_full(orc, monkeypatch, tile):
-    """The planner's choice (16-row units) and the 32-row units, every row."""
+    """The planner's choice, both load forms of the 16-row units, and the 32-row units, every row."""
     if tile != "default":
-        monkeypatch.setenv("AD_MFMA_TILE", tile)
+        monkeypatch.setenv("AD_MFMA_TILE", tile[:2])
+        monkeypatch.setenv("AD_MFMA_ROWS", "1" if tile == "16rows" else "0")
     say(f"[gpu] workload 6 (fp8 paged ragged): full size, every row, tile {tile}")
     w = inputs.make(6)
     out, lse, step = run(w)

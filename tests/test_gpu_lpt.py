@@ -68,11 +68,12 @@ def test_placement_changes_nothing(orc, monkeypatch, kernel, kind, S):
         assert_matches(o1, l1, ref_o, ref_l, w.dtype, f"fused={fused}")
 
 
-@pytest.mark.parametrize("kernel", ["valu", "mfma16"])
+@pytest.mark.parametrize("kernel", ["valu", "mfma16", "mfma16rows"])
 def test_placement_fp8_int4_and_drafts(orc, monkeypatch, kernel):
     """Quantised caches and packed draft tokens with tree masks, placement forced on and off."""
-    monkeypatch.setenv("AD_PARTIAL_KERNEL", KERNELS[kernel][0])
-    monkeypatch.setenv("AD_MFMA_TILE", KERNELS[kernel][1])
+    monkeypatch.setenv("AD_PARTIAL_KERNEL", KERNELS[kernel[:6]][0])
+    monkeypatch.setenv("AD_MFMA_TILE", KERNELS[kernel[:6]][1])
+    monkeypatch.setenv("AD_MFMA_ROWS", "1" if kernel.endswith("rows") else "0")
     lens = [300, 45, 0, 129, 1024, 1, 640]
     for fmt in ("fp8", "int4"):
         say(f"[gpu] placement {kernel} {fmt}")
