@@ -71,10 +71,21 @@ __device__ __forceinline__ float quad_max(float x) { return pair_max(pair16_max(
 __device__ __forceinline__ float quad_sum(float x) { return pair_sum(pair16_sum(x)); }
 
 // 8 int4 fields of a word as bf16 values 128 + f, in the order fields 0, 4, 1, 5, 2, 6, 3, 7 (each
-// pair (j, j + 4) is one mask and one OR: exact, since 128 + f needs 8 significant bits).
-__device__ __forceinline__ u32x4 int4_x8(uint32_t w) {
-    return u32x4{(w & 0x000F000Fu) | 0x43004300u, ((w >> 4) & 0x000F000Fu) | 0x43004300u,
-                 ((w >> 8) & 0x000F000Fu) | 0x43004300u, ((w >> 12) & 0x000F000Fu) | 0x43004300u};
+// pair (j, j + 4) is the word shifted by 4 j, masked with 0x000F000F and ORed with the exponent
+// pattern 0x43004300: exact, since 128 + f needs 8 significant bits). mask and bits hold those
+// two constants in registers (Int4Consts): a three-operand instruction on this architecture takes
+// no literal, so only then does the mask and the OR become one v_and_or_b32.
+struct Int4Consts {
+    uint32_t mask, bits;
+};
+__device__ __forceinline__ Int4Consts int4_consts() {
+    Int4Consts k{0x000F000Fu, 0x43004300u};
+    asm volatile("" : "+v"(k.mask), "+v"(k.bits));  // keep them in registers, opaque to folding
+    return k;
+}
+__device__ __forceinline__ u32x4 int4_x8(uint32_t w, Int4Consts k) {
+    return u32x4{(w & k.mask) | k.bits, ((w >> 4) & k.mask) | k.bits, ((w >> 8) & k.mask) | k.bits,
+                 ((w >> 12) & k.mask) | k.bits};
 }
 // The query's 8 bf16 values of the same 8 dimensions (a 16-byte load q), in that order.
 __device__ __forceinline__ u32x4 int4_order(u32x4 q) {
@@ -156,10 +167,15 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     __shared__ __attribute__((aligned(16))) float s_alpha[kWaves][kRows];
     __shared__ float s_m[kWaves][kRows], s_l[kWaves][kRows], s_lf[kWaves][kRows];
     __shared__ float s_fw[kWaves][kRows], s_inv[kRows];  // combine weights of the waves' partials, 1 / l
-    // Quantised cache: per wave and tile key, the key scale, the value scale and its reciprocal
-    // (int4: and the key's shift - 128 scale, the value's shift), 0 for a key that is not read, read
-    // back in the score accumulator's key order
+    // Quantised cache: per wave and tile key, the key scale times scale * log2(e) (the scores'
+    // base-2 units), the value scale and its reciprocal (int4: and the key's (shift - 128 scale)
+    // times scale * log2(e), the value's shift), 0 for a key that is not read, read back in the
+    // score accumulator's key order
     constexpr int kQW = QUANT ? kWaves : 1, kIW = INT4 ? kWaves : 1;
+    const Int4Consts i4k = [] {
+        if constexpr (INT4) return int4_consts();
+        else return Int4Consts{0u, 0u};
+    }();
     __shared__ __attribute__((aligned(16))) float s_ks[kQW][kTile], s_vs[kQW][kTile], s_vr[kQW][kTile];
     __shared__ __attribute__((aligned(16))) float s_kz[kIW][kTile], s_vz[kIW][kTile];
     __shared__ float s_corr[kIW][kRows];  // int4: the shifts' share of each wave's rows
@@ -368,7 +384,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                     st_lds16(vr + (((2 * pc + 1) ^ swz<D>(row)) << 4), e4m3_x8(w[2], w[3]));
                     if (pc == 0) {  // a key that is not read takes scale 0
                         const float vsv = live ? cur.vs[kb][jr] : 0.f;
-                        s_ks[wave][row] = live ? cur.ks[kb][jr] : 0.f;
+                        s_ks[wave][row] = live ? cur.ks[kb][jr] * p.scale_log2 : 0.f;
                         s_vs[wave][row] = vsv;
                         s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
                     }
@@ -386,14 +402,14 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
                         *(__attribute__((address_space(3))) u32x4 *)(vr + (((4 * grp + j) ^ swz<D>(row)) << 4)) =
-                            int4_x8(w[j]);
+                            int4_x8(w[j], i4k);
                     if (grp == 0) {  // a key that is not read takes scales and shifts 0
                         const bool live = cur.live[kb][0];
                         float ksc, ksh, vsc, vsh;
                         int4_coef(cur.kc[kb], ksc, ksh);
                         int4_coef(cur.vc[kb], vsc, vsh);
-                        s_ks[wave][row] = live ? ksc : 0.f;
-                        s_kz[wave][row] = live ? fmaf(-128.f, ksc, ksh) : 0.f;
+                        s_ks[wave][row] = live ? ksc * p.scale_log2 : 0.f;
+                        s_kz[wave][row] = live ? fmaf(-128.f, ksc, ksh) * p.scale_log2 : 0.f;
                         s_vs[wave][row] = live ? vsc : 0.f;
                         s_vr[wave][row] = live && vsc != 0.f ? __builtin_amdgcn_rcpf(vsc) : 0.f;
                         s_vz[wave][row] = live ? vsh : 0.f;
@@ -409,7 +425,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                     }
                     if (grp == 0) {  // a key that is not read takes scale 0
                         const float vsv = cur.live[kb][0] ? cur.vs[kb][0] : 0.f;
-                        s_ks[wave][row] = cur.live[kb][0] ? cur.ks[kb][0] : 0.f;
+                        s_ks[wave][row] = cur.live[kb][0] ? cur.ks[kb][0] * p.scale_log2 : 0.f;
                         s_vs[wave][row] = vsv;
                         s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
                     }
@@ -428,7 +444,7 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
             sc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
             if constexpr (INT4) {
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) sc[kb] = mfma16(int4_x8(cur.k[kb][0][ks]), qb[ks], sc[kb]);
+                for (int ks = 0; ks < kKs; ++ks) sc[kb] = mfma16(int4_x8(cur.k[kb][0][ks], i4k), qb[ks], sc[kb]);
             } else if constexpr (FP8) {
 #pragma unroll
                 for (int j = 0; j < kLoads; ++j) {
@@ -455,13 +471,13 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                 vr4[kb] = *(const f32x4 *)&s_vr[wave][16 * kb + 4 * grp];
                 vz4[kb] = *(const f32x4 *)&s_vz[wave][16 * kb + 4 * grp];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[kb][e] = fmaf(sc[kb][e], k4[e], z4[e] * qsum) * p.scale_log2;
+                for (int e = 0; e < 4; ++e) sv[kb][e] = fmaf(sc[kb][e], k4[e], z4[e] * qsum);
             } else if constexpr (FP8) {
                 const f32x4 k4 = *(const f32x4 *)&s_ks[wave][16 * kb + 4 * grp];
                 vs4[kb] = *(const f32x4 *)&s_vs[wave][16 * kb + 4 * grp];
                 vr4[kb] = *(const f32x4 *)&s_vr[wave][16 * kb + 4 * grp];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sv[kb][e] = sc[kb][e] * (p.scale_log2 * k4[e]);
+                for (int e = 0; e < 4; ++e) sv[kb][e] = sc[kb][e] * k4[e];
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sv[kb][e] = sc[kb][e] * p.scale_log2;
