@@ -195,6 +195,20 @@ __device__ __forceinline__ UnitId decode_unit_lpt(const PartialParams &p) {
     return u;
 }
 
+// An int4 cache's fields become bf16 pairs 128 + f as ((word >> 4 j) & mask) | bits, with mask
+// 0x000F000F (fields j and j + 4 of the word) and bits 0x43004300 (the exponent of 128 in each
+// half). A three-operand instruction takes no literal on this architecture, so with the two
+// constants as literals the compiler splits each mask-and-OR in two; held in registers they make
+// one v_and_or_b32. The empty asm keeps them in registers, out of reach of constant folding.
+struct Int4Consts {
+    uint32_t mask, bits;
+};
+__device__ __forceinline__ Int4Consts int4_consts() {
+    Int4Consts k{0x000F000Fu, 0x43004300u};
+    asm volatile("" : "+v"(k.mask), "+v"(k.bits));
+    return k;
+}
+
 // Query tokens of sequence b and the packed row of its token 0: q_len tokens at row b * q_len, or
 // with q_starts the count q_starts[b+1] - q_starts[b] clamped to [0, q_len] (so that the padded
 // partial rows stay in bounds) at row q_starts[b].

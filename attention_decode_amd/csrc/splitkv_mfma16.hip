@@ -71,18 +71,8 @@ __device__ __forceinline__ float quad_max(float x) { return pair_max(pair16_max(
 __device__ __forceinline__ float quad_sum(float x) { return pair_sum(pair16_sum(x)); }
 
 // 8 int4 fields of a word as bf16 values 128 + f, in the order fields 0, 4, 1, 5, 2, 6, 3, 7 (each
-// pair (j, j + 4) is the word shifted by 4 j, masked with 0x000F000F and ORed with the exponent
-// pattern 0x43004300: exact, since 128 + f needs 8 significant bits). mask and bits hold those
-// two constants in registers (Int4Consts): a three-operand instruction on this architecture takes
-// no literal, so only then does the mask and the OR become one v_and_or_b32.
-struct Int4Consts {
-    uint32_t mask, bits;
-};
-__device__ __forceinline__ Int4Consts int4_consts() {
-    Int4Consts k{0x000F000Fu, 0x43004300u};
-    asm volatile("" : "+v"(k.mask), "+v"(k.bits));  // keep them in registers, opaque to folding
-    return k;
-}
+// pair (j, j + 4) is the word shifted by 4 j, masked and ORed with the exponent pattern, one
+// v_and_or_b32 with Int4Consts: exact, since 128 + f needs 8 significant bits).
 __device__ __forceinline__ u32x4 int4_x8(uint32_t w, Int4Consts k) {
     return u32x4{(w & k.mask) | k.bits, ((w >> 4) & k.mask) | k.bits, ((w >> 8) & k.mask) | k.bits,
                  ((w >> 12) & k.mask) | k.bits};

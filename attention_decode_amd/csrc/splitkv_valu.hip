@@ -275,6 +275,11 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
                 for (int j = 0; j < 4; ++j) qf[r][i * 4 + j] = as_f32(qv[r][i][j]) * p.scale_log2;
     }
 
+    const Int4Consts i4k = [] {
+        if constexpr (INT4) return int4_consts();
+        else return Int4Consts{0u, 0u};
+    }();
+
     // ---- key addressing
     const KV *kbase = static_cast<const KV *>(p.k) + (int64_t)h * p.k_s[2];
     const KV *vbase = static_cast<const KV *>(p.v) + (int64_t)h * p.v_s[2];
@@ -399,7 +404,7 @@ __device__ __forceinline__ void partial_valu_body(const PartialParams &p) {
                 for (int w = 0; w < kIW; ++w)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        kf[4 * w + j] = as_bf16x2(((cur.k[u][0][w] >> (4 * j)) & 0x000F000Fu) | 0x43004300u);
+                        kf[4 * w + j] = as_bf16x2(((cur.k[u][0][w] >> (4 * j)) & i4k.mask) | i4k.bits);
                 float sh;
                 int4_coef(cur.k[u][0][2], ksc, sh);
                 koff = fmaf(-128.f, ksc, sh);
