@@ -271,74 +271,137 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
     struct Buf {
         u32x4 k[2][kLoads];
         u32x4 v[2][kLoads];
-        float ks[2][kR], vs[2][kR];  // fp8: the keys' scales as loaded (any value for a key that is not read)
+        float ks[2], vs[2];  // fp8: the scales of key l % 16 as loaded (any value for a key that is not read)
+        bool slive[2];       // fp8: that key is read
         uint32_t kc[2], vc[2];  // int4: the coefficient words
         bool live[2][kR];      // quantised: the lane's key is read
         int base;
     };
+    // ROWS: a block wholly inside the split and the unit's visible range lies in one page or one
+    // listed block (both at least 16 keys, aligned): one lookup and one row address for the wave,
+    // and each lane's row i of the block at i times the row stride from it, one 32 x 32 -> 64-bit
+    // multiply-add (strides below 2^26 elements; other strides, and the other blocks, address key by
+    // key). That saves the per-key lookups and 64-bit arithmetic of a lane's two rows per block (fp8
+    // 106.6 -> 104.5 us per step on the ragged fp8 workload); with one row per lane and block the
+    // wait for the wave-wide lookup costs more than it saves (int4 77.5 -> 81.5 us), so the other
+    // forms address key by key. ROWS: the lane's rows are keys 8 jr + l / 8 and its scales those of
+    // key l % 16; otherwise both are key l % 16.
+    const int lane_key = ROWS ? (lane >> 3) : c16;
+    constexpr uint64_t kNarrow = uint64_t(1) << 26;
+    const bool narrow = ROWS && (uint64_t)p.k_s[1] < kNarrow && (uint64_t)p.v_s[1] < kNarrow &&
+                        (!FP8 || ((uint64_t)p.ks_s[1] < kNarrow && (uint64_t)p.vs_s[1] < kNarrow));
+    auto row_at = [](const auto *base, int i, int64_t stride) { return base + (uint64_t)(uint32_t)i * (uint32_t)stride; };
     auto fetch = [&](Buf &f, int base) {
         f.base = base;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int jr = 0; jr < kR; ++jr) {
-            const int vb = base + 16 * kb;  // uniform
-            const int v = vb + (ROWS ? 8 * jr + (lane >> 3) : c16);
-            const KV *kp = safe, *vp = safe;
+        for (int kb = 0; kb < 2; ++kb) {
+            const int vb = base + 16 * kb;  // uniform, a multiple of 16
+            const KV *kp[kR], *vp[kR];
             const float *ksp = p.k_scale, *vsp = p.v_scale;  // the arrays' first scales: always readable
-            if (v < t1) {
-                if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
-                    if (v >= lo_min && v < hi_max) {
-                        const int64_t page = s_map[(v >> map_shift) - map_first];
+            bool slive = false;                                // the scales' key is read
+            // Only addresses are formed here; the loads below are issued on every path.
+            bool whole = ROWS && narrow && vb + 16 <= t1;  // uniform
+            int64_t page = 0;
+            int pos0 = vb;
+            if constexpr (MODE == KV_SPARSE) {
+                if (whole) pos0 = __builtin_amdgcn_readfirstlane(logical(vb));
+                whole = whole && pos0 + 16 <= L;
+            }
+            whole = whole && pos0 >= lo_min && pos0 + 16 <= hi_max;
+            if constexpr (MODE == KV_PAGED)
+                if (whole) page = __builtin_amdgcn_readfirstlane(s_map[(vb >> map_shift) - map_first]);
+            if (whole) {
+                const int slot = MODE == KV_PAGED ? (vb & map_mask) : pos0;
+                const int64_t pk = MODE == KV_PAGED ? page * p.k_s[0] : 0, pv = MODE == KV_PAGED ? page * p.v_s[0] : 0;
+#pragma unroll
+                for (int jr = 0; jr < kR; ++jr) {
+                    kp[jr] = row_at(kbase + pk + (int64_t)(slot + 8 * jr) * p.k_s[1], lane_key, p.k_s[1]);
+                    vp[jr] = row_at(vbase + pv + (int64_t)(slot + 8 * jr) * p.v_s[1], lane_key, p.v_s[1]);
+                }
+                if constexpr (FP8) {
+                    const int64_t pks = MODE == KV_PAGED ? page * p.ks_s[0] : 0;
+                    const int64_t pvs = MODE == KV_PAGED ? page * p.vs_s[0] : 0;
+                    ksp = row_at(ksbase + pks + (int64_t)slot * p.ks_s[1], c16, p.ks_s[1]);
+                    vsp = row_at(vsbase + pvs + (int64_t)slot * p.vs_s[1], c16, p.vs_s[1]);
+                }
+                slive = true;
+            } else {
+                // key v's row offsets (64-bit), or false for a key that is not read
+                auto rows_of = [&](int v, int64_t &rk, int64_t &rv, int64_t &rks, int64_t &rvs) -> bool {
+                    if (v >= t1) return false;
+                    if constexpr (MODE == KV_PAGED) {  // logical position = v, and v < t1 <= L
+                        if (v < lo_min || v >= hi_max) return false;
+                        const int64_t pg = s_map[(v >> map_shift) - map_first];
                         const int slot = v & map_mask;
-                        kp = kbase + page * p.k_s[0] + slot * p.k_s[1];
-                        vp = vbase + page * p.v_s[0] + slot * p.v_s[1];
-                        if constexpr (FP8) {
-                            ksp = ksbase + page * p.ks_s[0] + slot * p.ks_s[1];
-                            vsp = vsbase + page * p.vs_s[0] + slot * p.vs_s[1];
-                        }
+                        rk = pg * p.k_s[0] + slot * p.k_s[1];
+                        rv = pg * p.v_s[0] + slot * p.v_s[1];
+                        rks = pg * p.ks_s[0] + slot * p.ks_s[1];
+                        rvs = pg * p.vs_s[0] + slot * p.vs_s[1];
+                    } else {
+                        const int pos = logical(v);
+                        if (pos >= L || pos < lo_min || pos >= hi_max) return false;
+                        rk = (int64_t)pos * p.k_s[1];
+                        rv = (int64_t)pos * p.v_s[1];
+                        rks = (int64_t)pos * p.ks_s[1];
+                        rvs = (int64_t)pos * p.vs_s[1];
                     }
-                } else {
-                    const int pos = logical(v);
-                    if (pos < L && pos >= lo_min && pos < hi_max) {
-                        kp = kbase + (int64_t)pos * p.k_s[1];
-                        vp = vbase + (int64_t)pos * p.v_s[1];
-                        if constexpr (FP8) {
-                            ksp = ksbase + (int64_t)pos * p.ks_s[1];
-                            vsp = vsbase + (int64_t)pos * p.vs_s[1];
+                    return true;
+                };
+#pragma unroll
+                for (int jr = 0; jr < kR; ++jr) {
+                    int64_t rk = 0, rv = 0, rks = 0, rvs = 0;
+                    const bool live = rows_of(vb + 8 * jr + lane_key, rk, rv, rks, rvs);
+                    kp[jr] = live ? kbase + rk : safe;
+                    vp[jr] = live ? vbase + rv : safe;
+                    if constexpr (FP8 && !ROWS) {
+                        if (live) {
+                            ksp = ksbase + rks;
+                            vsp = vsbase + rvs;
                         }
+                        slive = live;
+                    }
+                }
+                if constexpr (FP8 && ROWS) {
+                    int64_t rk = 0, rv = 0, rks = 0, rvs = 0;
+                    slive = rows_of(vb + c16, rk, rv, rks, rvs);
+                    if (slive) {
+                        ksp = ksbase + rks;
+                        vsp = vsbase + rvs;
                     }
                 }
             }
-            if constexpr (INT4) {  // rows are 4-byte aligned only: word loads
-                const uint32_t *kw = kp + 1 + 4 * grp, *vw = vp + 1 + 4 * grp;
-                f.k[kb][0] = u32x4{kw[0], kw[1], kw[2], kw[3]};
-                f.v[kb][0] = u32x4{vw[0], vw[1], vw[2], vw[3]};
-                f.kc[kb] = kp[0];
-                f.vc[kb] = vp[0];
-                f.live[kb][0] = kp != safe;
-            } else if constexpr (ROWS) {
-                f.k[kb][jr] = ld16_stream(kp + 16 * (lane & 7));
-                f.v[kb][jr] = ld16_stream(vp + 16 * (lane & 7));
-                f.ks[kb][jr] = *ksp;
-                f.vs[kb][jr] = *vsp;
-                f.live[kb][jr] = kp != safe;
-            } else if constexpr (FP8) {
+            if constexpr (FP8) {  // used only once this buffer is current (a select there would wait)
+                f.ks[kb] = *ksp;
+                f.vs[kb] = *vsp;
+                f.slive[kb] = slive;
+            }
 #pragma unroll
-                for (int j = 0; j < kLoads; ++j)
-                    f.k[kb][j] = j == kLoads - 1 ? ld16_last(kp + 64 * j + 16 * grp) : ld16(kp + 64 * j + 16 * grp);
+            for (int jr = 0; jr < kR; ++jr) {
+                if constexpr (INT4) {  // rows are 4-byte aligned only: word loads
+                    const uint32_t *kw = kp[0] + 1 + 4 * grp, *vw = vp[0] + 1 + 4 * grp;
+                    f.k[kb][0] = u32x4{kw[0], kw[1], kw[2], kw[3]};
+                    f.v[kb][0] = u32x4{vw[0], vw[1], vw[2], vw[3]};
+                    f.kc[kb] = kp[0][0];
+                    f.vc[kb] = vp[0][0];
+                    f.live[kb][0] = kp[0] != safe;
+                } else if constexpr (ROWS) {
+                    f.k[kb][jr] = ld16_stream(kp[jr] + 16 * (lane & 7));
+                    f.v[kb][jr] = ld16_stream(vp[jr] + 16 * (lane & 7));
+                    f.live[kb][jr] = kp[jr] != safe;
+                } else if constexpr (FP8) {
 #pragma unroll
-                for (int j = 0; j < kLoads; ++j)
-                    f.v[kb][j] = j == kLoads - 1 ? ld16_last(vp + 64 * j + 16 * grp) : ld16(vp + 64 * j + 16 * grp);
-                // used only once this buffer is current (a select here would wait for the prefetch)
-                f.ks[kb][0] = *ksp;
-                f.vs[kb][0] = *vsp;
-                f.live[kb][0] = kp != safe;
-            } else {
+                    for (int j = 0; j < kLoads; ++j)
+                        f.k[kb][j] = j == kLoads - 1 ? ld16_last(kp[0] + 64 * j + 16 * grp) : ld16(kp[0] + 64 * j + 16 * grp);
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) f.k[kb][ks] = ld16(kp + 32 * ks + 8 * grp);
+                    for (int j = 0; j < kLoads; ++j)
+                        f.v[kb][j] = j == kLoads - 1 ? ld16_last(vp[0] + 64 * j + 16 * grp) : ld16(vp[0] + 64 * j + 16 * grp);
+                    f.live[kb][0] = kp[0] != safe;
+                } else {
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) f.v[kb][ks] = ld16(vp + 32 * ks + 8 * grp);
+                    for (int ks = 0; ks < kKs; ++ks) f.k[kb][ks] = ld16(kp[0] + 32 * ks + 8 * grp);
+#pragma unroll
+                    for (int ks = 0; ks < kKs; ++ks) f.v[kb][ks] = ld16(vp[0] + 32 * ks + 8 * grp);
+                }
             }
         }
     };
@@ -372,12 +435,15 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                     lds_u8 *vr = vw + row * kRowBytes;
                     st_lds16(vr + (((2 * pc) ^ swz<D>(row)) << 4), e4m3_x8(w[0], w[1]));
                     st_lds16(vr + (((2 * pc + 1) ^ swz<D>(row)) << 4), e4m3_x8(w[2], w[3]));
-                    if (pc == 0) {  // a key that is not read takes scale 0
-                        const float vsv = live ? cur.vs[kb][jr] : 0.f;
-                        s_ks[wave][row] = live ? cur.ks[kb][jr] * p.scale_log2 : 0.f;
-                        s_vs[wave][row] = vsv;
-                        s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
-                    }
+                }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                if (grp == 0) {  // key 16 kb + c16's scales; a key that is not read takes scale 0
+                    const int row = 16 * kb + c16;
+                    const float vsv = cur.slive[kb] ? cur.vs[kb] : 0.f;
+                    s_ks[wave][row] = cur.slive[kb] ? cur.ks[kb] * p.scale_log2 : 0.f;
+                    s_vs[wave][row] = vsv;
+                    s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
                 }
         }
         // Other forms: V tile -> LDS, row 16 kb + c16; bf16 chunk 4 ks + grp; fp8 piece j as chunks
@@ -414,8 +480,8 @@ __global__ void __launch_bounds__(kThreads) partial_mfma16_kernel(const PartialP
                         st_lds16(vr + (((c0 + 1) ^ swz<D>(row)) << 4), e4m3_x8(w[2], w[3]));
                     }
                     if (grp == 0) {  // a key that is not read takes scale 0
-                        const float vsv = cur.live[kb][0] ? cur.vs[kb][0] : 0.f;
-                        s_ks[wave][row] = cur.live[kb][0] ? cur.ks[kb][0] * p.scale_log2 : 0.f;
+                        const float vsv = cur.slive[kb] ? cur.vs[kb] : 0.f;
+                        s_ks[wave][row] = cur.slive[kb] ? cur.ks[kb] * p.scale_log2 : 0.f;
                         s_vs[wave][row] = vsv;
                         s_vr[wave][row] = vsv != 0.f ? __builtin_amdgcn_rcpf(vsv) : 0.f;
                     }
