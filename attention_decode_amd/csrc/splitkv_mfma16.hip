@@ -1,6 +1,6 @@
 // splitkv_mfma16.hip -- partial split-KV pass on the matrix cores for work units of at most 16 query
-// rows (bf16 or fp8 caches): small GQA groups times speculative tokens, e.g. 4 query heads per KV
-// head over an fp8 cache.
+// rows (bf16, fp8 or one-group int4 caches): small GQA groups times speculative tokens, e.g. 4
+// query heads per KV head over an fp8 or int4 cache.
 //
 // It computes what the 32-row matrix-core pass (splitkv_mfma.hip) computes: per work unit (split s,
 // block of up to 16 query rows r = t*G + g of KV head h, sequence b) the attention of those rows
@@ -25,9 +25,11 @@
 //     XOR-swizzled by row as in the 32-row pass: both the stores of 16 rows and the transposing
 //     reads of 4 rows x 2 chunks are free of bank conflicts).
 //   * Head-dim order of the score reduction: k-step ks of a bf16 cache covers elements 32ks ..
-//     32ks+31, lane group l/16 taking 8 of them; an fp8 lane loads 16 bytes (elements 64j + 16(l/16)
-//     .. +15) and converts them into the operands of k-steps 2j and 2j+1. Q is loaded in the same
-//     order (the order of a reduction is free as long as both operands share it).
+//     32ks+31, lane group l/16 taking 8 of them; an fp8 operand takes 16 bytes (elements 64j +
+//     16(l/16) .. +15) into k-steps 2j and 2j+1, loaded straight into the operand (half rows) or,
+//     by default, loaded as whole 128-byte rows and read back from a per-wave LDS tile (ROWS);
+//     an int4 operand takes a lane's 4 words of fields in the order int4_x8 produces. Q is loaded
+//     in the same order (the order of a reduction is free as long as both operands share it).
 //   * Everything else follows the 32-row pass: a work group of 4 waves each taking every 4th 32-key
 //     tile with loads one tile ahead; keys outside the split, past the sequence, seen by no row of
 //     the unit or in unlisted blocks never read (their loads go to the unit's own query row, their
