@@ -100,3 +100,40 @@ def test_token_major_fp8(orc, monkeypatch, fp8_kernel):
     ref_o, ref_l = oracle_of(orc, w)
     out, lse = run(t, num_splits=2)
     assert_matches(out, lse, ref_o, ref_l, w.dtype, "fp8 token-major")
+
+
+@pytest.mark.parametrize("config,rows", [(6, "1"), (6, "0"), (8, None)], ids=["fp8_whole_rows", "fp8_half_rows", "int4"])
+def test_token_major_quantised_full_size(monkeypatch, config, rows):
+    """The ragged fp8 and int4 workloads at full size, cache (and fp8 row scales) stored
+    token-major, on the 16-row kernel (fp8 in both load forms; the whole-row form addresses a block
+    from one page lookup and the row stride, here Hkv rows): the oracle's result, and the
+    head-major result bit for bit."""
+    monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+    if rows is not None:
+        monkeypatch.setenv("AD_MFMA_ROWS", rows)
+    say(f"[gpu] workload {config} token-major, AD_MFMA_ROWS={rows}")
+    w = inputs.make(config)
+    t = inputs.token_major(w)
+    out, lse = run(t)
+    ref_o, ref_l = reference(config)
+    assert_tight(out, lse, ref_o, ref_l, torch.bfloat16, f"workload {config} token-major")
+    o2, l2 = run(w)
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2), \
+        "token-major and head-major results differ"
+
+
+@pytest.mark.parametrize("groups", [1, 4])
+def test_token_major_int4(orc, monkeypatch, groups):
+    """An int4 pool (one coefficient group per row on the 16-row kernel, four on the vector kernel),
+    stored token-major, NaN coefficients in every unreferenced row."""
+    monkeypatch.delenv("AD_PARTIAL_KERNEL", raising=False)
+    say(f"[gpu] token-major int4 pool, groups {groups}")
+    w = inputs.paged(seq_lens=[5, 300, 1000, 17], num_q_heads=16, num_kv_heads=4, head_dim=128, page_size=16,
+                     seed=75, kv_format="int4", kv_groups=groups, poison=True)
+    t = inputs.token_major(w)
+    ref_o, ref_l = oracle_of(orc, w)
+    for S in (1, 2):
+        out, lse = run(t, num_splits=S)
+        assert_matches(out, lse, ref_o, ref_l, w.dtype, f"int4 token-major S={S}")
+        o2, l2 = run(w, num_splits=S)
+        assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
