@@ -168,8 +168,8 @@ int check_sparse(const ad_sparse *sp) {
 }
 
 // ------------------------------------------------------------------ planning
-// The latent-attention kernel takes 128 query rows (heads x query tokens) per work unit.
-int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, 128); }
+// The latent-attention kernel takes 64 query rows (heads x query tokens) per work unit.
+int mla_row_blocks(const ad_decode_args *a) { return (int)cdiv((int64_t)a->num_q_heads * a->q_len, ad::mla::kRows); }
 
 // Which partial kernel runs, and how the G * q_len query rows of one KV head are blocked into work
 // units: the matrix-core kernels (bf16 with more than 8 rows, any fp8 cache, and an int4 cache of

@@ -49,7 +49,7 @@ def test_paged_entry_point_small(orc, S):
 
 
 # The planner's choice (splits, keys per split) for the workloads on a 256-compute-unit MI355X.
-PLANS = {1: (4, 128), 2: (2, 2048), 3: (5, 1648), 4: (4, 1056), 5: (8, 1024), 6: (3, 2736),
+PLANS = {1: (4, 128), 2: (2, 2048), 3: (5, 1648), 4: (4, 1056), 5: (4, 2048), 6: (3, 2736),
          7: (2, 4096), 8: (3, 2736)}
 
 

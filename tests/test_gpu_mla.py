@@ -7,7 +7,7 @@ import torch
 
 from attention_decode_amd import _abi, inputs
 from attention_decode_amd.step import DecodeStep
-from gpu_util import assert_matches, assert_tight, gpu_available, oracle_of, say
+from gpu_util import assert_matches, assert_matches_beyond_rounding, assert_tight, gpu_available, oracle_of, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -67,8 +67,9 @@ def test_mla_splitkv_partials_small(orc):
 
 
 def test_workload5_partials_sampled_rows(orc):
-    """Workload 5's own 8 splits of 1024 keys, written by attn_decode_mla_splitkv: every split of
-    the heads of sequences 0 and 31 and 64 random rows, against the oracle on each key range."""
+    """Workload 5 in 8 splits of 1024 keys (twice the planner's count, so more split boundaries),
+    written by attn_decode_mla_splitkv: every split of the heads of sequences 0 and 31 and 64
+    random rows, against the oracle on each key range."""
     say("[gpu] workload 5 split partials, sampled rows")
     w = inputs.make(5)
     S = 8
@@ -140,6 +141,27 @@ def test_mla_score_far_above_first_tile(orc):
     assert np.min(ref_l.reshape(2, 32)[0]) > 60       # the key really dominates sequence 0
     out, lse, _ = run(w, num_splits=1)
     assert_matches(out, lse, ref_o, ref_l, w.dtype, "far score")
+
+
+@pytest.mark.parametrize("head", [5, 27])
+def test_mla_score_far_above_first_tile_one_row(orc, head):
+    """As above, but only one query head sees the far key: the work group must still notice that a
+    single row (held by lanes other than the first of its waves) went past its reference max, and
+    recompute (a vote taken by one lane alone left that row's output NaN). Other heads see the
+    far key's large value row with moderate weight, so outputs reach about 8.3, where bf16's own
+    rounding is 0.03: the tolerance applies beyond that rounding."""
+    say(f"[gpu] mla: one row ({head}) far above its first tile's max")
+    lens = [300, 300]
+    w = inputs.mla(batch=2, num_heads=32, kv_len=300, page_size=16, seq_lens=lens, seed=12)
+    u = w.storage["q"][0, 0, head].clone()
+    j0 = 250
+    page = int(w.block_table[0, j0 // 16])
+    w.storage["ckv"][page, j0 % 16, 0] = (3.0 * u.float()).to(w.dtype)
+    ref_o, ref_l = oracle_of(orc, w)
+    lse0 = ref_l.reshape(2, 32)[0]
+    assert lse0[head] > 60 and np.delete(lse0, head).max() < 30  # only that row is dominated
+    out, lse, _ = run(w, num_splits=1)
+    assert_matches_beyond_rounding(out, lse, ref_o, ref_l, w.dtype, f"far score on head {head}")
 
 
 def test_mla_split_invariance():

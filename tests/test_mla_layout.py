@@ -64,7 +64,10 @@ def check(lib, w, S, chunk=None):
 
 
 def test_full_mla_workload(checker):
-    """32 sequences of 8192 keys on 64-key pages, 8 splits of 1024 keys (the plan for 256 CUs)."""
+    """32 sequences of 8192 keys on 64-key pages, 4 splits of 2048 keys (the plan for 256 CUs) and 8
+    of 1024."""
+    n = check(checker, inputs.make(5), 4)
+    assert n > 10 ** 7
     n = check(checker, inputs.make(5), 8)
     assert n > 10 ** 7
 
