@@ -16,7 +16,7 @@
 // key) in one LDS object and the rotary rows (64 bf16 = 8 chunks per key) in another. Chunk c of
 // key k sits at position c ^ lat_swz(k) (latent) or c ^ rope_swz(k) (rotary) of the key's row, so
 // that the score-operand reads (16 keys, one chunk each, per 16 lanes) and the transposing value
-// reads (4 keys x 4 chunks per 32 lanes) hit distinct banks, with 32 or 64 banks.
+// reads (4 keys x 4 chunks per 32 lanes) hit distinct banks in a model of 32 or of 64 banks.
 #pragma once
 
 #include <stdint.h>
@@ -67,9 +67,10 @@ static_assert(kWaves <= 2 * kSlots, "two waves stage in each latent slot");
 static_assert(kTile % 16 == 0, "tiles start on 16-key boundaries, so a rotary group of 8 keys stays in one page");
 
 // Latent: a permutation of 0..15 over any 16 consecutive keys whose low 3 bits are a permutation
-// over any 8 (the score-operand reads of 16 keys at one chunk are conflict-free whether the LDS
-// serves 8 or 16 lanes of 16 bytes per cycle), and whose bits 1-2 and bits 2-3 are each distinct
-// over keys 4j .. 4j + 3 (the transposing reads of 4 keys x 2 or 4 chunks likewise).
+// over any 8 (the score-operand reads of 16 keys at one chunk are conflict-free in a model that
+// serves 8 and in one that serves 16 lanes of 16 bytes per cycle), and whose bits 1-2 and bits 2-3
+// are each distinct over keys 4j .. 4j + 3 (the transposing reads of 4 keys x 2 or 4 chunks
+// likewise).
 AD_HD int lat_swz(int k) {
     constexpr int kBase = (0 << 0) | (6 << 4) | (10 << 8) | (12 << 12);  // 0, 6, 10, 12 by k % 4
     return ((kBase >> (4 * (k & 3))) & 15) ^ ((k >> 2) & 3);

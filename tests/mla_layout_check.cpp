@@ -15,7 +15,8 @@
 //     and key, and no two writes land on one place;
 //   - every operand read, probability exchange and staging access stays inside its LDS object,
 //     and the per-lane forms of the offsets the kernel keeps in registers equal the plain ones;
-//   - the score-operand and value-operand reads are free of bank conflicts with 32 or 64 banks.
+//   - the score-operand and value-operand reads are free of bank conflicts in models of 32 and of
+//     64 banks.
 // Built with g++ and called through ctypes by tests/test_mla_layout.py; no GPU involved.
 #include <stdint.h>
 #include <stdio.h>
@@ -111,7 +112,7 @@ int conflict_degree(const int *addr, int bytes, int banks) {
 }
 
 // The score-operand reads (latent and rotary) and the transposing value reads are free of bank
-// conflicts whether the LDS serves 128 or 256 bytes per cycle (32 or 64 banks).
+// conflicts in a model of 32 banks (128 bytes per cycle) and in one of 64 (256 bytes per cycle).
 bool check_banks() {
     int a[64];
     for (int banks = 32; banks <= 64; banks *= 2) {
