@@ -410,10 +410,8 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
     // barrier also ends every read of tile i-2's slot, into which the step then copies tile i+2,
     // and every read of the probability buffer this step writes (tile i-2's). Copies past the end
     // read nothing or the query row, so every step issues the same number of copies and the vmcnt
-    // count is exact. The first round of four steps runs before the loop: every ring object has
-    // then been copied into on both edges into the loop, and the compiler's wait insertion keeps
-    // track of which slot each copy writes (entered straight from the first copies, the loop's
-    // first reads waited for later tiles as well).
+    // count is exact. The first tile has no value products before it (base == t0); the last
+    // tile's follow the loop.
     auto run_main = [&]() {
         int pg_next = 0;  // page ids of the next tile to copy (lookup)
         auto step = [&](lds_u8 *cur, lds_u8 *qcur, lds_u8 *prev, lds_u8 *fill, lds_u8 *qfill, lds_u8 *pout,
