@@ -164,6 +164,27 @@ def test_mla_score_far_above_first_tile_one_row(orc, head):
     assert_matches_beyond_rounding(out, lse, ref_o, ref_l, w.dtype, f"far score on head {head}")
 
 
+def test_mla_far_score_with_masks_and_splits(orc):
+    """The exact recompute under a causal sliding window with two query tokens and three splits:
+    one head of the first token sees the far key (in the last split, inside both tokens' windows);
+    the split holding it recomputes, with the rows the window hides from part of the split kept
+    at probability 0, and the merge weighs it against the other splits."""
+    say("[gpu] mla: far score under causal + window, 2 tokens, 3 splits")
+    lens = [300, 260]
+    w = inputs.mla(batch=2, num_heads=32, kv_len=300, page_size=16, seq_lens=lens, q_len=2, causal=True,
+                   window=200, seed=14)
+    head = 9
+    u = w.storage["q"][0, 0, head].clone()
+    j0 = 250
+    page = int(w.block_table[0, j0 // 16])
+    w.storage["ckv"][page, j0 % 16, 0] = (3.0 * u.float()).to(w.dtype)
+    ref_o, ref_l = oracle_of(orc, w)
+    lse = ref_l.reshape(2, 2, 32)
+    assert lse[0, 0, head] > 60 and np.delete(lse[0, 0], head).max() < 30
+    out, lse_, _ = run(w, num_splits=3)
+    assert_matches_beyond_rounding(out, lse_, ref_o, ref_l, w.dtype, "far score, masked, 3 splits")
+
+
 def test_mla_split_invariance():
     say("[gpu] mla split invariance")
     w = inputs.mla(batch=2, num_heads=128, kv_len=3000, page_size=64, seq_lens=[3000, 1777], seed=13)
