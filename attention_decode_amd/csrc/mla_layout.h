@@ -42,7 +42,9 @@ constexpr int kLatRowBytes = kLatent * 2;         // 1024
 constexpr int kRopeRowBytes = kRope * 2;          // 128
 constexpr int kLatBytes = kTile * kLatRowBytes;   // latent object of a slot: 32 KB
 constexpr int kRopeBytes = kTile * kRopeRowBytes; // rotary object of a slot: 4 KB
-constexpr int kSlots = 4;                         // ring depth: one tile in use, three in flight
+// Ring depth: the main loop has two tiles in use (value products, scores) and two in flight; the
+// exact pass's score-only loop one in use and three in flight.
+constexpr int kSlots = 4;
 constexpr int kColsPerWave = kLatent / kWaves;    // value columns whose products a wave accumulates (64)
 constexpr int kSlabsPerWave = kColsPerWave / 32;  // 32-column output slabs per wave (2)
 constexpr int kValueBlocks = kRows / 32;          // 32-row blocks of the value product (2)
