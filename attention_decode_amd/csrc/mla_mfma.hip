@@ -57,9 +57,12 @@ using namespace mla;
 constexpr int kKs = (kLatent + kRope) / 32;  // k-steps (32 values) of the score product
 constexpr int kLatKs = kLatent / 32;
 constexpr float kHeadroom = 64.f;
-constexpr int kPipe = 4;  // score-operand reads in flight ahead of the matrix products
-constexpr int kIssueAt = 3;  // the score product after which a step issues its copies
-constexpr int kChains = 1;   // independent accumulation chains of the score product
+// Score-operand reads in flight ahead of the matrix products (6 or 8 measured no faster).
+constexpr int kPipe = 4;
+// The score product after which a step issues its copies (after the 9th or 13th measured slower).
+constexpr int kIssueAt = 3;
+// Independent accumulation chains of the score product (2 or 3 measured no faster).
+constexpr int kChains = 1;
 
 // s_waitcnt with vmcnt(n) and no wait on the other counters (gfx9 encoding).
 constexpr int vmcnt_only(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -308,8 +311,7 @@ __global__ void __launch_bounds__(kThreads) mla_partial_kernel(const PartialPara
         auto k_operand = [&](int ks) -> u32x4 {
             return ks < kLatKs ? lds16(cur + kl[ks & 3] + 256 * (ks >> 2)) : lds16(rcur + kr[ks - kLatKs]);
         };
-        // kChains independent accumulators (k-step ks into chain ks % kChains), so that a product
-        // does not wait for the previous one's result
+        // k-step ks accumulates into chain ks % kChains
         f32x4 sc[kChains];
 #pragma unroll
         for (int c = 0; c < kChains; ++c) sc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
