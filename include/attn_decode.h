@@ -260,7 +260,7 @@ int attn_decode_merge(const float *part_o, const float *part_lse, const int32_t 
  * one group per compute unit) whose units hold at most 8 query rows, else the
  * partial pass and the merge kernel run as two launches in the same workspace. AD_FUSED_MERGE=0 / 1
  * forces two launches / one launch (testing aid, see the conventions above).
- * workspace: device memory of at least attn_decode_workspace_size(args, paged, num_splits)
+ * workspace: device memory of at least attn_decode_workspace_size(args, paged, sparse, num_splits)
  * bytes, 256-byte aligned. Its first AD_COUNTER_BYTES MUST be zero before its first use (zero
  * the allocation once); every call leaves them zero and writes its partials only after them, so
  * the workspace is reused as is by any later call, of any shape or split count, and by
