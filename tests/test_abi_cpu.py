@@ -513,3 +513,27 @@ def test_noalloc_rejects_a_step_beyond_its_scratch():
     assert rc == -7
     assert "scratch" in ad.attn_decode_last_error()
     assert _abi.lib().attn_decode_noalloc(None, None, None, 2, None) == -1
+
+
+def test_split_page_map_limit():
+    """A split of a paged cache stages its page ids in LDS: 1038 pages of keys per split (258 for
+    MLA), plus two for a split that starts inside a page. With the count forced, a split of
+    exactly that many pages is planned and one page more is refused (the workspace query returns
+    0 and names the limit)."""
+    L = _abi.lib()
+    for mla, limit in ((False, 1038), (True, 258)):
+        for pages, ok in ((limit, True), (limit + 1, False)):
+            keys = 16 * pages
+            if mla:
+                q = torch.zeros(1, 1, 16, 512, dtype=torch.bfloat16)
+                ckv = torch.zeros(pages + 2, 16, 1, 512, dtype=torch.bfloat16)
+                a = _abi.make_args(q, ckv, None, scale=0.1, kv_len_max=keys, out=q.clone(), head_dim_qk=576)
+            else:
+                q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16)
+                pool = torch.zeros(pages + 2, 1, 16, 128, dtype=torch.bfloat16).permute(0, 2, 1, 3)
+                a = _abi.make_args(q, pool, pool, scale=0.1, kv_len_max=keys, out=q.clone())
+            pg = _abi.make_paged(torch.zeros(1, pages + 2, dtype=torch.int32), 16)
+            n = L.attn_decode_workspace_size(ctypes.byref(a), ctypes.byref(pg), None, 1)
+            assert (n > 0) == ok, (mla, pages, n, _abi.attn_decode_last_error())
+            if not ok:
+                assert "pages/blocks per split" in _abi.attn_decode_last_error()
