@@ -537,3 +537,18 @@ def test_split_page_map_limit():
             assert (n > 0) == ok, (mla, pages, n, _abi.attn_decode_last_error())
             if not ok:
                 assert "pages/blocks per split" in _abi.attn_decode_last_error()
+
+
+def test_work_unit_limit():
+    """The whole-step entry keeps one 4-byte arrival counter per work unit (sequence x KV head x
+    block of query rows) in a fixed 1 MiB region: 262,144 units at most. One unit more is refused
+    on the host, before any HIP call. (A call at the limit would go on to launch, so it is not
+    made here: the pointers are host memory.)"""
+    limit = (1 << 20) // 4
+    a, keep = _args()
+    a.num_q_heads, a.num_kv_heads = 16, 4   # 4 rows per KV head: one row block per KV head
+    a.batch = limit // 4 + 1                # one sequence past the limit; no kernel reads the strides
+    a.q_stride[0] = a.k_stride[0] = a.v_stride[0] = a.out_stride[0] = 0
+    a.q_stride[2] = a.out_stride[2] = a.k_stride[2] = a.v_stride[2] = 0
+    assert _decode_call(a)[0] == -5
+    assert "work units" in _abi.attn_decode_last_error()
