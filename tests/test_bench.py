@@ -1,7 +1,8 @@
 """The bench.py output contract: one JSON line on stdout with the metric and its unit, the step's
 throughput and time, the run's shape, a roofline object for the dominant kernel (achieved over
 peak) and a CPU-baseline object (the oracle timed on a bounded sample); more than one GPU is
-refused with a message, before any GPU is touched."""
+refused with a message, before any GPU is touched; and the roofline's counter-measured traffic is
+reported only while the sources it was measured on are unchanged."""
 import json
 import os
 import subprocess
@@ -51,3 +52,35 @@ def test_json_line_contract():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["unit"] == d["unit"]
     assert cb["sample"]
+
+
+def test_traffic_record_goes_stale_with_its_sources(tmp_path, monkeypatch):
+    """`roofline.traffic` comes from a committed counter record that names the sources it was
+    measured on and their sha256: it is reported while they are unchanged, and null (None) once
+    any of them changes (a comment included) or is missing."""
+    import shutil
+    import bench
+    rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_mla_partial.json")))
+    for rel in rec["sources"]:
+        os.makedirs(tmp_path / os.path.dirname(rel), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, rel), tmp_path / rel)
+    os.makedirs(tmp_path / "profiles")
+    shutil.copy(os.path.join(ROOT, "profiles", "traffic_mla_partial.json"), tmp_path / "profiles")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.load_traffic("mla_partial") == rec["bytes_per_launch"]
+    planner = tmp_path / "attention_decode_amd" / "csrc" / "api.cpp"
+    planner.write_text(planner.read_text() + "// edited\n")
+    assert bench.load_traffic("mla_partial") is None
+    planner.unlink()
+    assert bench.load_traffic("mla_partial") is None
+    assert bench.load_traffic("no_such_kernel") is None
+
+
+def test_committed_traffic_records_are_current():
+    """Every committed counter record matches the sources as they stand, so the traffic that
+    bench reports comes from the kernels in this tree."""
+    import glob
+    import bench
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "traffic_*.json"))):
+        tag = os.path.basename(path)[len("traffic_"):-len(".json")]
+        assert bench.load_traffic(tag) is not None, f"{tag}: sources changed since its counter run"
