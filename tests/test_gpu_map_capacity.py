@@ -1,9 +1,10 @@
-"""GPU parity at the page-map limit. A split of a paged cache stages its page ids in LDS: at most
-1038 pages of keys per split on the GQA kernels and 258 on the MLA kernel, plus two for a split
-that starts inside a page. Each case below forces splits at that limit, or within a page of it
-with split starts inside a page, on each partial kernel form: the vector kernel (8 rows per KV
-head), the 32-row matrix-core kernel (32 rows), the 16-row kernel (fp8, 4 rows) and MLA. Every
-result must match the fp64 oracle; the host refuses a split one page longer (CPU ABI tests)."""
+"""GPU parity at the page-map limit. A split of a paged cache (or of a block list) stages its page
+(block) ids in LDS: at most 1038 per split on the GQA kernels and 258 on the MLA kernel, plus two
+for a split that starts inside a page. Each case below forces splits at that limit, or within a
+page of it with split starts inside a page, on each partial kernel form: the vector kernel (8
+rows per KV head), the 32-row matrix-core kernel (32 rows), the 16-row kernel (fp8, 4 rows) and
+MLA, paged and with block lists. Every result must match the fp64 oracle; the host refuses a
+split one page longer (CPU ABI tests)."""
 import pytest
 import torch
 
@@ -30,6 +31,12 @@ CASES = [
     ("mfma16_fp8_page32_inside_pages", inputs.paged,
      dict(seq_lens=[66400], num_q_heads=4, num_kv_heads=1, head_dim=128, page_size=32, seed=94,
           kv_format="fp8"), 2, 1038),
+    ("vector_blocklist16_exact", inputs.sparse,
+     dict(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=128, kv_len=16 * 2076, q_len=1, block_size=16,
+          blocks=list(range(0, 2076, 2)), causal=False, seed=97), 1, 1038),
+    ("mfma32_blocklist16_exact", inputs.sparse,
+     dict(batch=1, num_q_heads=32, num_kv_heads=1, head_dim=128, kv_len=16 * 2076, q_len=1, block_size=16,
+          blocks=list(range(1, 2076, 2)), causal=False, seed=98), 1, 1038),
     ("mla_page16_exact", inputs.mla,
      dict(batch=1, num_heads=16, kv_len=16 * 258, page_size=16, seed=95), 1, 258),
     ("mla_page64_inside_pages", inputs.mla,
@@ -40,9 +47,11 @@ CASES = [
 @pytest.mark.parametrize("name,gen,kw,S,limit", CASES, ids=[c[0] for c in CASES])
 def test_split_at_page_map_limit(orc, name, gen, kw, S, limit):
     w = gen(**kw)
-    L = w.kv_len_max
+    if w.num_blocks is not None:  # a block list: splits cover listed keys, the map holds block ids
+        L, page = int(w.block_idx.shape[-1]) * w.block_size, w.block_size
+    else:
+        L, page = w.kv_len_max, w.page_size
     chunk = chunk_of(L, S)
-    page = w.page_size
     # the most pages any split of this plan touches (a split may start inside a page)
     spans = [((min((s + 1) * chunk, L) - 1) // page) - (s * chunk) // page + 1 for s in range(S) if s * chunk < L]
     say(f"[gpu] {name}: L={L}, S={S}, chunk={chunk}, page={page}, pages per split {spans} (limit {limit} + 2)")
